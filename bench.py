@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the ISPA hot path on one MI355X.
+
+One step = one full ISPA warmup of a Wan-1.3B-shaped model (workload "wan1.3b-warmup"): 30 layers x
+4 chunks of dual-stream attention (12 heads x 128, 4680 queries per 3-frame chunk, history growing
+0 -> 9 frames) each followed by the warmup-statistics update, then the batched ridge solve of all
+30 layers (d = 1536, lambda = 1e-2), their reconstruction errors, and the selection of K = 15
+L-Layers (errors copied to the host and ranked there). Inputs are seeded synthetic tensors already
+resident in HBM when the timed region starts.
+
+Prints one JSON line. `value` is the step's algorithmic TFLOP/s (attention 4 n_q n_keys H d_h per
+call, statistics 4 N d^2 per chunk, solve 13/3 d^3, error 6 d^3 per layer) over the measured step
+time; the attention kernel's own rate, its fraction of the bf16 MFMA peak, and the absorb time per
+layer are reported beside it, with the oracle timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count (tuning only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-only-cfg", type=int, default=None,
+                    help="time only ispa_attn_dual on workload 2, 4 (chunk 4) or 5 and print its rate")
+    return ap.parse_args()
+
+
+def bf16_dev(x, torch):
+    import ispa_inputs as inputs
+    bits = inputs.bf16_bits(x)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda", non_blocking=False)
+
+
+def attn_flops(n_q, n_keys, H, dh):
+    return 4.0 * n_q * n_keys * H * dh
+
+
+def attn_bytes(n_q, n_keys, H, dh, elem=2):
+    # Q, K, V read once; A_loc, A_full written once; three LSE rows
+    return elem * (n_q * H * dh + 2 * n_keys * H * dh + 2 * n_q * H * dh) + 3 * 4 * H * n_q
+
+
+class Layer:
+    """Device-resident inputs of one layer: the key/value cache of all 12 warmup frames and the four
+    chunks' queries."""
+
+    def __init__(self, wl, layer, torch):
+        import ispa_inputs as inputs
+        cache = inputs.LayerCache(wl, layer)
+        self.k = bf16_dev(cache.k, torch)
+        self.v = bf16_dev(cache.v, torch)
+        self.q = []
+        for c in range(len(wl.chunks)):
+            inp = inputs.attention_inputs(wl.cfg, layer, c, cache=cache)
+            self.q.append(bf16_dev(inp["q"], torch))
+        self.w = torch.from_numpy(inputs.weight(wl.cfg, layer)).to("cuda")
+
+    def seg(self, r):
+        import ispa_inputs as inputs
+        a, b = r[0] * inputs.FRAME_TOKENS, r[1] * inputs.FRAME_TOKENS
+        return self.k[a:b], self.v[a:b]
+
+
+def cpu_baseline(wl):
+    """The oracle (fp64 NumPy) on a bounded sample of the same workload, timed on the host cores."""
+    import ispa_inputs as inputs
+    from oracle import absorb as oab
+    from oracle import attention as oatt
+    cores = len(os.sched_getaffinity(0))
+    H, dh, d = wl.n_heads, wl.head_dim, wl.d
+    # (a) attention of 256 query rows of chunk 4 (all heads, 18720 keys)
+    inp = inputs.attention_inputs(wl.cfg, 0, 3)
+    rows = np.arange(256)
+    t0 = time.perf_counter()
+    oatt.dual_stream(inp, rows=rows)
+    t_att = time.perf_counter() - t0
+    n_keys = sum(inp[k].shape[0] for k in ("sink_k", "cur_k", "hist_k"))
+    f_att = attn_flops(len(rows), n_keys, H, dh)
+    # (b) Layer Absorb of one layer: statistics over the 4 warmup chunks, solve, error
+    chunks = [inputs.absorb_rows(wl.cfg, 0, c) for c in range(len(wl.chunks))]
+    w = inputs.weight(wl.cfg, 0).astype(np.float64)
+    t0 = time.perf_counter()
+    st = oab.accumulate([(c["a_loc"], c["a_full"]) for c in chunks])
+    dw = oab.ridge_delta_w(st["G"], st["C"], w, wl.lam)
+    oab.layer_error_stats(st["G"], st["C"], st["H"], w, dw)
+    t_abs = time.perf_counter() - t0
+    n_rows = sum(c["a_loc"].shape[0] for c in chunks)
+    f_abs = 4.0 * n_rows * d * d + 13.0 / 3.0 * d ** 3 + 6.0 * d ** 3
+    return {
+        "value": round((f_att + f_abs) / (t_att + t_abs) / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle: dual-stream attention of 256 query rows x 12 heads over "
+                   f"{n_keys} keys (chunk 4, layer 0) in {t_att:.2f} s, plus Layer Absorb of one "
+                   f"layer (statistics of 4 x 4680 rows, solve, error at d={d}) in {t_abs:.2f} s; "
+                   f"same algorithmic FLOP count as the GPU step"),
+        "absorb_ms_per_layer": round(t_abs * 1e3, 1),
+    }
+
+
+def attn_only(cfg, steps, warmup, torch):
+    import ispa_inputs as inputs
+    import kv_cache_attention_split_amd as ispa
+    wl = inputs.CONFIGS[cfg]
+    chunk = 3 if cfg in (3, 4) else 0
+    inp = inputs.attention_inputs(cfg, 0, chunk)
+    dev = {k: bf16_dev(inp[k], torch) for k in ("q", "sink_k", "sink_v", "cur_k", "cur_v", "hist_k", "hist_v")}
+    n_q = inp["q"].shape[0]
+    H, dh = wl.n_heads, wl.head_dim
+    a_loc = torch.empty((n_q, H * dh), dtype=torch.bfloat16, device="cuda")
+    a_full = torch.empty_like(a_loc)
+    lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
+    n_keys = sum(inp[k].shape[0] for k in ("sink_k", "cur_k", "hist_k"))
+    res = {}
+    for mode in ("dual", "local"):
+        full = mode == "dual"
+
+        def call():
+            ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"],
+                                dev["hist_k"], dev["hist_v"], wl.scale, a_loc, a_full if full else None,
+                                lse[0], lse[1] if full else None, lse[2] if full else None)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nk = n_keys if full else inp["sink_k"].shape[0] + inp["cur_k"].shape[0]
+        fl = attn_flops(n_q, nk, H, dh)
+        res[mode] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                     "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    print(json.dumps({"workload": wl.name, "attention": res}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    import ispa_inputs as inputs
+    import kv_cache_attention_split_amd as ispa
+
+    if args.attn_only_cfg is not None:
+        attn_only(args.attn_only_cfg, args.steps, args.warmup, torch)
+        return
+
+    wl = inputs.CONFIGS[3]
+    n_layers = args.layers or wl.n_layers
+    H, dh, d = wl.n_heads, wl.head_dim, wl.d
+    n_q = inputs.CHUNK_TOKENS
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(os.sched_getaffinity(0)))) as ex:
+        layers = list(ex.map(lambda l: Layer(wl, l, torch), range(n_layers)))
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t0
+
+    a_loc = torch.empty((n_q, d), dtype=torch.bfloat16, device="cuda")
+    a_full = torch.empty_like(a_loc)
+    lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
+    stats = [[torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)] for _ in range(n_layers)]
+    dW = [torch.empty((d, d), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    info = torch.zeros((n_layers,), dtype=torch.int32, device="cuda")
+    eps = torch.zeros((n_layers,), dtype=torch.float64, device="cuda")
+    ref = torch.zeros((n_layers,), dtype=torch.float64, device="cuda")
+    ws_solve = torch.empty(ispa.ispa_absorb_solve_workspace(d, n_layers), dtype=torch.uint8, device="cuda")
+    ws_err = torch.empty(ispa.ispa_layer_error_workspace(d, n_layers), dtype=torch.uint8, device="cuda")
+    Gs = [s[0] for s in stats]
+    Xs = [s[1] for s in stats]
+    Fs = [s[2] for s in stats]
+    Ws = [L.w for L in layers]
+
+    seg_keys = [sum(inputs.CONFIGS[3].segment_sizes(c)[k] for k in ("n_sink", "n_cur", "n_hist"))
+                for c in range(len(wl.chunks))]
+    flops_attn = sum(attn_flops(n_q, nk, H, dh) for nk in seg_keys) * n_layers
+    flops_stats = 4.0 * n_q * len(wl.chunks) * d * d * n_layers
+    flops_solve = 13.0 / 3.0 * d ** 3 * n_layers
+    flops_err = 6.0 * d ** 3 * n_layers
+    flops_step = flops_attn + flops_stats + flops_solve + flops_err
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    timing = {"attn": [], "stats": [], "solve": [], "error": []}
+
+    def step(record: bool):
+        for s in stats:
+            for t in s:
+                t.zero_()
+        for li, L in enumerate(layers):
+            for c, ch in enumerate(wl.chunks):
+                sk, sv = L.seg(ch.sink)
+                ck, cv = L.seg(ch.cur)
+                hk, hv = L.seg(ch.hist)
+                if record:
+                    e0, e1, e2 = ev(), ev(), ev()
+                    e0.record()
+                ispa.ispa_attn_dual(L.q[c], sk, sv, ck, cv, hk, hv, wl.scale, a_loc, a_full,
+                                    lse[0], lse[1], lse[2])
+                if record:
+                    e1.record()
+                ispa.ispa_absorb_accumulate(a_loc, a_full, stats[li][0], stats[li][1], stats[li][2])
+                if record:
+                    e2.record()
+                    timing["attn"].append((e0, e1, seg_keys[c]))
+                    timing["stats"].append((e1, e2))
+        if record:
+            e3, e4, e5 = ev(), ev(), ev()
+            e3.record()
+        ispa.ispa_absorb_solve(Gs, Xs, Ws, dW, wl.lam, info, ws_solve)
+        if record:
+            e4.record()
+        ispa.ispa_layer_error(Gs, Xs, Fs, Ws, dW, eps, ref, ws_err)
+        if record:
+            e5.record()
+            timing["solve"].append((e3, e4))
+            timing["error"].append((e4, e5))
+        eps_host = eps.cpu().numpy()        # synchronises: the ranking runs on the host
+        return ispa.ispa_rank_layers(eps_host.tolist(), min(wl.k_select, n_layers))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    # per-kernel event timing (separate pass, so the step timing below carries no event overhead)
+    step(True)
+    torch.cuda.synchronize()
+    att = [(a.elapsed_time(b), nk) for a, b, nk in timing["attn"]]
+    att_ms = sum(t for t, _ in att)
+    att_avg_ms = att_ms / len(att)
+    att_flops_per_launch = flops_attn / len(att)
+    stats_ms = sum(a.elapsed_time(b) for a, b in timing["stats"])
+    solve_ms = sum(a.elapsed_time(b) for a, b in timing["solve"])
+    err_ms = sum(a.elapsed_time(b) for a, b in timing["error"])
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        sel, flags = step(False)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    att_tflops = att_flops_per_launch / att_avg_ms / 1e9
+    info_h = info.cpu().tolist()
+    out = {
+        "metric": "dual-stream attn TFLOP/s (% MFMA peak); ΔW absorb ms/layer, 1.3B shape",
+        "value": round(flops_step / ms_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) queries/values, AR(1) rho=0.95 keys across latent frames, W ~ N(0,1/d))",
+        "config": {"workload": "wan1.3b-warmup", "layers": n_layers, "chunks": len(wl.chunks),
+                   "heads": H, "head_dim": dh, "queries_per_chunk": n_q,
+                   "keys_per_chunk": seg_keys, "lambda": wl.lam, "k_select": min(wl.k_select, n_layers)},
+        "attn_tflops": round(att_tflops, 1),
+        "attn_frac_mfma_peak": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+        "attn_ms_per_layer": round(att_ms / n_layers, 4),
+        "absorb_ms_per_layer": round((stats_ms + solve_ms + err_ms) / n_layers, 4),
+        "absorb_breakdown_ms_per_layer": {"statistics": round(stats_ms / n_layers, 4),
+                                          "solve": round(solve_ms / n_layers, 4),
+                                          "error": round(err_ms / n_layers, 4)},
+        "stats_tflops": round(flops_stats / stats_ms / 1e9, 1),
+        "solve_info_nonzero": int(sum(1 for x in info_h if x != 0)),
+        "selected_l_layers": sel,
+        "roofline": {"kernel": "attn_dual_bf16_kernel", "bound": "mfma",
+                     "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(att_avg_ms, 5),
+                     "flops_per_launch": att_flops_per_launch},
+        "setup_s": round(t_setup, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

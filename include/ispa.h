@@ -1,0 +1,178 @@
+/*
+ * ispa.h - C ABI of the ISPA hot path on AMD Instinct MI355X (gfx950).
+ *
+ * ISPA ("Instance-Specific Parametric Absorption", technical summary pages on gist.science, Italian
+ * and Japanese editions) compresses the KV cache of a streaming autoregressive video model: during a
+ * warmup every layer produces a full-context and a local-context attention output, the gap between
+ * them is absorbed into the output projection by a closed-form ridge solve, and the layers where that
+ * works best drop their history cache. This library implements that path's device work.
+ *
+ * Conventions (all entry points):
+ *  - Tensors are caller-owned device memory (allocated by the caller, e.g. PyTorch). The library
+ *    never allocates or frees device memory and keeps no state between calls. Scratch memory is
+ *    passed in through (ws, ws_bytes); the matching *_workspace() function gives the size needed.
+ *  - Every call validates its arguments on the host first, enqueues its kernels on `stream`
+ *    (a hipStream_t; NULL is the default stream) and returns without waiting. An argument error
+ *    returns before anything is enqueued. Nothing throws across the ABI.
+ *  - Layouts are row-major. Token-major activations: Q, K, V are [n, H, d_h] with a row stride (in
+ *    elements) between tokens of at least H*d_h; A outputs are [n_q, H*d_h] with heads concatenated
+ *    (column h*d_h + c). LSE outputs are [H, n_q] fp32, natural log.
+ *  - Device pointers must be 16-byte aligned; bf16 row strides must be multiples of 8 elements and
+ *    fp32 row strides multiples of 4.
+ *  - Status codes: ISPA_OK, ISPA_E_ARG (bad pointer, size or alignment), ISPA_E_UNSUPPORTED (valid but
+ *    not implemented: head_dim, dtype), ISPA_E_WORKSPACE (ws too small), ISPA_E_HIP (a HIP launch
+ *    failed; hipGetLastError is cleared).
+ */
+#ifndef ISPA_H
+#define ISPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ISPA_OK = 0,
+  ISPA_E_ARG = -1,
+  ISPA_E_UNSUPPORTED = -2,
+  ISPA_E_WORKSPACE = -3,
+  ISPA_E_HIP = -4
+} ispa_status;
+
+typedef enum { ISPA_F32 = 0, ISPA_BF16 = 1 } ispa_dtype;
+
+/* One KV-cache segment of a layer: keys and values [n, H, d_h] in the call's dtype.
+ * row_stride (elements) is the distance between consecutive tokens, >= H*d_h. n may be 0 (then k and
+ * v may be NULL). */
+typedef struct {
+  const void *k;
+  const void *v;
+  int64_t n;
+  int64_t row_stride;
+} ispa_kv_segment;
+
+/* ---------------------------------------------------------------------------------------------
+ * Dual-stream attention (ISPA page, section 2 "Framework Core", stage 1 "Dual-Stream Warmup", and
+ * its Decomposable Attention paragraph).
+ *
+ * For every head h and query i (the current-chunk tokens):
+ *   A_loc   = softmax attention of q_i over the local keys  L = sink U cur
+ *   A_full  = softmax attention of q_i over all keys        U = sink U cur U hist
+ *   lse_X   = log sum_{j in X} exp(softmax_scale * q_i . k_j)   for X = L, hist, U
+ * Both outputs come from one pass over the cache: the local keys are visited first and their
+ * normalised output and LSE are stored, then the same running softmax state continues over the
+ * history keys. No mask: every query sees every key of the three segments.
+ *
+ *   dt            ISPA_BF16 (bf16 in, fp32 accumulate, bf16 out) or ISPA_F32 (fp32 throughout)
+ *   n_heads       H >= 1; head_dim d_h in {64, 128}
+ *   softmax_scale tau > 0 (1/sqrt(d_h) in the usual case)
+ *   q             [n_q, H, d_h], row stride q_row_stride; n_q >= 0 (0 is a no-op)
+ *   sink, cur     local segments; sink.n + cur.n >= 1 (an empty local context is an argument error)
+ *   hist          history segment; hist.n may be 0: then a_full is bitwise a_loc, lse_hist = -inf
+ *                 and lse_full = lse_loc
+ *   a_loc         out [n_q, H*d_h] dtype dt, row stride H*d_h
+ *   a_full        out, same shape; NULL computes only the local branch (history is then ignored)
+ *   lse_loc       out [H, n_q] fp32 (may be NULL); lse_hist, lse_full likewise (NULL = not stored)
+ * ------------------------------------------------------------------------------------------- */
+ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                           const void *q, int64_t n_q, int64_t q_row_stride,
+                           ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                           void *a_loc, void *a_full,
+                           float *lse_loc, float *lse_hist, float *lse_full,
+                           void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Warmup statistics (ISPA page, section 2 stage 2 "Layer Absorb": the closed form needs
+ * A_loc^T A_loc and A_loc^T (A_full - A_loc) over the warmup rows; stage 1 says these rows are the
+ * warmup chunks' attention outputs).
+ *
+ * Adds one chunk of rows to the layer's running sums (fp32, no 1/N scaling):
+ *   G += A_loc^T A_loc      X += A_loc^T A_full      F += A_full^T A_full   (each [d, d])
+ * so that C = X - G = A_loc^T (A_full - A_loc) and H = F - X - X^T + G = D^T D with
+ * D = A_full - A_loc. The products only ever multiply exact input values (D is never rounded).
+ * G and F are exactly symmetric. The caller zeroes G, X, F before the first chunk; the sums are
+ * deterministic (no atomics) and can be saved and restored between chunks.
+ *
+ *   dt        ISPA_BF16 or ISPA_F32 (type of a_loc / a_full)
+ *   n_rows    rows in this chunk (>= 0); d = H*d_h (>= 1)
+ *   a_loc, a_full   [n_rows, d] row-major (row stride d)
+ *   G, X      [d, d] fp32, accumulated in place; F may be NULL when the error is not needed
+ *   ws        unused by the current kernels (ispa_absorb_accumulate_workspace returns 0)
+ * ------------------------------------------------------------------------------------------- */
+size_t ispa_absorb_accumulate_workspace(int64_t n_rows, int32_t d);
+ispa_status ispa_absorb_accumulate(ispa_dtype dt, int64_t n_rows, int32_t d,
+                                   const void *a_loc, const void *a_full,
+                                   float *G, float *X, float *F,
+                                   void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Closed-form absorb update (ISPA page, section 2 stage 2 "Layer Absorb", second display equation):
+ *   dW = (A_loc^T A_loc + lambda I)^-1 A_loc^T (A_full - A_loc) W = (G + lambda I)^-1 (X - G) W
+ * the minimiser of || A_loc (W + dW) - A_full W ||_F^2 + lambda || dW ||_F^2 (first display equation).
+ * Solved per layer by a blocked fp32 Cholesky factorisation G + lambda I = L L^T and two blocked
+ * triangular solves; batched over layers.
+ *
+ *   d          matrix size (>= 1); batch = number of layers (>= 0)
+ *   lambda     ridge weight (>= 0; 0 only if G is positive definite)
+ *   G, X       host arrays of `batch` device pointers to [d, d] fp32 statistics
+ *   W          host array of device pointers to [d, d] fp32: W[d_in, d_out] with y = A W, or, if
+ *              w_is_linear_weight, an nn.Linear weight [d_out, d_in] (y = A W^T)
+ *   dW         host array of device pointers, out [d, d] fp32 in the same orientation as W
+ *   info       device int32 [batch], out: 0 = ok, k > 0 = the leading minor of order k of
+ *              G + lambda I is not positive (dW of that layer is then undefined)
+ *   ws         device scratch of at least ispa_absorb_solve_workspace(d, batch) bytes
+ * ------------------------------------------------------------------------------------------- */
+size_t ispa_absorb_solve_workspace(int32_t d, int32_t batch);
+ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda,
+                              const float *const *G, const float *const *X,
+                              const float *const *W, int32_t w_is_linear_weight,
+                              float *const *dW, int32_t *info,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Reconstruction error per layer (ISPA page, section 2 "Dynamic Layer Selection": layers are ranked
+ * by their reconstruction error after the warmup). For the given dW (any dW, not only the optimum):
+ *   eps = || A_loc (W + dW) - A_full W ||_F^2
+ *       = <W, F W> - 2 <W + dW, X W> + <W + dW, G (W + dW)>      (sums over the warmup rows)
+ *   ref = || A_full W ||_F^2 = <W, F W>
+ * from the statistics of ispa_absorb_accumulate. Products in fp32, inner products in fp64.
+ *
+ *   G, X, F, W, dW   host arrays of `batch` device pointers ([d, d] fp32; W, dW oriented as in
+ *                    ispa_absorb_solve)
+ *   eps        device double [batch], out
+ *   ref        device double [batch], out (may be NULL)
+ *   ws         device scratch of at least ispa_layer_error_workspace(d, batch) bytes
+ * ------------------------------------------------------------------------------------------- */
+size_t ispa_layer_error_workspace(int32_t d, int32_t batch);
+ispa_status ispa_layer_error(int32_t d, int32_t batch,
+                             const float *const *G, const float *const *X, const float *const *F,
+                             const float *const *W, int32_t w_is_linear_weight,
+                             const float *const *dW, double *eps, double *ref,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Layer selection (ISPA page, section 2 "Dynamic Layer Selection" and stage 3 "Memory-Efficient
+ * Inference": the K layers with the lowest error become L-Layers, the other N - K stay F-Layers).
+ * Host-only, no GPU work. Ascending eps, ties to the lower layer index, NaN ranks last.
+ *
+ *   eps         host double [n_layers]
+ *   k           0 <= k <= n_layers
+ *   selected    host int32 [k], out: chosen layers in ascending-eps order (may be NULL if k == 0)
+ *   is_l_layer  host uint8 [n_layers], out: 1 for chosen layers (may be NULL)
+ * ------------------------------------------------------------------------------------------- */
+ispa_status ispa_rank_layers(const double *eps, int32_t n_layers, int32_t k,
+                             int32_t *selected, uint8_t *is_l_layer);
+
+/* Human-readable name of a status code (static storage). */
+const char *ispa_status_string(ispa_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t ispa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISPA_H */

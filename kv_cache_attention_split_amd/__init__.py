@@ -1,0 +1,171 @@
+"""Python binding of libispa.so, the gfx950 library for ISPA's dual-stream attention and Layer Absorb.
+
+The functions below carry the names of the C ABI (include/ispa.h) and only marshal arguments: torch
+tensors become device pointers, sizes and strides, and the call is enqueued on the current HIP
+stream (or the one given). Every step of the computation runs in the library's HIP kernels; there is
+no fallback. If libispa.so is missing, importing the functions raises.
+
+Build the library with ``python -m kv_cache_attention_split_amd.build`` (or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVSegment, lib, lib_path,  # noqa: F401
+                   status_string)
+
+__all__ = [
+    "ispa_attn_dual", "ispa_absorb_accumulate", "ispa_absorb_accumulate_workspace",
+    "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_layer_error",
+    "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_status_string", "ispa_version",
+    "IspaError", "lib_path",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ISPA_BF16
+    if t.dtype == torch.float32:
+        return ISPA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _check(status: int, what: str) -> None:
+    if status != ISPA_OK:
+        raise IspaError(status, f"{what}: {status_string(status)}")
+
+
+def _seg(k, v, n_heads: int, head_dim: int) -> KVSegment:
+    if k is None or k.shape[0] == 0:
+        return KVSegment(None, None, 0, n_heads * head_dim)
+    for t in (k, v):
+        if t.dim() != 3 or t.shape[1] != n_heads or t.shape[2] != head_dim:
+            raise ValueError(f"K/V segment must be [n, {n_heads}, {head_dim}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != head_dim:
+            raise ValueError("K/V segment rows must be contiguous over (H, d_h)")
+    if k.shape[0] != v.shape[0] or k.stride(0) != v.stride(0):
+        raise ValueError("K and V of a segment must have the same length and row stride")
+    return KVSegment(k.data_ptr(), v.data_ptr(), int(k.shape[0]), int(k.stride(0)))
+
+
+def ispa_attn_dual(q, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v, softmax_scale: float,
+                   a_loc, a_full=None, lse_loc=None, lse_hist=None, lse_full=None, stream=None) -> None:
+    """Dual-stream attention (see ispa_attn_dual in include/ispa.h).
+
+    q: [n_q, H, d_h]; *_k/*_v: [n, H, d_h] (a segment may be None or have n = 0); a_loc / a_full:
+    [n_q, H*d_h] preallocated outputs of q's dtype; lse_*: [H, n_q] float32 outputs or None.
+    """
+    n_q, H, dh = (int(x) for x in q.shape)
+    if q.stride(2) != 1 or q.stride(1) != dh:
+        raise ValueError("q rows must be contiguous over (H, d_h)")
+    for o in (a_loc, a_full):
+        if o is not None and (tuple(o.shape) != (n_q, H * dh) or not o.is_contiguous() or o.dtype != q.dtype):
+            raise ValueError("outputs must be contiguous [n_q, H*d_h] of q's dtype")
+    torch = _torch()
+    for o in (lse_loc, lse_hist, lse_full):
+        if o is not None and (tuple(o.shape) != (H, n_q) or not o.is_contiguous() or o.dtype != torch.float32):
+            raise ValueError("LSE outputs must be contiguous float32 [H, n_q]")
+    st = lib().ispa_attn_dual(
+        _dtype_code(q), H, dh, ctypes.c_float(softmax_scale), _ptr(q), n_q, int(q.stride(0)),
+        _seg(sink_k, sink_v, H, dh), _seg(cur_k, cur_v, H, dh), _seg(hist_k, hist_v, H, dh),
+        _ptr(a_loc), _ptr(a_full), _ptr(lse_loc), _ptr(lse_hist), _ptr(lse_full), _stream_handle(stream))
+    _check(st, "ispa_attn_dual")
+
+
+def ispa_absorb_accumulate_workspace(n_rows: int, d: int) -> int:
+    return int(lib().ispa_absorb_accumulate_workspace(int(n_rows), int(d)))
+
+
+def ispa_absorb_accumulate(a_loc, a_full, G, X, F=None, ws=None, stream=None) -> None:
+    """G += A_loc^T A_loc, X += A_loc^T A_full, F += A_full^T A_full (fp32 [d, d], in place)."""
+    n, d = (int(x) for x in a_loc.shape)
+    if tuple(a_full.shape) != (n, d) or a_full.dtype != a_loc.dtype:
+        raise ValueError("a_loc and a_full must match")
+    for t in (a_loc, a_full, G, X) + ((F,) if F is not None else ()):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    st = lib().ispa_absorb_accumulate(
+        _dtype_code(a_loc), n, d, _ptr(a_loc), _ptr(a_full), _ptr(G), _ptr(X), _ptr(F),
+        _ptr(ws), 0 if ws is None else int(ws.numel() * ws.element_size()), _stream_handle(stream))
+    _check(st, "ispa_absorb_accumulate")
+
+
+def _ptr_array(ts: Sequence) -> ctypes.Array:
+    arr = (ctypes.c_void_p * max(1, len(ts)))()
+    for i, t in enumerate(ts):
+        if not t.is_contiguous():
+            raise ValueError("per-layer matrices must be contiguous")
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def ispa_absorb_solve_workspace(d: int, batch: int) -> int:
+    return int(lib().ispa_absorb_solve_workspace(int(d), int(batch)))
+
+
+def ispa_absorb_solve(G: Sequence, X: Sequence, W: Sequence, dW: Sequence, lam: float, info,
+                      ws, w_is_linear_weight: bool = False, stream=None) -> None:
+    """dW_l = (G_l + lam I)^-1 (X_l - G_l) W_l for each layer l (lists of [d, d] fp32 tensors)."""
+    batch = len(G)
+    d = int(G[0].shape[0]) if batch else 0
+    if not (len(X) == len(W) == len(dW) == batch):
+        raise ValueError("G, X, W, dW must have one entry per layer")
+    st = lib().ispa_absorb_solve(
+        d, batch, ctypes.c_float(lam), _ptr_array(G), _ptr_array(X), _ptr_array(W),
+        1 if w_is_linear_weight else 0, _ptr_array(dW), _ptr(info), _ptr(ws),
+        0 if ws is None else int(ws.numel() * ws.element_size()), _stream_handle(stream))
+    _check(st, "ispa_absorb_solve")
+
+
+def ispa_layer_error_workspace(d: int, batch: int) -> int:
+    return int(lib().ispa_layer_error_workspace(int(d), int(batch)))
+
+
+def ispa_layer_error(G: Sequence, X: Sequence, F: Sequence, W: Sequence, dW: Sequence, eps, ref=None,
+                     ws=None, w_is_linear_weight: bool = False, stream=None) -> None:
+    """eps_l = ||A_loc (W + dW) - A_full W||_F^2 from the statistics; ref_l = ||A_full W||_F^2."""
+    batch = len(G)
+    d = int(G[0].shape[0]) if batch else 0
+    st = lib().ispa_layer_error(
+        d, batch, _ptr_array(G), _ptr_array(X), _ptr_array(F), _ptr_array(W),
+        1 if w_is_linear_weight else 0, _ptr_array(dW), _ptr(eps), _ptr(ref), _ptr(ws),
+        0 if ws is None else int(ws.numel() * ws.element_size()), _stream_handle(stream))
+    _check(st, "ispa_layer_error")
+
+
+def ispa_rank_layers(eps: Sequence[float], k: int):
+    """Host-only layer selection: (selected indices in ascending-eps order, 0/1 L-Layer flags)."""
+    n = len(eps)
+    e = (ctypes.c_double * max(1, n))(*[float(x) for x in eps])
+    sel = (ctypes.c_int32 * max(1, k))()
+    flag = (ctypes.c_uint8 * max(1, n))()
+    st = lib().ispa_rank_layers(e, n, int(k), sel, flag)
+    _check(st, "ispa_rank_layers")
+    return [int(sel[i]) for i in range(k)], [int(flag[i]) for i in range(n)]
+
+
+def ispa_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def ispa_version() -> int:
+    return int(lib().ispa_version())

@@ -1,0 +1,502 @@
+// C ABI of the ISPA hot path (declared in include/ispa.h): argument validation, workspace layout,
+// and the launch sequences. Validation runs before any HIP call, so argument errors are reported
+// without touching the GPU.
+#include "ispa.h"
+#include "ispa_internal.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+using namespace ispa;
+
+namespace {
+
+constexpr int32_t kVersion = 100;   // 0.1.0
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline ispa_status hip_status(hipError_t e) { return e == hipSuccess ? ISPA_OK : ISPA_E_HIP; }
+
+#define ISPA_TRY(expr)                             \
+  do {                                             \
+    hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return ISPA_E_HIP;       \
+  } while (0)
+
+ispa_status check_segment(const ispa_kv_segment &s, int64_t min_stride, int64_t align_elems) {
+  if (s.n < 0) return ISPA_E_ARG;
+  if (s.n == 0) return ISPA_OK;
+  if (s.k == nullptr || s.v == nullptr) return ISPA_E_ARG;
+  if (!aligned16(s.k) || !aligned16(s.v)) return ISPA_E_ARG;
+  if (s.row_stride < min_stride || s.row_stride % align_elems != 0) return ISPA_E_ARG;
+  return ISPA_OK;
+}
+
+// ---- workspace layouts ---------------------------------------------------------------------------
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int solve_nb(int d) { return (d % 128 == 0) ? 128 : 64; }
+
+struct SolveLayout {
+  size_t mat;            // bytes of one d x d fp32 matrix (padded)
+  size_t linv;           // bytes of one layer's diagonal-block inverses
+  size_t per_layer;
+  size_t total(int batch) const { return per_layer * (size_t)batch; }
+};
+SolveLayout solve_layout(int d) {
+  SolveLayout s;
+  const int nb = solve_nb(d);
+  const int nt = (d + nb - 1) / nb;
+  s.mat = round_up((size_t)d * d * sizeof(float), 256);
+  s.linv = round_up((size_t)nt * nb * nb * sizeof(float), 256);
+  s.per_layer = 3 * s.mat + s.linv;     // L, B, W (standard orientation), Linv blocks
+  return s;
+}
+
+struct ErrLayout {
+  size_t mat, part;
+  int tiles;
+  size_t total(int batch) const { return (2 * mat + 3 * part) * (size_t)batch; }
+};
+ErrLayout err_layout(int d) {
+  ErrLayout e;
+  e.mat = round_up((size_t)d * d * sizeof(float), 256);
+  e.tiles = gemm_tiles(d, d);
+  e.part = round_up((size_t)e.tiles * sizeof(double), 256);
+  return e;
+}
+
+ispa_status check_square_batch(int32_t d, int32_t batch) {
+  if (d <= 0 || batch < 0) return ISPA_E_ARG;
+  if (d % 64 != 0) return ISPA_E_UNSUPPORTED;
+  return ISPA_OK;
+}
+
+ispa_status check_ptr_array(const float *const *a, int32_t batch) {
+  if (batch == 0) return ISPA_OK;
+  if (a == nullptr) return ISPA_E_ARG;
+  for (int32_t i = 0; i < batch; ++i)
+    if (a[i] == nullptr || !aligned16(a[i])) return ISPA_E_ARG;
+  return ISPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ispa_version(void) { return kVersion; }
+
+const char *ispa_status_string(ispa_status s) {
+  switch (s) {
+    case ISPA_OK: return "ISPA_OK";
+    case ISPA_E_ARG: return "ISPA_E_ARG: invalid argument (pointer, size, stride or alignment)";
+    case ISPA_E_UNSUPPORTED: return "ISPA_E_UNSUPPORTED: valid but not implemented (dtype, head_dim, d)";
+    case ISPA_E_WORKSPACE: return "ISPA_E_WORKSPACE: workspace too small";
+    case ISPA_E_HIP: return "ISPA_E_HIP: a HIP call failed";
+  }
+  return "ISPA: unknown status";
+}
+
+// ------------------------------------------------------------------------------------------------
+ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                           const void *q, int64_t n_q, int64_t q_row_stride, ispa_kv_segment sink,
+                           ispa_kv_segment cur, ispa_kv_segment hist, void *a_loc, void *a_full,
+                           float *lse_loc, float *lse_hist, float *lse_full, void *stream) {
+  if (dt != ISPA_BF16 && dt != ISPA_F32) return ISPA_E_UNSUPPORTED;
+  if (n_heads <= 0 || n_q < 0) return ISPA_E_ARG;
+  if (head_dim != 64 && head_dim != 128) return ISPA_E_UNSUPPORTED;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return ISPA_E_ARG;
+  if (n_q > INT32_MAX / 2) return ISPA_E_ARG;
+  const int64_t width = (int64_t)n_heads * head_dim;
+  const int64_t align_elems = dt == ISPA_BF16 ? 8 : 4;
+  if (sink.n < 0 || cur.n < 0 || hist.n < 0) return ISPA_E_ARG;
+  if (sink.n + cur.n < 1) return ISPA_E_ARG;
+  ispa_status st;
+  if ((st = check_segment(sink, width, align_elems)) != ISPA_OK) return st;
+  if ((st = check_segment(cur, width, align_elems)) != ISPA_OK) return st;
+  if (a_full != nullptr && (st = check_segment(hist, width, align_elems)) != ISPA_OK) return st;
+  if (n_q == 0) return ISPA_OK;
+  if (q == nullptr || !aligned16(q) || q_row_stride < width || q_row_stride % align_elems != 0)
+    return ISPA_E_ARG;
+  if (a_loc == nullptr || !aligned16(a_loc)) return ISPA_E_ARG;
+  if (a_full != nullptr && !aligned16(a_full)) return ISPA_E_ARG;
+
+  AttnArgs a;
+  a.q = q;
+  a.q_stride = q_row_stride;
+  a.sink_k = sink.k;
+  a.sink_v = sink.v;
+  a.sink_n = sink.n;
+  a.sink_stride = sink.row_stride;
+  a.cur_k = cur.k;
+  a.cur_v = cur.v;
+  a.cur_n = cur.n;
+  a.cur_stride = cur.row_stride;
+  const bool want_full = a_full != nullptr;
+  a.hist_k = want_full ? hist.k : nullptr;
+  a.hist_v = want_full ? hist.v : nullptr;
+  a.hist_n = want_full ? hist.n : 0;
+  a.hist_stride = want_full ? hist.row_stride : 0;
+  a.a_loc = a_loc;
+  a.a_full = a_full;
+  a.lse_loc = lse_loc;
+  a.lse_hist = want_full ? lse_hist : nullptr;
+  a.lse_full = want_full ? lse_full : nullptr;
+  a.n_q = (int32_t)n_q;
+  a.n_heads = n_heads;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = dt == ISPA_BF16 ? launch_attn_bf16(a, head_dim, s) : launch_attn_f32(a, head_dim, s);
+  return hip_status(e);
+}
+
+// ------------------------------------------------------------------------------------------------
+size_t ispa_absorb_accumulate_workspace(int64_t n_rows, int32_t d) {
+  (void)n_rows;
+  (void)d;
+  return 0;
+}
+
+ispa_status ispa_absorb_accumulate(ispa_dtype dt, int64_t n_rows, int32_t d, const void *a_loc,
+                                   const void *a_full, float *G, float *X, float *F, void *ws,
+                                   size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (dt != ISPA_BF16 && dt != ISPA_F32) return ISPA_E_UNSUPPORTED;
+  if (n_rows < 0 || d <= 0) return ISPA_E_ARG;
+  if (d % 64 != 0) return ISPA_E_UNSUPPORTED;
+  if (G == nullptr || X == nullptr || !aligned16(G) || !aligned16(X)) return ISPA_E_ARG;
+  if (F != nullptr && !aligned16(F)) return ISPA_E_ARG;
+  if (n_rows == 0) return ISPA_OK;
+  if (a_loc == nullptr || a_full == nullptr || !aligned16(a_loc) || !aligned16(a_full)) return ISPA_E_ARG;
+  if (n_rows > INT32_MAX) return ISPA_E_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == ISPA_BF16)
+    return hip_status(launch_gram_bf16(n_rows, d, (const uint16_t *)a_loc, (const uint16_t *)a_full,
+                                       G, X, F, s));
+  // fp32 rows: three GEMMs  G += A_loc^T A_loc, X += A_loc^T A_full, F += A_full^T A_full
+  GemmShape sh{};
+  sh.M = d;
+  sh.N = d;
+  sh.K = (int)n_rows;
+  sh.lda = d;
+  sh.ldb = d;
+  sh.ldc = d;
+  sh.ta = 1;
+  sh.tb = 0;
+  sh.alpha = 1.f;
+  sh.beta = 1.f;
+  GemmBatch b{};
+  const float *al = (const float *)a_loc, *af = (const float *)a_full;
+  int cnt = 0;
+  b.A[cnt] = al; b.B[cnt] = al; b.C[cnt] = G; ++cnt;
+  b.A[cnt] = al; b.B[cnt] = af; b.C[cnt] = X; ++cnt;
+  if (F != nullptr) { b.A[cnt] = af; b.B[cnt] = af; b.C[cnt] = F; ++cnt; }
+  return hip_status(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+}
+
+// ------------------------------------------------------------------------------------------------
+size_t ispa_absorb_solve_workspace(int32_t d, int32_t batch) {
+  if (d <= 0 || batch <= 0) return 0;
+  return solve_layout(d).total(batch);
+}
+
+ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const float *const *G,
+                              const float *const *X, const float *const *W, int32_t w_is_linear_weight,
+                              float *const *dW, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
+  ispa_status st = check_square_batch(d, batch);
+  if (st != ISPA_OK) return st;
+  if (!(lambda >= 0.f) || !std::isfinite(lambda)) return ISPA_E_ARG;
+  if (batch == 0) return ISPA_OK;
+  if ((st = check_ptr_array(G, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array(X, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array(W, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array((const float *const *)dW, batch)) != ISPA_OK) return st;
+  if (info == nullptr) return ISPA_E_ARG;
+  const SolveLayout lay = solve_layout(d);
+  if (ws == nullptr || ws_bytes < lay.total(batch) || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return ws == nullptr || ws_bytes < lay.total(batch) ? ISPA_E_WORKSPACE : ISPA_E_ARG;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int nb = solve_nb(d);
+  const int nt = (d + nb - 1) / nb;
+  const int64_t mat_f = (int64_t)(lay.mat / sizeof(float));
+  const int64_t per_f = (int64_t)(lay.per_layer / sizeof(float));
+
+  for (int p0 = 0; p0 < batch; p0 += kMaxBatch) {
+    const int cnt = std::min(batch - p0, kMaxBatch);
+    float *base = (float *)ws + (int64_t)p0 * per_f;
+    // per-layer regions: [L | B | Wn | Linv], stride per_f
+    auto Lp = [&](int i) { return base + (int64_t)i * per_f; };
+    auto Bp = [&](int i) { return base + (int64_t)i * per_f + mat_f; };
+    auto Wp = [&](int i) { return base + (int64_t)i * per_f + 2 * mat_f; };
+    auto Vp = [&](int i) { return base + (int64_t)i * per_f + 3 * mat_f; };
+    const int64_t linv_blk = (int64_t)nb * nb;
+
+    ISPA_TRY(launch_zero_i32(info + p0, cnt, s));
+    CPtrBatch g{};
+    for (int i = 0; i < cnt; ++i) g.p[i] = G[p0 + i];
+    ISPA_TRY(launch_shift_copy(g, Lp(0), per_f, d, lambda, cnt, s));
+
+    // W in the standard orientation (y = A W)
+    const float *Wuse[kMaxBatch];
+    if (w_is_linear_weight) {
+      CPtrBatch in{};
+      PtrBatch out{};
+      for (int i = 0; i < cnt; ++i) {
+        in.p[i] = W[p0 + i];
+        out.p[i] = Wp(i);
+        Wuse[i] = Wp(i);
+      }
+      ISPA_TRY(launch_transpose(in, out, d, cnt, s));
+    } else {
+      for (int i = 0; i < cnt; ++i) Wuse[i] = W[p0 + i];
+    }
+
+    // B = (X - G) W
+    {
+      GemmBatch b{};
+      GemmShape sh{};
+      sh.M = d; sh.N = d; sh.K = d;
+      sh.lda = d; sh.ldb = d; sh.ldc = d;
+      sh.ta = 0; sh.tb = 0; sh.sub = 1;
+      sh.alpha = 1.f; sh.beta = 0.f;
+      for (int i = 0; i < cnt; ++i) {
+        b.A[i] = X[p0 + i];
+        b.A2[i] = G[p0 + i];
+        b.B[i] = Wuse[i];
+        b.C[i] = Bp(i);
+      }
+      ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+    }
+
+    // blocked right-looking Cholesky: L L^T = G + lambda I
+    for (int k = 0; k < nt; ++k) {
+      const int k0 = k * nb;
+      ISPA_TRY(launch_potrf_diag(Lp(0), per_f, d, k0, nb, Vp(0) + k * linv_blk, per_f, info + p0, cnt, s));
+      const int rem = d - k0 - nb;
+      if (rem <= 0) continue;
+      // panel: L[k0+nb:, k0:k0+nb] = A[k0+nb:, k0:k0+nb] Linv_k^T
+      {
+        GemmBatch b{};
+        GemmShape sh{};
+        sh.M = rem; sh.N = nb; sh.K = nb;
+        sh.lda = d; sh.ldb = nb; sh.ldc = d;
+        sh.ta = 0; sh.tb = 1;
+        sh.alpha = 1.f; sh.beta = 0.f;
+        for (int i = 0; i < cnt; ++i) {
+          float *panel = Lp(i) + (int64_t)(k0 + nb) * d + k0;
+          b.A[i] = panel;
+          b.B[i] = Vp(i) + k * linv_blk;
+          b.C[i] = panel;
+        }
+        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      }
+      // trailing update (lower tiles): A22 -= L21 L21^T
+      {
+        GemmBatch b{};
+        GemmShape sh{};
+        sh.M = rem; sh.N = rem; sh.K = nb;
+        sh.lda = d; sh.ldb = d; sh.ldc = d;
+        sh.ta = 0; sh.tb = 1; sh.lower = 1;
+        sh.alpha = -1.f; sh.beta = 1.f;
+        for (int i = 0; i < cnt; ++i) {
+          const float *panel = Lp(i) + (int64_t)(k0 + nb) * d + k0;
+          b.A[i] = panel;
+          b.B[i] = panel;
+          b.C[i] = Lp(i) + (int64_t)(k0 + nb) * d + k0 + nb;
+        }
+        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      }
+    }
+
+    // forward substitution: L Y = B, block rows top to bottom
+    for (int k = 0; k < nt; ++k) {
+      const int k0 = k * nb;
+      {
+        GemmBatch b{};
+        GemmShape sh{};
+        sh.M = nb; sh.N = d; sh.K = nb;
+        sh.lda = nb; sh.ldb = d; sh.ldc = d;
+        sh.ta = 0; sh.tb = 0;
+        sh.alpha = 1.f; sh.beta = 0.f;
+        for (int i = 0; i < cnt; ++i) {
+          b.A[i] = Vp(i) + k * linv_blk;
+          b.B[i] = Bp(i) + (int64_t)k0 * d;
+          b.C[i] = Bp(i) + (int64_t)k0 * d;
+        }
+        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      }
+      const int rem = d - k0 - nb;
+      if (rem <= 0) continue;
+      {
+        GemmBatch b{};
+        GemmShape sh{};
+        sh.M = rem; sh.N = d; sh.K = nb;
+        sh.lda = d; sh.ldb = d; sh.ldc = d;
+        sh.ta = 0; sh.tb = 0;
+        sh.alpha = -1.f; sh.beta = 1.f;
+        for (int i = 0; i < cnt; ++i) {
+          b.A[i] = Lp(i) + (int64_t)(k0 + nb) * d + k0;
+          b.B[i] = Bp(i) + (int64_t)k0 * d;
+          b.C[i] = Bp(i) + (int64_t)(k0 + nb) * d;
+        }
+        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      }
+    }
+    // back substitution: L^T dW = Y, block rows bottom to top
+    for (int k = nt - 1; k >= 0; --k) {
+      const int k0 = k * nb;
+      {
+        GemmBatch b{};
+        GemmShape sh{};
+        sh.M = nb; sh.N = d; sh.K = nb;
+        sh.lda = nb; sh.ldb = d; sh.ldc = d;
+        sh.ta = 1; sh.tb = 0;
+        sh.alpha = 1.f; sh.beta = 0.f;
+        for (int i = 0; i < cnt; ++i) {
+          b.A[i] = Vp(i) + k * linv_blk;
+          b.B[i] = Bp(i) + (int64_t)k0 * d;
+          b.C[i] = Bp(i) + (int64_t)k0 * d;
+        }
+        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      }
+      if (k0 == 0) continue;
+      {
+        GemmBatch b{};
+        GemmShape sh{};
+        sh.M = k0; sh.N = d; sh.K = nb;
+        sh.lda = d; sh.ldb = d; sh.ldc = d;
+        sh.ta = 1; sh.tb = 0;
+        sh.alpha = -1.f; sh.beta = 1.f;
+        for (int i = 0; i < cnt; ++i) {
+          b.A[i] = Lp(i) + (int64_t)k0 * d;     // opA[r][kk] = L[k0 + kk][r], r < k0
+          b.B[i] = Bp(i) + (int64_t)k0 * d;
+          b.C[i] = Bp(i);
+        }
+        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      }
+    }
+    // dW in the caller's orientation
+    CPtrBatch in{};
+    PtrBatch out{};
+    for (int i = 0; i < cnt; ++i) {
+      in.p[i] = Bp(i);
+      out.p[i] = dW[p0 + i];
+    }
+    if (w_is_linear_weight)
+      ISPA_TRY(launch_transpose(in, out, d, cnt, s));
+    else
+      ISPA_TRY(launch_copy(in, out, d, cnt, s));
+  }
+  return ISPA_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+size_t ispa_layer_error_workspace(int32_t d, int32_t batch) {
+  if (d <= 0 || batch <= 0) return 0;
+  return err_layout(d).total(batch);
+}
+
+ispa_status ispa_layer_error(int32_t d, int32_t batch, const float *const *G, const float *const *X,
+                             const float *const *F, const float *const *W, int32_t w_is_linear_weight,
+                             const float *const *dW, double *eps, double *ref, void *ws, size_t ws_bytes,
+                             void *stream) {
+  ispa_status st = check_square_batch(d, batch);
+  if (st != ISPA_OK) return st;
+  if (batch == 0) return ISPA_OK;
+  if ((st = check_ptr_array(G, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array(X, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array(F, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array(W, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array(dW, batch)) != ISPA_OK) return st;
+  if (eps == nullptr) return ISPA_E_ARG;
+  const ErrLayout lay = err_layout(d);
+  if (ws == nullptr || ws_bytes < lay.total(batch)) return ISPA_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ISPA_E_ARG;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t mat_f = (int64_t)(lay.mat / sizeof(float));
+  float *mats = (float *)ws;                                        // [batch][2][mat]
+  double *part = (double *)((char *)ws + 2 * lay.mat * (size_t)batch);   // [3][batch][part]
+  const int64_t part_d = (int64_t)(lay.part / sizeof(double));
+
+  for (int p0 = 0; p0 < batch; p0 += kMaxBatch) {
+    const int cnt = std::min(batch - p0, kMaxBatch);
+    auto Wn = [&](int i) { return mats + (int64_t)(p0 + i) * 2 * mat_f; };
+    auto Wp = [&](int i) { return mats + (int64_t)(p0 + i) * 2 * mat_f + mat_f; };
+    const float *Wuse[kMaxBatch];
+    if (w_is_linear_weight) {
+      CPtrBatch in{}, in2{}, a{}, b{};
+      PtrBatch out{}, out2{}, o{};
+      for (int i = 0; i < cnt; ++i) {
+        in.p[i] = W[p0 + i];
+        out.p[i] = Wn(i);
+        in2.p[i] = dW[p0 + i];
+        out2.p[i] = Wp(i);
+        a.p[i] = Wn(i);
+        b.p[i] = Wp(i);
+        o.p[i] = Wp(i);
+        Wuse[i] = Wn(i);
+      }
+      ISPA_TRY(launch_transpose(in, out, d, cnt, s));
+      ISPA_TRY(launch_transpose(in2, out2, d, cnt, s));
+      ISPA_TRY(launch_add(a, b, o, d, cnt, s));
+    } else {
+      CPtrBatch a{}, b{};
+      PtrBatch o{};
+      for (int i = 0; i < cnt; ++i) {
+        a.p[i] = W[p0 + i];
+        b.p[i] = dW[p0 + i];
+        o.p[i] = Wp(i);
+        Wuse[i] = W[p0 + i];
+      }
+      ISPA_TRY(launch_add(a, b, o, d, cnt, s));
+    }
+    GemmShape sh{};
+    sh.M = d; sh.N = d; sh.K = d;
+    sh.lda = d; sh.ldb = d; sh.ldc = d; sh.lde = d;
+    sh.ta = 0; sh.tb = 0; sh.dot = 1;
+    sh.alpha = 1.f; sh.beta = 0.f;
+    // term 0: <W, F W>   term 1: <W', X W>   term 2: <W', G W'>   (W' = W + dW)
+    for (int term = 0; term < 3; ++term) {
+      GemmBatch b{};
+      for (int i = 0; i < cnt; ++i) {
+        b.A[i] = term == 0 ? F[p0 + i] : term == 1 ? X[p0 + i] : G[p0 + i];
+        b.B[i] = term == 2 ? Wp(i) : Wuse[i];
+        b.E[i] = term == 0 ? Wuse[i] : Wp(i);
+      }
+      ISPA_TRY(launch_gemm_f32(b, cnt, sh, part + ((int64_t)term * batch + p0) * part_d, part_d, s));
+    }
+  }
+  const double coef_eps[3] = {1.0, -2.0, 1.0};
+  ISPA_TRY(launch_reduce_partials(part, batch, part_d, lay.tiles, 3, coef_eps, eps, s));
+  if (ref != nullptr) {
+    const double coef_ref[1] = {1.0};
+    ISPA_TRY(launch_reduce_partials(part, batch, part_d, lay.tiles, 1, coef_ref, ref, s));
+  }
+  return ISPA_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+ispa_status ispa_rank_layers(const double *eps, int32_t n_layers, int32_t k, int32_t *selected,
+                             uint8_t *is_l_layer) {
+  if (n_layers < 0 || k < 0 || k > n_layers) return ISPA_E_ARG;
+  if (n_layers > 0 && eps == nullptr) return ISPA_E_ARG;
+  if (k > 0 && selected == nullptr) return ISPA_E_ARG;
+  std::vector<int32_t> order(n_layers);
+  std::iota(order.begin(), order.end(), 0);
+  auto key = [&](int32_t i) { return std::isnan(eps[i]) ? INFINITY : eps[i]; };
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return key(a) < key(b); });
+  for (int32_t i = 0; i < k; ++i) selected[i] = order[i];
+  if (is_l_layer != nullptr) {
+    std::memset(is_l_layer, 0, (size_t)n_layers);
+    for (int32_t i = 0; i < k; ++i) is_l_layer[order[i]] = 1;
+  }
+  return ISPA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the HIP kernel files.
+// Nothing here is part of the public ABI (include/ispa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace ispa {
+
+// ------------------------------------------------------------------------------------------------
+// Attention
+// ------------------------------------------------------------------------------------------------
+struct AttnArgs {
+  const void *q;
+  int64_t q_stride;                 // elements between query tokens
+  const void *sink_k, *sink_v;
+  int64_t sink_n, sink_stride;
+  const void *cur_k, *cur_v;
+  int64_t cur_n, cur_stride;
+  const void *hist_k, *hist_v;
+  int64_t hist_n, hist_stride;      // hist_n is 0 when only the local branch is wanted
+  void *a_loc, *a_full;
+  float *lse_loc, *lse_hist, *lse_full;
+  int32_t n_q, n_heads;
+  float scale_log2;                 // softmax_scale * log2(e)
+};
+
+hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs &a, int head_dim, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------------
+// Gram accumulation (bf16 rows, fp32 sums)
+// ------------------------------------------------------------------------------------------------
+hipError_t launch_gram_bf16(int64_t n_rows, int d, const uint16_t *a_loc, const uint16_t *a_full,
+                            float *G, float *X, float *F, hipStream_t s);
+
+// ------------------------------------------------------------------------------------------------
+// fp32 batched GEMM on MFMA:  C[i][j] = alpha * sum_k opA[i][k] opB[k][j] + beta * C[i][j]
+//   ta = 0: opA[i][k] = A[i*lda + k]        ta = 1: opA[i][k] = A[k*lda + i]
+//   tb = 0: opB[k][j] = B[k*ldb + j]        tb = 1: opB[k][j] = B[j*ldb + k]
+//   a2 != NULL (ta = 0 only): opA = A - A2 elementwise (same lda)
+//   lower: skip 128x128 output tiles lying strictly above the diagonal (col0 > row0 + 127)
+//   dot mode (E != NULL): instead of storing C, write per-tile partial sums
+//     sum_{tile} E[i*lde + j] * (alpha * (AB)[i][j]) in fp64 to part[p * tiles + tile]
+// ------------------------------------------------------------------------------------------------
+constexpr int kMaxGemmBatch = 48;
+
+struct GemmBatch {
+  const float *A[kMaxGemmBatch];
+  const float *A2[kMaxGemmBatch];
+  const float *B[kMaxGemmBatch];
+  float *C[kMaxGemmBatch];
+  const float *E[kMaxGemmBatch];
+};
+
+struct GemmShape {
+  int M, N, K;
+  int lda, ldb, ldc, lde;
+  int ta, tb, lower, sub, dot;
+  float alpha, beta;
+};
+
+// Launch one batched GEMM of `count` problems (count <= kMaxGemmBatch). `part` is required in dot mode.
+hipError_t launch_gemm_f32(const GemmBatch &b, int count, const GemmShape &sh, double *part,
+                           int64_t part_stride, hipStream_t s);
+int gemm_tiles(int M, int N);     // number of output tiles (partials per problem in dot mode)
+
+// Sum the dot partials per problem in a fixed order (deterministic), over `terms` groups:
+//   out[p] = sum_g coef[g] * sum_{t < tiles} part[(g * count + p) * stride + t]
+hipError_t launch_reduce_partials(const double *part, int count, int64_t stride, int tiles, int terms,
+                                  const double *coef /* host, terms <= 4 */, double *out,
+                                  hipStream_t s);
+
+// ------------------------------------------------------------------------------------------------
+// Blocked Cholesky building blocks
+// ------------------------------------------------------------------------------------------------
+constexpr int kMaxBatch = 48;
+struct PtrBatch {
+  float *p[kMaxBatch];
+};
+struct CPtrBatch {
+  const float *p[kMaxBatch];
+};
+
+// L = G + lambda I (full copy) for each layer
+hipError_t launch_shift_copy(const CPtrBatch &G, float *L, int64_t L_stride, int d, float lambda,
+                             int count, hipStream_t s);
+// Factor the nb x nb diagonal block at (k0, k0) of each L in place (lower Cholesky) and write its
+// inverse to Linv (nb x nb, row-major). info[layer] records the first failing column (1-based).
+hipError_t launch_potrf_diag(float *L, int64_t L_stride, int d, int k0, int nb, float *Linv,
+                             int64_t Linv_stride, int32_t *info, int count, hipStream_t s);
+// out = in^T for d x d matrices (batch, per-layer pointers)
+hipError_t launch_transpose(const CPtrBatch &in, const PtrBatch &out, int d, int count, hipStream_t s);
+// out = a + b (elementwise, d x d)
+hipError_t launch_add(const CPtrBatch &a, const CPtrBatch &b, const PtrBatch &out, int d, int count,
+                      hipStream_t s);
+hipError_t launch_copy(const CPtrBatch &in, const PtrBatch &out, int d, int count, hipStream_t s);
+hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t s);
+
+}  // namespace ispa

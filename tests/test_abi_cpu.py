@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, rejects bad
+arguments before touching the device, sizes its workspaces, and ranks layers like the oracle.
+
+Only argument errors are exercised here: validation returns before any HIP call, so fake (aligned,
+non-null) pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import kv_cache_attention_split_amd as ispa
+from kv_cache_attention_split_amd import _abi
+from oracle import absorb as oab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ispa.h")
+
+FAKE = 0x10000      # aligned, never dereferenced
+FAKE2 = 0x20000
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ispa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _abi.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert "ispa_attn_dual" in names and "ispa_absorb_solve" in names and "ispa_layer_error" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (ispa_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        getattr(L, n)
+    assert set(_abi.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version(L):
+    for code in (0, -1, -2, -3, -4):
+        assert ispa.ispa_status_string(code).startswith("ISPA")
+    assert ispa.ispa_version() >= 100
+
+
+def seg(k=FAKE, v=FAKE2, n=16, stride=256):
+    return _abi.KVSegment(k, v, n, stride)
+
+
+def attn(L, dt=1, H=2, dh=128, scale=0.088, q=FAKE, n_q=32, q_stride=256, sink=None, cur=None,
+         hist=None, a_loc=FAKE, a_full=FAKE2):
+    sink = sink if sink is not None else seg()
+    cur = cur if cur is not None else seg()
+    hist = hist if hist is not None else seg()
+    return L.ispa_attn_dual(dt, H, dh, ctypes.c_float(scale), q, n_q, q_stride, sink, cur, hist,
+                            a_loc, a_full, None, None, None, None)
+
+
+def test_attn_argument_errors(L):
+    assert attn(L, dh=96) == _abi.ISPA_E_UNSUPPORTED
+    assert attn(L, dt=7) == _abi.ISPA_E_UNSUPPORTED
+    assert attn(L, H=0) == _abi.ISPA_E_ARG
+    assert attn(L, scale=0.0) == _abi.ISPA_E_ARG
+    assert attn(L, scale=float("nan")) == _abi.ISPA_E_ARG
+    assert attn(L, n_q=-1) == _abi.ISPA_E_ARG
+    # empty local context (softmax over an empty set)
+    assert attn(L, sink=seg(n=0), cur=seg(n=0)) == _abi.ISPA_E_ARG
+    # misaligned pointers, short or misaligned strides
+    assert attn(L, q=MISALIGNED) == _abi.ISPA_E_ARG
+    assert attn(L, cur=seg(k=MISALIGNED)) == _abi.ISPA_E_ARG
+    assert attn(L, q_stride=128) == _abi.ISPA_E_ARG
+    assert attn(L, sink=seg(stride=260)) == _abi.ISPA_E_ARG     # not a multiple of 8
+    assert attn(L, hist=seg(n=-3)) == _abi.ISPA_E_ARG
+    assert attn(L, a_loc=0) == _abi.ISPA_E_ARG
+    assert attn(L, a_loc=MISALIGNED) == _abi.ISPA_E_ARG
+    # missing K/V of a non-empty segment
+    assert attn(L, cur=seg(k=0)) == _abi.ISPA_E_ARG
+    # n_q == 0 is a no-op that succeeds without touching the device
+    assert attn(L, n_q=0) == _abi.ISPA_OK
+
+
+def test_accumulate_argument_errors(L):
+    f = L.ispa_absorb_accumulate
+    assert f(1, 100, 100, FAKE, FAKE2, FAKE, FAKE, FAKE, None, 0, None) == _abi.ISPA_E_UNSUPPORTED
+    assert f(1, -1, 128, FAKE, FAKE2, FAKE, FAKE, FAKE, None, 0, None) == _abi.ISPA_E_ARG
+    assert f(1, 10, 128, FAKE, FAKE2, None, FAKE, FAKE, None, 0, None) == _abi.ISPA_E_ARG
+    assert f(1, 10, 128, MISALIGNED, FAKE2, FAKE, FAKE, FAKE, None, 0, None) == _abi.ISPA_E_ARG
+    assert f(3, 10, 128, FAKE, FAKE2, FAKE, FAKE, FAKE, None, 0, None) == _abi.ISPA_E_UNSUPPORTED
+    assert f(1, 0, 128, None, None, FAKE, FAKE, None, None, 0, None) == _abi.ISPA_OK
+    assert L.ispa_absorb_accumulate_workspace(4680, 1536) == 0
+
+
+def ptrs(n, base=FAKE):
+    arr = (ctypes.c_void_p * n)()
+    for i in range(n):
+        arr[i] = base + 0x1000 * i
+    return arr
+
+
+def test_solve_argument_errors_and_workspace(L):
+    d, b = 256, 3
+    need = L.ispa_absorb_solve_workspace(d, b)
+    assert need >= 3 * d * d * 4 * b
+    assert L.ispa_absorb_solve_workspace(1536, 30) == 30 * L.ispa_absorb_solve_workspace(1536, 1)
+    s = L.ispa_absorb_solve
+    P = ptrs(b)
+    assert s(100, b, ctypes.c_float(1e-2), P, P, P, 0, P, FAKE, FAKE, need, None) == _abi.ISPA_E_UNSUPPORTED
+    assert s(d, b, ctypes.c_float(-1.0), P, P, P, 0, P, FAKE, FAKE, need, None) == _abi.ISPA_E_ARG
+    assert s(d, b, ctypes.c_float(1e-2), P, P, P, 0, P, FAKE, FAKE, need - 1, None) == _abi.ISPA_E_WORKSPACE
+    assert s(d, b, ctypes.c_float(1e-2), P, P, P, 0, P, None, FAKE, need, None) == _abi.ISPA_E_ARG
+    bad = ptrs(b)
+    bad[1] = MISALIGNED
+    assert s(d, b, ctypes.c_float(1e-2), P, bad, P, 0, P, FAKE, FAKE, need, None) == _abi.ISPA_E_ARG
+    assert s(d, 0, ctypes.c_float(1e-2), None, None, None, 0, None, None, None, 0, None) == _abi.ISPA_OK
+
+
+def test_error_argument_errors_and_workspace(L):
+    d, b = 128, 2
+    need = L.ispa_layer_error_workspace(d, b)
+    assert need >= 2 * d * d * 4 * b
+    f = L.ispa_layer_error
+    P = ptrs(b)
+    assert f(d, b, P, P, P, P, 0, P, FAKE, None, FAKE, need - 8, None) == _abi.ISPA_E_WORKSPACE
+    assert f(d, b, P, P, P, P, 0, P, None, None, FAKE, need, None) == _abi.ISPA_E_ARG
+    assert f(96, b, P, P, P, P, 0, P, FAKE, None, FAKE, need, None) == _abi.ISPA_E_UNSUPPORTED
+
+
+def test_rank_layers_matches_oracle():
+    rng = np.random.default_rng(0)
+    for trial in range(50):
+        n = int(rng.integers(1, 40))
+        k = int(rng.integers(0, n + 1))
+        eps = rng.integers(0, 6, size=n).astype(float) * rng.choice([1.0, 1e-3])
+        if trial % 7 == 0:
+            eps[rng.integers(0, n)] = np.nan
+        sel, flags = ispa.ispa_rank_layers(eps.tolist(), k)
+        ref_sel, ref_mask = oab.rank_layers(eps, k)
+        assert sel == ref_sel.tolist()
+        assert flags == ref_mask.astype(int).tolist()
+
+
+def test_rank_layers_errors(L):
+    e = (ctypes.c_double * 3)(1.0, 2.0, 3.0)
+    sel = (ctypes.c_int32 * 4)()
+    assert L.ispa_rank_layers(e, 3, 4, sel, None) == _abi.ISPA_E_ARG
+    assert L.ispa_rank_layers(e, 3, -1, sel, None) == _abi.ISPA_E_ARG
+    assert L.ispa_rank_layers(None, 3, 1, sel, None) == _abi.ISPA_E_ARG
+    assert L.ispa_rank_layers(e, 3, 0, None, None) == _abi.ISPA_OK

@@ -1,0 +1,260 @@
+"""GPU parity of the Layer Absorb path (statistics, ridge solve, reconstruction error) against the
+fp64 oracle on identical seeded inputs.
+
+Gates: statistics rel-Frobenius <= 1e-5 (fp32 sums of exact products); dW rel-Frobenius <= 1e-3
+(fp32 statistics and fp32 Cholesky); eps relative <= 1e-3.
+"""
+import numpy as np
+import pytest
+
+import ispa_inputs as inputs
+from oracle import absorb as oab
+from oracle import attention as oatt
+
+from gpu_helpers import rel_fro, run_attn, to_dev, to_host64, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _zeros(d):
+    torch = torch_mod()
+    return [torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)]
+
+
+def _accumulate(chunks, dtype, d, with_f=True):
+    import kv_cache_attention_split_amd as ispa
+    G, X, F = _zeros(d)
+    for a_loc, a_full in chunks:
+        ispa.ispa_absorb_accumulate(to_dev(a_loc, dtype), to_dev(a_full, dtype), G, X, F if with_f else None)
+    torch_mod().cuda.synchronize()
+    return G, X, F
+
+
+@pytest.mark.parametrize("d,n,dtype", [(1536, 4680, "bf16"), (192, 333, "bf16"), (128, 128, "f32"),
+                                       (320, 517, "f32")])
+def test_statistics_full_compare(d, n, dtype):
+    _log(f"case: statistics d={d} rows={n} {dtype}")
+    rows = inputs.absorb_rows(3, 0, 3, d=d, n_rows=n, dtype=dtype)
+    G, X, F = _accumulate([(rows["a_loc"], rows["a_full"])], dtype, d)
+    ref = oab.grams(rows["a_loc"], rows["a_full"])
+    for name, t in (("G", G), ("X", X), ("F", F)):
+        err = rel_fro(to_host64(t), ref[name])
+        _log(f"  {name}: rel_fro {err:.2e}")
+        assert err <= 1e-5, (name, err)
+    if dtype == "bf16":
+        torch = torch_mod()
+        assert torch.equal(G, G.T) and torch.equal(F, F.T)
+
+
+def test_statistics_four_chunks_and_zero_gap():
+    """Four warmup chunks of workload 3 (1.3B shape); the first two have no history, so after them
+    X equals G bitwise (C = X - G = 0)."""
+    d = 1536
+    chunks = [inputs.absorb_rows(3, 1, c) for c in range(4)]
+    torch = torch_mod()
+    import kv_cache_attention_split_amd as ispa
+    G, X, F = _zeros(d)
+    for c in range(2):
+        ispa.ispa_absorb_accumulate(to_dev(chunks[c]["a_loc"], "bf16"), to_dev(chunks[c]["a_full"], "bf16"), G, X, F)
+    torch.cuda.synchronize()
+    assert torch.equal(X, G), "X != G with A_full == A_loc"
+    assert torch.equal(F, G)
+    for c in range(2, 4):
+        ispa.ispa_absorb_accumulate(to_dev(chunks[c]["a_loc"], "bf16"), to_dev(chunks[c]["a_full"], "bf16"), G, X, F)
+    torch.cuda.synchronize()
+    ref = oab.accumulate([(ch["a_loc"], ch["a_full"]) for ch in chunks])
+    for name, t in (("G", G), ("X", X), ("F", F)):
+        err = rel_fro(to_host64(t), ref[name])
+        _log(f"  {name}: rel_fro {err:.2e}")
+        assert err <= 1e-5
+
+
+def test_statistics_14b_sampled_tiles():
+    d, n = 5120, 4680
+    _log("case: statistics d=5120 (14B shape), sampled 128x128 blocks")
+    rows = inputs.absorb_rows(4, 0, 3)
+    G, X, F = _accumulate([(rows["a_loc"], rows["a_full"])], "bf16", d)
+    a = rows["a_loc"].astype(np.float64)
+    b = rows["a_full"].astype(np.float64)
+    rng = np.random.default_rng(0)
+    for _ in range(4):
+        i0, j0 = (int(x) * 128 for x in rng.integers(0, d // 128, size=2))
+        ai, aj = a[:, i0:i0 + 128], a[:, j0:j0 + 128]
+        bi, bj = b[:, i0:i0 + 128], b[:, j0:j0 + 128]
+        for name, t, ref in (("G", G, ai.T @ aj), ("X", X, ai.T @ bj), ("F", F, bi.T @ bj)):
+            got = to_host64(t[i0:i0 + 128, j0:j0 + 128])
+            assert rel_fro(got, ref) <= 1e-5, (name, i0, j0)
+
+
+def _stats64(d, n_rows, seed_layer, cfg=3, n_chunks=1):
+    chunks = [inputs.absorb_rows(cfg, seed_layer, 3 - c, d=d, n_rows=n_rows) for c in range(n_chunks)]
+    st = oab.accumulate([(c["a_loc"], c["a_full"]) for c in chunks])
+    return st
+
+
+def _solve_gpu(Gs, Xs, Ws, lam, linear=False):
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    d = Gs[0].shape[0]
+    b = len(Gs)
+    dW = [torch.full((d, d), float("nan"), dtype=torch.float32, device="cuda") for _ in range(b)]
+    info = torch.full((b,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(ispa.ispa_absorb_solve_workspace(d, b), dtype=torch.uint8, device="cuda")
+    ispa.ispa_absorb_solve(Gs, Xs, Ws, dW, lam, info, ws, w_is_linear_weight=linear)
+    torch.cuda.synchronize()
+    return dW, info
+
+
+@pytest.mark.parametrize("d,n_rows,batch", [(1536, 4680 * 2, 2), (320, 700, 3), (128, 128, 1)])
+def test_solve_against_oracle(d, n_rows, batch):
+    _log(f"case: solve d={d} rows={n_rows} batch={batch}")
+    lam = 1e-2
+    Gs, Xs, Ws, refs = [], [], [], []
+    for layer in range(batch):
+        st = _stats64(d, n_rows // 2, layer, n_chunks=2)
+        G32 = st["G"].astype(np.float32)
+        X32 = st["X"].astype(np.float32)
+        W = inputs.weight(3, layer, d=d)
+        Gs.append(to_dev(G32, "f32"))
+        Xs.append(to_dev(X32, "f32"))
+        Ws.append(to_dev(W, "f32"))
+        # oracle on the same fp32 statistics
+        G64 = G32.astype(np.float64)
+        refs.append(oab.ridge_delta_w(G64, X32.astype(np.float64) - G64, W, lam))
+    dW, info = _solve_gpu(Gs, Xs, Ws, lam)
+    assert info.cpu().tolist() == [0] * batch
+    for i in range(batch):
+        err = rel_fro(to_host64(dW[i]), refs[i])
+        _log(f"  layer {i}: dW rel_fro {err:.2e}")
+        assert err <= 1e-3
+    # nn.Linear orientation gives the transpose
+    WT = [w.t().contiguous() for w in Ws]
+    dWT, info = _solve_gpu(Gs, Xs, WT, lam, linear=True)
+    for i in range(batch):
+        assert rel_fro(to_host64(dWT[i]).T, refs[i]) <= 1e-3
+
+
+def test_solve_14b_shape():
+    d = 5120
+    _log("case: solve d=5120")
+    st = _stats64(d, 5600, 0, cfg=4)
+    G32 = st["G"].astype(np.float32)
+    X32 = st["X"].astype(np.float32)
+    W = inputs.weight(4, 0)
+    dW, info = _solve_gpu([to_dev(G32, "f32")], [to_dev(X32, "f32")], [to_dev(W, "f32")], 1e-2)
+    assert info.cpu().tolist() == [0]
+    G64 = G32.astype(np.float64)
+    ref = oab.ridge_delta_w(G64, X32.astype(np.float64) - G64, W, 1e-2)
+    err = rel_fro(to_host64(dW[0]), ref)
+    _log(f"  dW rel_fro {err:.2e}")
+    assert err <= 1e-3
+
+
+def test_solve_zero_gap_gives_zero_update_and_info():
+    torch = torch_mod()
+    d = 256
+    st = _stats64(d, 600, 5)
+    G = to_dev(st["G"].astype(np.float32), "f32")
+    W = to_dev(inputs.weight(3, 5, d=d), "f32")
+    dW, info = _solve_gpu([G], [G.clone()], [W], 1e-2)
+    assert info.cpu().tolist() == [0]
+    assert bool(torch.all(dW[0] == 0)), "C = 0 must give dW = 0 exactly"
+    # lambda = 0 with G = 0: first pivot is zero -> info = 1; a negative diagonal entry -> its column
+    Z = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    _, info = _solve_gpu([Z], [Z.clone()], [W], 0.0)
+    assert info.cpu().tolist() == [1]
+    Gb = G.clone()
+    Gb[200, 200] = -1.0
+    _, info = _solve_gpu([Gb], [G.clone()], [W], 1e-2)
+    assert info.cpu().tolist()[0] == 201
+
+
+def _error_gpu(Gs, Xs, Fs, Ws, dWs, linear=False):
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    d, b = Gs[0].shape[0], len(Gs)
+    eps = torch.full((b,), float("nan"), dtype=torch.float64, device="cuda")
+    ref = torch.full((b,), float("nan"), dtype=torch.float64, device="cuda")
+    ws = torch.empty(ispa.ispa_layer_error_workspace(d, b), dtype=torch.uint8, device="cuda")
+    ispa.ispa_layer_error(Gs, Xs, Fs, Ws, dWs, eps, ref, ws, w_is_linear_weight=linear)
+    torch.cuda.synchronize()
+    return eps.cpu().numpy(), ref.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,n_rows", [(1536, 4680), (192, 400)])
+def test_layer_error_against_oracle(d, n_rows):
+    _log(f"case: layer error d={d}")
+    rows = inputs.absorb_rows(3, 2, 3, d=d, n_rows=n_rows)
+    st = oab.grams(rows["a_loc"], rows["a_full"])
+    G32, X32, F32 = (st[k].astype(np.float32) for k in ("G", "X", "F"))
+    W = inputs.weight(3, 2, d=d)
+    G64, X64, F64 = (x.astype(np.float64) for x in (G32, X32, F32))
+    C64 = X64 - G64
+    H64 = F64 - X64 - X64.T + G64
+    dW = oab.ridge_delta_w(G64, C64, W, 1e-2).astype(np.float32)
+    cands = [dW, np.zeros_like(dW)]
+    Gs = [to_dev(G32, "f32")] * 2
+    Xs = [to_dev(X32, "f32")] * 2
+    Fs = [to_dev(F32, "f32")] * 2
+    Ws = [to_dev(W, "f32")] * 2
+    eps, ref = _error_gpu(Gs, Xs, Fs, Ws, [to_dev(c, "f32") for c in cands])
+    for i, c in enumerate(cands):
+        want = oab.layer_error_stats(G64, C64, H64, W, c)
+        _log(f"  eps[{i}] gpu {eps[i]:.6e} oracle {want:.6e}")
+        assert abs(eps[i] - want) <= 1e-3 * abs(want)
+    assert abs(ref[0] - oab.reference_energy(F64, W)) <= 1e-5 * ref[0]
+    # linear-weight orientation
+    eps_t, _ = _error_gpu(Gs[:1], Xs[:1], Fs[:1], [to_dev(W.T.copy(), "f32")], [to_dev(dW.T.copy(), "f32")], linear=True)
+    assert abs(eps_t[0] - eps[0]) <= 1e-6 * abs(eps[0])
+
+
+def test_chain_workload1_fp32():
+    """Workload 1 end to end on the device (fp32): attention -> statistics -> dW -> eps, against the
+    oracle chain in fp64."""
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    inp = inputs.attention_inputs(1)
+    _, out = run_attn(inp)
+    d = 128
+    G, X, F = _zeros(d)
+    ispa.ispa_absorb_accumulate(out["a_loc"], out["a_full"], G, X, F)
+    W = inputs.weight(1, 0)
+    Wd = to_dev(W, "f32")
+    dW, info = _solve_gpu([G], [X], [Wd], 1e-2)
+    assert info.cpu().tolist() == [0]
+    eps, ref = _error_gpu([G], [X], [F], [Wd], dW)
+    o = oatt.dual_stream(inp)
+    st = oab.grams(o["A_loc"], o["A_full"])
+    dW_ref = oab.ridge_delta_w(st["G"], st["C"], W, 1e-2)
+    eps_ref = oab.layer_error_rows(o["A_loc"], o["A_full"], W, dW_ref)
+    e_dw = rel_fro(to_host64(dW[0]), dW_ref)
+    _log(f"  chain: dW rel_fro {e_dw:.2e}; eps gpu {eps[0]:.6e} oracle {eps_ref:.6e}")
+    assert e_dw <= 1e-3
+    assert abs(eps[0] - eps_ref) <= 1e-3 * eps_ref
+
+
+def test_rank_on_device_errors():
+    """Ranking of eps computed on the device agrees with the oracle's ranking of its own eps,
+    except where two layers' errors are within the tolerance (either order is then accepted)."""
+    import kv_cache_attention_split_amd as ispa
+    d, n_layers, k = 192, 6, 3
+    Gs, Xs, Fs, Ws, dWs, eps_ref = [], [], [], [], [], []
+    for layer in range(n_layers):
+        rows = inputs.absorb_rows(3, layer, 3, d=d, n_rows=400)
+        st = oab.grams(rows["a_loc"], rows["a_full"])
+        G32, X32, F32 = (st[x].astype(np.float32) for x in ("G", "X", "F"))
+        W = inputs.weight(3, layer, d=d)
+        dW = oab.ridge_delta_w(st["G"], st["C"], W, 1e-2)
+        eps_ref.append(oab.layer_error_rows(rows["a_loc"], rows["a_full"], W, dW))
+        Gs.append(to_dev(G32, "f32")); Xs.append(to_dev(X32, "f32")); Fs.append(to_dev(F32, "f32"))
+        Ws.append(to_dev(W, "f32")); dWs.append(to_dev(dW.astype(np.float32), "f32"))
+    eps, _ = _error_gpu(Gs, Xs, Fs, Ws, dWs)
+    sel, _ = ispa.ispa_rank_layers(eps.tolist(), k)
+    ref_sel, _ = oab.rank_layers(np.array(eps_ref), k)
+    srt = np.sort(eps_ref)
+    if abs(srt[k] - srt[k - 1]) > 2e-3 * srt[k]:
+        assert sorted(sel) == sorted(ref_sel.tolist())

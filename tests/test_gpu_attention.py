@@ -1,0 +1,175 @@
+"""GPU parity of ispa_attn_dual against the fp64 oracle (same seeded inputs).
+
+Small cases are compared element by element over every output; workload-size cases (1.3B chunk 4,
+14B chunk 4, the 60-frame-history rollout) are compared on sampled query rows, which the oracle
+evaluates one by one, plus properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import ispa_inputs as inputs
+from oracle import attention as oatt
+
+from gpu_helpers import (check_attention, run_attn, to_dev, to_host64, empty_outputs, torch_mod,
+                         max_abs, rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def test_workload1_fp32_full_compare():
+    inp = inputs.attention_inputs(1)
+    _log("case: workload 1 (fp32, 2x64, 128 q, 64/128/512 keys)")
+    _, out = run_attn(inp)
+    ref = oatt.dual_stream(inp)
+    rep = check_attention(out, ref, "f32")
+    _log(f"  {rep}")
+
+
+@pytest.mark.parametrize("case", [
+    # seed, H, dh, n_q, sink, cur, hist  (several tiles, ragged tails everywhere)
+    (1, 2, 128, 300, 70, 100, 333),
+    (2, 3, 64, 130, 0, 64, 65),
+    (3, 1, 128, 129, 1, 0, 1),
+    (4, 2, 128, 64, 5, 7, 0),
+    (5, 2, 64, 257, 200, 300, 700),
+])
+def test_bf16_small_full_compare(case):
+    seed, H, dh, n_q, ns, nc, nh = case
+    _log(f"case: bf16 seed={seed} H={H} dh={dh} n_q={n_q} sink={ns} cur={nc} hist={nh}")
+    inp = inputs.attention_case(seed, H, dh, n_q, ns, nc, nh, dtype="bf16", rho=0.95)
+    _, out = run_attn(inp)
+    ref = oatt.dual_stream(inp)
+    rep = check_attention(out, ref, "bf16")
+    _log(f"  {rep}")
+
+
+def test_fp32_head128_and_ragged():
+    inp = inputs.attention_case(7, 2, 128, 150, 33, 40, 97, dtype="f32")
+    _log("case: fp32 H=2 dh=128 n_q=150 33/40/97")
+    _, out = run_attn(inp)
+    check_attention(out, oatt.dual_stream(inp), "f32")
+
+
+def test_empty_history_is_bitwise_local():
+    inp = inputs.attention_case(8, 2, 128, 200, 64, 100, 0, dtype="bf16")
+    _log("case: empty history")
+    _, out = run_attn(inp)
+    torch = torch_mod()
+    assert torch.equal(out["a_full"], out["a_loc"])
+    assert torch.equal(out["lse_full"], out["lse_loc"])
+    assert bool(torch.all(torch.isneginf(out["lse_hist"])))
+    check_attention(out, oatt.dual_stream(inp), "bf16")
+
+
+def test_local_only_call_matches_dual_local():
+    """a_full = NULL computes the local branch alone; it equals the dual call's A_loc bitwise."""
+    inp = inputs.attention_case(9, 2, 128, 190, 64, 130, 300, dtype="bf16")
+    _log("case: local-only vs dual")
+    dev, out = run_attn(inp)
+    _, out_l = run_attn(inp, want_full=False, dev=dev)
+    torch = torch_mod()
+    assert torch.equal(out_l["a_loc"], out["a_loc"])
+    assert torch.equal(out_l["lse_loc"], out["lse_loc"])
+
+
+def test_zero_queries_uniform_weights():
+    """P-3 on the device: Q = 0 gives uniform weights, lse = log(n) and A = mean of V."""
+    inp = inputs.attention_case(10, 2, 128, 96, 100, 200, 1000, dtype="bf16")
+    inp["q"] = np.zeros_like(inp["q"])
+    _log("case: Q = 0")
+    _, out = run_attn(inp)
+    n_loc, n_all = 300, 1300
+    lse_loc = to_host64(out["lse_loc"])
+    lse_full = to_host64(out["lse_full"])
+    lse_hist = to_host64(out["lse_hist"])
+    assert np.max(np.abs(lse_loc - math.log(n_loc))) <= 1e-6 * math.log(n_loc)
+    assert np.max(np.abs(lse_full - math.log(n_all))) <= 1e-6 * math.log(n_all)
+    assert np.max(np.abs(lse_hist - math.log(1000))) <= 1e-6 * math.log(1000)
+    ref = oatt.dual_stream(inp)
+    check_attention(out, ref, "bf16")
+
+
+def test_deterministic_repeat():
+    inp = inputs.attention_case(11, 2, 128, 200, 64, 100, 250, dtype="bf16")
+    dev, out1 = run_attn(inp)
+    _, out2 = run_attn(inp, dev=dev)
+    torch = torch_mod()
+    for k in ("a_loc", "a_full", "lse_loc", "lse_hist", "lse_full"):
+        assert torch.equal(out1[k], out2[k]), k
+
+
+def test_strided_rows():
+    """Token rows with a stride larger than H*d_h (a view into a wider buffer)."""
+    torch = torch_mod()
+    inp = inputs.attention_case(12, 2, 64, 100, 30, 60, 90, dtype="bf16")
+    dev = {}
+    for k in ("q", "sink_k", "sink_v", "cur_k", "cur_v", "hist_k", "hist_v"):
+        x = to_dev(inp[k], "bf16")
+        n = x.shape[0]
+        wide = torch.zeros((n, 3, 64), dtype=x.dtype, device="cuda")
+        wide[:, 1:3] = x
+        dev[k] = wide[:, 1:3]
+    _log("case: strided rows")
+    _, out = run_attn(inp, dev=dev)
+    check_attention(out, oatt.dual_stream(inp), "bf16")
+
+
+def _sampled(cfg, chunk=0, n_rows=48, seed=0, heads=None):
+    inp = inputs.attention_inputs(cfg, 0, chunk)
+    rng = np.random.default_rng(seed)
+    n_q = inp["q"].shape[0]
+    rows = np.unique(np.concatenate([rng.choice(n_q, n_rows, replace=False), [0, n_q - 1]]))
+    return inp, rows
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_workload_sampled_rows(cfg):
+    inp, rows = _sampled(cfg)
+    s = inputs.CONFIGS[cfg].segment_sizes()
+    _log(f"case: workload {cfg} sampled rows ({len(rows)}) {s}")
+    _, out = run_attn(inp)
+    ref = oatt.dual_stream(inp, rows=rows)
+    rep = check_attention(out, ref, "bf16", rows=rows)
+    _log(f"  {rep}")
+
+
+def test_workload4_chunk4_sampled_rows():
+    inp, rows = _sampled(4, chunk=3, n_rows=24)
+    _log("case: workload 4 chunk 4 (40 heads) sampled rows")
+    _, out = run_attn(inp)
+    ref = oatt.dual_stream(inp, rows=rows)
+    rep = check_attention(out, ref, "bf16", rows=rows)
+    _log(f"  {rep}")
+
+
+def test_workload5_merge_equals_single_pass():
+    """The dual call's A_full/lse_full equal a single pass with all keys in the local run, and
+    lse_full = logaddexp(lse_loc, lse_hist) on the device outputs."""
+    torch = torch_mod()
+    inp = inputs.attention_inputs(5)
+    _log("case: workload 5 merge vs single pass")
+    dev, out = run_attn(inp)
+    one = dict(inp)
+    one["cur_k"] = np.concatenate([inp["cur_k"], inp["hist_k"]])
+    one["cur_v"] = np.concatenate([inp["cur_v"], inp["hist_v"]])
+    one["hist_k"] = inp["hist_k"][:0]
+    one["hist_v"] = inp["hist_v"][:0]
+    dev1 = dict(dev)
+    dev1["cur_k"] = torch.cat([dev["cur_k"], dev["hist_k"]])
+    dev1["cur_v"] = torch.cat([dev["cur_v"], dev["hist_v"]])
+    dev1["hist_k"] = dev["hist_k"][:0]
+    dev1["hist_v"] = dev["hist_v"][:0]
+    _, single = run_attn(one, dev=dev1)
+    a_dual = to_host64(out["a_full"])
+    a_single = to_host64(single["a_loc"])
+    assert max_abs(a_dual, a_single) <= 2e-3
+    assert rel_fro(a_dual, a_single) <= 5e-3
+    assert max_abs(to_host64(out["lse_full"]), to_host64(single["lse_loc"])) <= 1e-4
+    lse = np.logaddexp(to_host64(out["lse_loc"]), to_host64(out["lse_hist"]))
+    assert max_abs(lse, to_host64(out["lse_full"])) <= 1e-4
