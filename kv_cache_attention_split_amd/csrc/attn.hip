@@ -83,6 +83,9 @@ __device__ __forceinline__ const uint16_t *run_row(const SegRun &r, int64_t j, i
 }
 
 // Global -> register prefetch of key/value tile t (t < nt_loc: local run, else history run).
+// Common case: the tile lies inside one sub-run (sink, current or history) and needs no clamping;
+// then one uniform base pointer and a 32-bit row offset address every row. Tiles that cross the
+// sink/current split or the end of a run take the per-row path.
 template <int D, int BK>
 __device__ __forceinline__ void load_tile(const AttnArgs &a, int t, int nt_loc, int tid, int head_off,
                                           int vg, int vc, u32x4 (&kreg)[BK * D / 8 / kThreads],
@@ -93,6 +96,27 @@ __device__ __forceinline__ void load_tile(const AttnArgs &a, int t, int nt_loc, 
   const bool hist = t >= nt_loc;
   const SegRun run = seg_run(a, hist);
   const int64_t j0 = (int64_t)(hist ? t - nt_loc : t) * BK;
+  const int64_t j1 = j0 + BK;
+  const bool in_first = j1 <= run.split && j1 <= run.n;
+  const bool in_second = j0 >= run.split && j1 <= run.n;
+  if (in_first || in_second) {
+    const uint16_t *kb = in_first ? run.k0 + j0 * run.s0 : run.k1 + (j0 - run.split) * run.s1;
+    const uint16_t *vb = in_first ? run.v0 + j0 * run.s0 : run.v1 + (j0 - run.split) * run.s1;
+    const int st = (int)(in_first ? run.s0 : run.s1);
+    kb += head_off;
+    vb += head_off;
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int idx = tid + kThreads * i;
+      const int row = idx / CPR, c = idx % CPR;
+      kreg[i] = *(const u32x4 *)(kb + (row * st + 8 * c));
+    }
+    if (tid < VPAIRS) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vreg[e] = *(const u32x4 *)(vb + ((4 * vg + e) * st + 8 * vc));
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < KLD; ++i) {
     const int idx = tid + kThreads * i;
@@ -139,7 +163,7 @@ __device__ __forceinline__ void store_tile(uint16_t *k_lds, uint16_t *v_lds, int
 }
 
 template <int D, int QB>
-__global__ void __launch_bounds__(kThreads) attn_dual_bf16_kernel(AttnArgs a, int n_qt) {
+__global__ void __launch_bounds__(kThreads, QB == 1 ? 2 : 1) attn_dual_bf16_kernel(AttnArgs a, int n_qt) {
   constexpr int BK = 64;             // keys per tile
   constexpr int KST = D + 8;         // K tile row stride (elements), padded against bank conflicts
   constexpr int VST = BK + 8;        // V^T tile row stride
