@@ -16,8 +16,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int BT = 128;          // output tile
-constexpr int BR = 64;           // rows per stage
-constexpr int ST = BR + 8;       // LDS row stride (elements) of the transposed operand tiles
+constexpr int BR = 32;           // rows per stage
+constexpr int RB = BT * 2;       // bytes of one tile row (128 bf16)
 
 struct GramArgs {
   const uint16_t *a_loc, *a_full;
@@ -37,8 +37,39 @@ __device__ __forceinline__ void tri_decode(int idx, int T, int &ti, int &tj) {
   tj = r + idx;
 }
 
-__global__ void __launch_bounds__(kThreads) gram_bf16_kernel(GramArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][BT * ST];   // [buf][operand]
+// Operand tiles are kept row-major in LDS ([row of the chunk][128 columns], 256 bytes per row) with
+// the 16-byte chunks of row r stored at position c ^ (4 (r mod 4)). ds_read_b64_tr_b16 then yields
+// MFMA operands directly: in each 16-lane group, source lane s addresses row k0 + s/4, columns
+// n0 + 4 (s mod 4) .. +3, and result lane i receives column n0 + i of rows k0 .. k0+3. The swizzle
+// spreads the 4 rows of one read over distinct banks.
+__device__ __forceinline__ int swz_off(int r, int col) {   // byte offset of (r, col) in a tile
+  const int c = col >> 3;
+  return r * RB + (((c ^ (4 * (r & 3))) << 4) | ((col & 7) << 1));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 read_operand(const uint8_t *tile, int cb, int kb, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int n0 = cb + 16 * (g & 1);
+  const int k0 = kb + 8 * (g >> 1);
+  const int col = n0 + 4 * (s & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(tile + swz_off(k0 + (s >> 2), col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(tile + swz_off(k0 + 4 + (s >> 2), col)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
+  // [buf][operand] tiles of BR x 128 bf16; after the main loop the same space holds the fp32 result
+  // tile (128 x 129 floats)
+  constexpr int kTileBytes = BR * RB;
+  constexpr int kLdsBytes = BT * (BT + 1) * 4 > 4 * kTileBytes ? BT * (BT + 1) * 4 : 4 * kTileBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+  auto tile_ptr = [&](int buf, int op) { return smem + (2 * buf + op) * kTileBytes; };
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -64,48 +95,45 @@ __global__ void __launch_bounds__(kThreads) gram_bf16_kernel(GramArgs g) {
   float *out = (mat == 0) ? g.G : (mat == 1) ? g.F : g.X;
   const int i0 = ti * BT, j0 = tj * BT;
   const int d = g.d;
+  const int64_t last_row = g.n_rows - 1;
 
-  // staging: each thread owns two (4-row group, 8-column chunk) pairs; threads 0..127 stage the
-  // left operand, 128..255 the right one.
-  const int op = tid >> 7;
-  const int sid = tid & 127;
-  const uint16_t *src = op ? Q : P;
-  const int col0 = op ? j0 : i0;
-  u32x4 r[2][4];
-  auto load = [&](int64_t n0) {
+  // staging: thread handles 16-byte chunks e = tid + 256 q (q = 0, 1) of each operand tile:
+  // row r = e / 16, chunk c = e % 16. Columns past d are clamped (their outputs are not stored).
+  int srow[2], scol_p[2], scol_q[2], soff[2];
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const int pair = sid + 128 * pp;
-      const int grp = pair & 15, ch = pair >> 4;
-      const int col = col0 + 8 * ch;
+  for (int q = 0; q < 2; ++q) {
+    const int e = tid + kThreads * q;
+    const int r = e >> 4, c = e & 15;
+    srow[q] = r;
+    const int cp = i0 + 8 * c, cq = j0 + 8 * c;
+    scol_p[q] = cp < d ? cp : d - 8;
+    scol_q[q] = cq < d ? cq : d - 8;
+    soff[q] = r * RB + ((c ^ (4 * (r & 3))) << 4);
+  }
+  u32x4 ra[4], rb[4];   // [operand * 2 + q]
+  auto load = [&](u32x4 (&r)[4], int64_t n0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t n = n0 + 4 * grp + e;
-        if (n < g.n_rows && col < d)
-          r[pp][e] = *(const u32x4 *)(src + n * d + col);
-        else
-          r[pp][e] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int q = 0; q < 2; ++q) {
+      int64_t n = n0 + srow[q];
+      n = n < last_row ? n : last_row;
+      r[q] = *(const u32x4 *)(P + n * d + scol_p[q]);
+      r[2 + q] = *(const u32x4 *)(Q + n * d + scol_q[q]);
     }
   };
-  auto store = [&](int buf) {
-    uint16_t *dst = lds[buf][op];
+  auto store = [&](const u32x4 (&r)[4], int buf, int64_t n0) {
+    if (n0 + BR - 1 <= last_row) {
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const int pair = sid + 128 * pp;
-      const int grp = pair & 15, ch = pair >> 4;
+      for (int q = 0; q < 2; ++q) {
+        *(u32x4 *)(tile_ptr(buf, 0) + soff[q]) = r[q];
+        *(u32x4 *)(tile_ptr(buf, 1) + soff[q]) = r[2 + q];
+      }
+    } else {   // tail stage: rows past the chunk end contribute zeros
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const uint32_t x0 = u4_get(r[pp][0], mm), x1 = u4_get(r[pp][1], mm);
-        const uint32_t x2 = u4_get(r[pp][2], mm), x3 = u4_get(r[pp][3], mm);
-        u32x2 lo, hi;
-        lo[0] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-        lo[1] = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
-        hi[0] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-        hi[1] = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
-        const int c = 8 * ch + 2 * mm;
-        *(u32x2 *)&dst[c * ST + 4 * grp] = lo;
-        *(u32x2 *)&dst[(c + 1) * ST + 4 * grp] = hi;
+      for (int q = 0; q < 2; ++q) {
+        const bool ok = n0 + srow[q] <= last_row;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *(u32x4 *)(tile_ptr(buf, 0) + soff[q]) = ok ? r[q] : z;
+        *(u32x4 *)(tile_ptr(buf, 1) + soff[q]) = ok ? r[2 + q] : z;
       }
     }
   };
@@ -118,39 +146,50 @@ __global__ void __launch_bounds__(kThreads) gram_bf16_kernel(GramArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
 
-  const int nst = (int)((g.n_rows + BR - 1) / BR);
-  if (nst > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) load((int64_t)(st + 1) * BR);
-    const uint16_t *As = lds[buf][0];
-    const uint16_t *Bs = lds[buf][1];
+  auto compute = [&](int buf) {
+    const uint8_t *As = tile_ptr(buf, 0);
+    const uint8_t *Bs = tile_ptr(buf, 1);
 #pragma unroll
     for (int t = 0; t < BR / 16; ++t) {
       bf16x8 av[2], bv[2];
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
-        av[bi] = *(const bf16x8 *)&As[(wm * 64 + bi * 32 + l32) * ST + 16 * t + 8 * hf];
+      for (int bi = 0; bi < 2; ++bi) av[bi] = read_operand(As, wm * 64 + bi * 32, 16 * t, lane);
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj)
-        bv[bj] = *(const bf16x8 *)&Bs[(wn * 64 + bj * 32 + l32) * ST + 16 * t + 8 * hf];
+      for (int bj = 0; bj < 2; ++bj) bv[bj] = read_operand(Bs, wn * 64 + bj * 32, 16 * t, lane);
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
         for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma_bf16_32x32x16(av[bi], bv[bj], acc[bi][bj]);
     }
-    if (st + 1 < nst) store(buf ^ 1);
+  };
+
+  // Two stages of global loads stay in flight: while stage s is multiplied out of LDS, stage s+1
+  // sits in one register set and stage s+2 is being fetched into the other. Loads are issued
+  // unconditionally (clamped rows), so no branch separates them from their use.
+  const int nst = (int)((g.n_rows + BR - 1) / BR);
+  load(ra, 0);
+  load(rb, BR);
+  store(ra, 0, 0);
+  __syncthreads();
+  int st = 0;
+  for (; st + 1 < nst; st += 2) {
+    load(ra, (int64_t)(st + 2) * BR);
+    compute(0);
+    store(rb, 1, (int64_t)(st + 1) * BR);
+    __syncthreads();
+    load(rb, (int64_t)(st + 3) * BR);
+    compute(1);
+    if (st + 2 < nst) store(ra, 0, (int64_t)(st + 2) * BR);
     __syncthreads();
   }
+  if (st < nst) compute(0);
+  __syncthreads();
 
   // Stage the 128x128 result in LDS (reusing the operand buffers), then add it to the running sums
-  // with coalesced accesses: the tile itself, and for off-diagonal symmetric tiles its mirror.
-  float *cs = (float *)&lds[0][0][0];
-  constexpr int CST = BT + 1;
+  // with coalesced 16-byte read-modify-writes: the tile itself, and for off-diagonal symmetric tiles
+  // its mirror. Each thread issues all of its loads before any add, so the round trips overlap.
+  float *cs = (float *)smem;
+  constexpr int CST = BT + 1;   // odd stride: both row-wise and column-wise reads spread over banks
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -162,16 +201,49 @@ __global__ void __launch_bounds__(kThreads) gram_bf16_kernel(GramArgs g) {
         cs[rr * CST + cc] = acc[bi][bj][v];
       }
   __syncthreads();
-  for (int e = tid; e < BT * BT; e += kThreads) {
-    const int rr = e >> 7, cc = e & 127;
-    const int gr = i0 + rr, gc = j0 + cc;
-    if (gr < d && gc < d) out[(int64_t)gr * d + gc] += cs[rr * CST + cc];
+  // thread -> (row rr = e / 32, 4-column group c4 = e % 32) for e = tid + 256 k, k < 16
+  constexpr int NV = BT * BT / 4 / kThreads;   // 16 float4 per thread
+  const int c4 = tid & 31;
+  const int rbase = tid >> 5;                  // 0..7; rows rbase + 8k
+  {
+    f32x4 cur[NV];
+    const int gc = j0 + 4 * c4;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int gr = i0 + rbase + 8 * k;
+      const int grc = gr < d ? gr : d - 1;
+      const int gcc = gc < d ? gc : d - 4;
+      cur[k] = *(const f32x4 *)&out[(int64_t)grc * d + gcc];
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int rr = rbase + 8 * k;
+      const int gr = i0 + rr;
+      f32x4 add;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) add[q] = cs[rr * CST + 4 * c4 + q];
+      if (gr < d && gc < d) *(f32x4 *)&out[(int64_t)gr * d + gc] = cur[k] + add;
+    }
   }
   if (mat != 2 && ti != tj) {
-    for (int e = tid; e < BT * BT; e += kThreads) {
-      const int rr = e >> 7, cc = e & 127;     // mirror position (j0 + rr, i0 + cc) = tile (cc, rr)
-      const int gr = j0 + rr, gc = i0 + cc;
-      if (gr < d && gc < d) out[(int64_t)gr * d + gc] += cs[cc * CST + rr];
+    // mirror: out[j0 + rr][i0 + cc] += tile[cc][rr]
+    f32x4 cur[NV];
+    const int gc = i0 + 4 * c4;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int gr = j0 + rbase + 8 * k;
+      const int grc = gr < d ? gr : d - 1;
+      const int gcc = gc < d ? gc : d - 4;
+      cur[k] = *(const f32x4 *)&out[(int64_t)grc * d + gcc];
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int rr = rbase + 8 * k;
+      const int gr = j0 + rr;
+      f32x4 add;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) add[q] = cs[(4 * c4 + q) * CST + rr];
+      if (gr < d && gc < d) *(f32x4 *)&out[(int64_t)gr * d + gc] = cur[k] + add;
     }
   }
 }

@@ -205,64 +205,119 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
 // ------------------------------------------------------------------------------------------------
 // Diagonal block: Cholesky factor and its inverse (one workgroup per layer).
 // ------------------------------------------------------------------------------------------------
-constexpr int kMaxNb = 128;
 
+// Register-blocked: a 16 x 16 grid of threads, thread (ty, tx) owning the R x R sub-block at rows
+// ty*R.., columns tx*R.. (R = nb / 16). Each elimination step publishes one column (factorisation)
+// or one row (inverse) through LDS, then every thread updates its own sub-block in registers: one
+// barrier per step and no dependent LDS chains.
+template <int NB>
 __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int64_t L_stride, int d,
-                                                              int k0, int nb, float *Linv_base,
+                                                              int k0, float *Linv_base,
                                                               int64_t Linv_stride, int32_t *info) {
+  constexpr int R = NB / 16;
   extern __shared__ float smem[];
-  const int ld = nb + 1;
-  float *A = smem;              // nb x ld
-  float *Xi = smem + nb * ld;   // nb x ld
+  float *colst = smem;              // [NB][NB]: column j of the updated block at step j (col-major)
+  float *rowst = smem + NB * NB;    // [NB][NB]: row j of U^-1 at step j
   __shared__ int bad;
   const int layer = blockIdx.x;
   float *L = Lbase + layer * L_stride;
   float *Linv = Linv_base + layer * Linv_stride;
   const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int r0 = ty * R, c0 = tx * R;
   if (tid == 0) bad = 0;
-  for (int e = tid; e < nb * nb; e += kThreads) {
-    const int r = e / nb, c = e % nb;
-    A[r * ld + c] = L[(int64_t)(k0 + r) * d + k0 + c];
-    Xi[r * ld + c] = (r == c) ? 1.f : 0.f;
+  float a[R][R];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int k = 0; k < R; ++k) a[i][k] = L[(int64_t)(k0 + r0 + i) * d + k0 + c0 + k];
+
+  // factorisation: at step j the owners of column j publish it; every thread then applies
+  // A[r][c] -= A[r][j] A[c][j] / A[j][j] to its lower-triangle elements with r, c > j.
+  for (int j = 0; j < NB; ++j) {
+    if (tx == j / R) {
+#pragma unroll
+      for (int k = 0; k < R; ++k)
+        if (c0 + k == j) {
+#pragma unroll
+          for (int i = 0; i < R; ++i) colst[j * NB + r0 + i] = a[i][k];
+        }
+    }
+    __syncthreads();
+    float piv = colst[j * NB + j];
+    if (!(piv > 0.f)) piv = 1.f;   // recorded below; keeps the rest finite
+    const float ip = 1.f / piv;
+    float cr[R], cc[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      cr[i] = colst[j * NB + r0 + i] * ip;
+      cc[i] = colst[j * NB + c0 + i];
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int r = r0 + i, c = c0 + k;
+        if (r > j && c > j && c <= r) a[i][k] = fmaf(-cr[i], cc[k], a[i][k]);
+      }
+  }
+  if (tid == 0) {
+    for (int j = 0; j < NB; ++j)
+      if (!(colst[j * NB + j] > 0.f)) {
+        bad = j + 1;
+        break;
+      }
+  }
+  // inverse of the unit-lower factor U[r][j] = colst[j][r] / piv_j by a forward sweep:
+  // Y = I; for each j, rows i > j: Y[i][c] -= U[i][j] Y[j][c].
+  float y[R][R];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int k = 0; k < R; ++k) y[i][k] = (r0 + i == c0 + k) ? 1.f : 0.f;
+  for (int j = 0; j < NB - 1; ++j) {
+    if (ty == j / R) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        if (r0 + i == j) {
+#pragma unroll
+          for (int k = 0; k < R; ++k) rowst[j * NB + c0 + k] = y[i][k];
+        }
+    }
+    __syncthreads();
+    float piv = colst[j * NB + j];
+    if (!(piv > 0.f)) piv = 1.f;
+    const float ip = 1.f / piv;
+    float u[R], yr[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      u[i] = colst[j * NB + r0 + i] * ip;
+      yr[i] = rowst[j * NB + c0 + i];
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int k = 0; k < R; ++k)
+        if (r0 + i > j && c0 + k <= j) y[i][k] = fmaf(-u[i], yr[k], y[i][k]);
+  }
+  // L = U D^1/2 (lower part of the block), Linv = D^-1/2 Y
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int r = r0 + i;
+    float pr = colst[r * NB + r];
+    if (!(pr > 0.f)) pr = 1.f;
+    const float isr = 1.f / sqrtf(pr);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int c = c0 + k;
+      Linv[r * NB + c] = y[i][k] * isr;
+      float pc = colst[c * NB + c];
+      if (!(pc > 0.f)) pc = 1.f;
+      if (c < r) L[(int64_t)(k0 + r) * d + k0 + c] = colst[c * NB + r] / sqrtf(pc);
+      else if (c == r) L[(int64_t)(k0 + r) * d + k0 + c] = sqrtf(pr);
+    }
   }
   __syncthreads();
-  // right-looking unblocked Cholesky of the block (lower triangle)
-  for (int j = 0; j < nb; ++j) {
-    float piv = A[j * ld + j];
-    if (!(piv > 0.f)) {
-      piv = 1.f;
-      if (tid == 0 && bad == 0) bad = j + 1;
-    }
-    const float ljj = sqrtf(piv);
-    const float inv = 1.f / ljj;
-    __syncthreads();
-    if (tid == 0) A[j * ld + j] = ljj;
-    for (int i = j + 1 + tid; i < nb; i += kThreads) A[i * ld + j] *= inv;
-    __syncthreads();
-    const int rem = nb - j - 1;
-    for (int e = tid; e < rem * rem; e += kThreads) {
-      const int r = j + 1 + e / rem, c = j + 1 + e % rem;
-      if (c <= r) A[r * ld + c] -= A[r * ld + j] * A[c * ld + j];
-    }
-    __syncthreads();
-  }
-  // inverse of the lower factor by a row sweep: L X = I
-  for (int j = 0; j < nb; ++j) {
-    const float inv = 1.f / A[j * ld + j];
-    for (int c = tid; c <= j; c += kThreads) Xi[j * ld + c] *= inv;
-    __syncthreads();
-    const int cols = j + 1, rows = nb - j - 1;
-    for (int e = tid; e < rows * cols; e += kThreads) {
-      const int i = j + 1 + e / cols, c = e % cols;
-      Xi[i * ld + c] -= A[i * ld + j] * Xi[j * ld + c];
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < nb * nb; e += kThreads) {
-    const int r = e / nb, c = e % nb;
-    Linv[r * nb + c] = Xi[r * ld + c];
-    if (c <= r) L[(int64_t)(k0 + r) * d + k0 + c] = A[r * ld + c];
-  }
   if (tid == 0 && bad != 0 && info[layer] == 0) info[layer] = k0 + bad;
 }
 
@@ -380,15 +435,21 @@ hipError_t launch_shift_copy(const CPtrBatch &G, float *L, int64_t L_stride, int
 
 hipError_t launch_potrf_diag(float *L, int64_t L_stride, int d, int k0, int nb, float *Linv,
                              int64_t Linv_stride, int32_t *info, int count, hipStream_t s) {
-  const size_t shmem = 2 * (size_t)nb * (nb + 1) * sizeof(float);
+  const size_t shmem = 2 * (size_t)nb * nb * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void *)potrf_diag_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        2 * kMaxNb * (kMaxNb + 1) * (int)sizeof(float));
+    hipFuncSetAttribute((const void *)potrf_diag_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        2 * 128 * 128 * (int)sizeof(float));
+    hipFuncSetAttribute((const void *)potrf_diag_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        2 * 64 * 64 * (int)sizeof(float));
     attr_set = true;
   }
-  hipLaunchKernelGGL(potrf_diag_kernel, dim3(count), dim3(kThreads), shmem, s, L, L_stride, d, k0, nb,
-                     Linv, Linv_stride, info);
+  if (nb == 128)
+    hipLaunchKernelGGL(potrf_diag_kernel<128>, dim3(count), dim3(kThreads), shmem, s, L, L_stride, d, k0,
+                       Linv, Linv_stride, info);
+  else
+    hipLaunchKernelGGL(potrf_diag_kernel<64>, dim3(count), dim3(kThreads), shmem, s, L, L_stride, d, k0,
+                       Linv, Linv_stride, info);
   return hipGetLastError();
 }
 
