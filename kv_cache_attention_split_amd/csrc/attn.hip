@@ -11,11 +11,16 @@
 //
 // bf16 kernel: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (bf16 in, fp32 accumulate);
 // the query index runs along the MFMA column, so each lane holds whole softmax rows' statistics and
-// the row max / row sum need only one exchange between the two wave halves. K tiles sit in LDS in
-// row-major [key][d]; V tiles are transposed into [d][key] while staging, with the keys of every
-// 16-key group permuted so that one 16-byte LDS read yields exactly the 8 keys a lane needs for the
-// P^T operand that the previous MFMA left in its registers. The running max is updated lazily: the
-// accumulator is rescaled only when the max grows by more than 2^8, so exp2 values stay <= 256.
+// the row max / row sum need only one exchange between the two wave halves. K and V tiles (64 keys)
+// are copied global -> LDS with global_load_lds (no staging registers) into row-major tiles whose
+// 16-byte chunks are XOR-swizzled per row; K operands are plain 16-byte LDS reads, V^T operands come
+// from ds_read_b64_tr_b16, whose 4-consecutive-key reads match the key order that the score MFMA
+// leaves in each lane's probability registers. The loop is software-pipelined by one tile: step t
+// issues the scores of tile t, then the value product of tile t-1 next to the softmax of tile t.
+// The running max is updated lazily: the accumulator is rescaled only when the max grows by more
+// than 2^8, so exp2 values stay <= 256.
+#include <type_traits>
+
 #include "ispa_internal.hpp"
 #include "device_common.hpp"
 
@@ -24,28 +29,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
-
-// Store one normalised 32-query block of the O^T accumulator as bf16 rows of A. Lane (l32, hf)
-// holds query l32 and, per 32-wide column block db, columns 8g + 4hf + {0..3}.
-template <int D>
-__device__ __forceinline__ void write_rows(const f32x16 (&o)[D / 32], float inv, void *out, int qi,
-                                           int n_q, int out_stride, int head_off, int hf) {
-  if (out == nullptr || qi >= n_q) return;
-  uint16_t *dst = (uint16_t *)out + (int64_t)qi * out_stride + head_off + 4 * hf;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 pk;
-      pk[0] = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
-      pk[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-      *(u32x2 *)(dst + 32 * db + 8 * g) = pk;
-    }
-}
-
-__device__ __forceinline__ void write_lse(float *out, float val, int head, int qi, int n_q, int hf) {
-  if (out != nullptr && hf == 0 && qi < n_q) out[(int64_t)head * n_q + qi] = val;
-}
 
 // Key/value rows of one segment run. The local run is the sink followed by the current chunk (two
 // pointers, split at the sink length); the history run is one pointer. All fields are uniform.
@@ -70,137 +53,131 @@ __device__ __forceinline__ SegRun seg_run(const AttnArgs &a, bool hist) {
   return r;
 }
 
-// Element offset of key row j of a run (rows past the end are clamped to the last row; their scores
-// are masked, so they only need to be readable).
-template <bool VALUE>
-__device__ __forceinline__ const uint16_t *run_row(const SegRun &r, int64_t j, int head_off) {
-  j = j < r.n ? j : r.n - 1;
-  const bool second = j >= r.split;
-  const int64_t jj = second ? j - r.split : j;
-  const uint16_t *base = VALUE ? (second ? r.v1 : r.v0) : (second ? r.k1 : r.k0);
-  const int64_t st = second ? r.s1 : r.s0;
-  return base + jj * st + head_off;
+// Key/value tiles live in LDS row-major ([key][d], D*2 bytes per row) with the 16-byte chunks of
+// row r stored at position chunk ^ swz(r). For D = 128 the swizzle is the bit-rotation
+// 4 (r mod 4) + (r/4 mod 4): the 16 rows of a K-operand read (same chunk) land on 16 different
+// positions, and so do the 4 rows x 4 chunks of a transposing V read.
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int kv_off(int r, int col) {   // byte offset of element (r, col)
+  return r * (D * 2) + ((((col >> 3) ^ kv_swz<D>(r))) << 4) + ((col & 7) << 1);
 }
 
-// Global -> register prefetch of key/value tile t (t < nt_loc: local run, else history run).
-// Common case: the tile lies inside one sub-run (sink, current or history) and needs no clamping;
-// then one uniform base pointer and a 32-bit row offset address every row. Tiles that cross the
-// sink/current split or the end of a run take the per-row path.
-template <int D, int BK>
-__device__ __forceinline__ void load_tile(const AttnArgs &a, int t, int nt_loc, int tid, int head_off,
-                                          int vg, int vc, u32x4 (&kreg)[BK * D / 8 / kThreads],
-                                          u32x4 (&vreg)[4]) {
-  constexpr int CPR = D / 8;
-  constexpr int KLD = BK * CPR / kThreads;
-  constexpr int VPAIRS = (BK / 4) * CPR;
-  const bool hist = t >= nt_loc;
-  const SegRun run = seg_run(a, hist);
-  const int64_t j0 = (int64_t)(hist ? t - nt_loc : t) * BK;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Stage one K or V tile (BK rows) into LDS with direct global->LDS loads: each wave instruction
+// fills 1 KiB (1024 / (2D) rows); lane l writes LDS position base + 16 l, so it fetches the global
+// chunk that the swizzle assigns to that position. The per-lane (row, chunk) of each of the wave's
+// instructions is fixed (`rr`, `cc8` = 8 * chunk), computed once by the caller.
+template <int D, int BK, bool VALUE>
+__device__ __forceinline__ void dma_tile(const SegRun &run, int64_t j0, int head_off, uint8_t *lds_tile,
+                                         int w, const int (&rr)[BK * D * 2 / 4096],
+                                         const int (&cc8)[BK * D * 2 / 4096]) {
+  constexpr int NW = BK * D * 2 / 4096;     // instructions per wave per tile
   const int64_t j1 = j0 + BK;
   const bool in_first = j1 <= run.split && j1 <= run.n;
   const bool in_second = j0 >= run.split && j1 <= run.n;
+  const uint16_t *base0 = VALUE ? run.v0 : run.k0;
+  const uint16_t *base1 = VALUE ? run.v1 : run.k1;
   if (in_first || in_second) {
-    const uint16_t *kb = in_first ? run.k0 + j0 * run.s0 : run.k1 + (j0 - run.split) * run.s1;
-    const uint16_t *vb = in_first ? run.v0 + j0 * run.s0 : run.v1 + (j0 - run.split) * run.s1;
-    const int st = (int)(in_first ? run.s0 : run.s1);
-    kb += head_off;
-    vb += head_off;
+    // whole tile inside one sub-run: uniform base + 32-bit per-lane offset
+    const uint16_t *tb = (in_first ? base0 + j0 * run.s0 : base1 + (j0 - run.split) * run.s1) + head_off;
+    const uint32_t st = (uint32_t)(in_first ? run.s0 : run.s1);
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / CPR, c = idx % CPR;
-      kreg[i] = *(const u32x4 *)(kb + (row * st + 8 * c));
-    }
-    if (tid < VPAIRS) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vreg[e] = *(const u32x4 *)(vb + ((4 * vg + e) * st + 8 * vc));
+    for (int ii = 0; ii < NW; ++ii) {
+      const uint32_t off = (uint32_t)rr[ii] * st + (uint32_t)cc8[ii];
+      __builtin_amdgcn_global_load_lds((const void *)(tb + off),
+                                       (__attribute__((address_space(3))) void *)(lds_tile + 1024 * (w + 4 * ii)),
+                                       16, 0, 0);
     }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < KLD; ++i) {
-    const int idx = tid + kThreads * i;
-    const int row = idx / CPR, c = idx % CPR;
-    kreg[i] = *(const u32x4 *)(run_row<false>(run, j0 + row, head_off) + 8 * c);
-  }
-  if (tid < VPAIRS) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      vreg[e] = *(const u32x4 *)(run_row<true>(run, j0 + 4 * vg + e, head_off) + 8 * vc);
+  for (int ii = 0; ii < NW; ++ii) {
+    int64_t j = j0 + rr[ii];
+    j = j < run.n ? j : run.n - 1;
+    const bool second = j >= run.split;
+    const int64_t jj = second ? j - run.split : j;
+    const uint16_t *src = (second ? base1 : base0) + jj * (second ? run.s1 : run.s0) + head_off + cc8[ii];
+    __builtin_amdgcn_global_load_lds((const void *)src,
+                                     (__attribute__((address_space(3))) void *)(lds_tile + 1024 * (w + 4 * ii)),
+                                     16, 0, 0);
   }
 }
 
-// Register -> LDS: K row-major [key][d]; V transposed to [d][key position] (4-key groups of each
-// 16-key run at positions {0,2,1,3}, see the kernel comment).
-template <int D, int BK, int KST, int VST>
-__device__ __forceinline__ void store_tile(uint16_t *k_lds, uint16_t *v_lds, int tid, int vc, int vpos,
-                                           const u32x4 (&kreg)[BK * D / 8 / kThreads],
-                                           const u32x4 (&vreg)[4]) {
-  constexpr int CPR = D / 8;
-  constexpr int KLD = BK * CPR / kThreads;
-  constexpr int VPAIRS = (BK / 4) * CPR;
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define ISPA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
+
+// Store one normalised 32-query block of the O^T accumulator as bf16 rows of A. Lane (l32, hf)
+// holds query l32 and, per 32-wide column block db, columns 8g + 4hf + {0..3}.
+template <int D>
+__device__ __forceinline__ void write_rows(const f32x16 (&o)[D / 32], float inv, void *out, int qi,
+                                           int n_q, int out_stride, int head_off, int hf) {
+  if (out == nullptr || qi >= n_q) return;
+  uint16_t *dst = (uint16_t *)out + (int64_t)qi * out_stride + head_off + 4 * hf;
 #pragma unroll
-  for (int i = 0; i < KLD; ++i) {
-    const int idx = tid + kThreads * i;
-    const int row = idx / CPR, c = idx % CPR;
-    *(u32x4 *)&k_lds[row * KST + 8 * c] = kreg[i];
-  }
-  if (tid < VPAIRS) {
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const uint32_t x0 = u4_get(vreg[0], mm), x1 = u4_get(vreg[1], mm);
-      const uint32_t x2 = u4_get(vreg[2], mm), x3 = u4_get(vreg[3], mm);
-      u32x2 lo, hi;
-      lo[0] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
-      const int d0 = 8 * vc + 2 * mm;
-      *(u32x2 *)&v_lds[d0 * VST + vpos] = lo;
-      *(u32x2 *)&v_lds[(d0 + 1) * VST + vpos] = hi;
+    for (int g = 0; g < 4; ++g) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv);
+      pk[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      *(u32x2 *)(dst + 32 * db + 8 * g) = pk;
     }
-  }
 }
 
-template <int D, int QB>
-__global__ void __launch_bounds__(kThreads, QB == 1 ? 2 : 1) attn_dual_bf16_kernel(AttnArgs a, int n_qt) {
-  constexpr int BK = 64;             // keys per tile
-  constexpr int KST = D + 8;         // K tile row stride (elements), padded against bank conflicts
-  constexpr int VST = BK + 8;        // V^T tile row stride
-  constexpr int BQ = 4 * 32 * QB;    // queries per workgroup
-  constexpr int NKK = D / 16;        // MFMA k-steps of Q.K
-  constexpr int NDB = D / 32;        // 32-wide output column blocks
-  constexpr int NB = BK / 32;        // 32-key blocks per tile
-  constexpr int CPR = D / 8;         // 16-byte chunks per key row
-  constexpr int KLD = BK * CPR / kThreads;
-  constexpr int VPAIRS = (BK / 4) * CPR;   // (4-key group, chunk) pairs per V tile
-  static_assert(KLD >= 1 && VPAIRS <= kThreads, "tile shape");
+__device__ __forceinline__ void write_lse(float *out, float val, int head, int qi, int n_q, int hf) {
+  if (out != nullptr && hf == 0 && qi < n_q) out[(int64_t)head * n_q + qi] = val;
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VST];
+#ifndef ISPA_ATTN_BK
+#define ISPA_ATTN_BK 64
+#endif
+#ifndef ISPA_ATTN_PIPE
+#define ISPA_ATTN_PIPE 1
+#endif
+#ifndef ISPA_ATTN_WGS
+#define ISPA_ATTN_WGS 2
+#endif
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel(AttnArgs a, int n_qt) {
+  constexpr int BK = ISPA_ATTN_BK;    // keys per tile
+  constexpr bool PIPE = ISPA_ATTN_PIPE;
+  constexpr int TB = BK * D * 2;      // bytes per K or V tile
+  constexpr int NKK = D / 16;         // MFMA k-steps of Q.K
+  constexpr int NDB = D / 32;         // 32-wide output column blocks
+  constexpr int NB = BK / 32;         // 32-key blocks per tile
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][TB];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int vid = xcd_remap(blockIdx.x, n_qt * a.n_heads);
   const int head = vid / n_qt, qt = vid % n_qt;
   const int head_off = head * D;
-  const int qrow0 = qt * BQ + w * 32 * QB;
+  const int qrow0 = qt * 128 + w * 32;
+  const int qi = qrow0 + l32;
   const int n_q = a.n_q;
   const int out_stride = a.n_heads * D;
   const float sl2 = a.scale_log2;
 
   // Q^T operand, kept in registers for the whole pass: lane holds query l32, d = 16kk + 8hf .. +8.
-  bf16x8 qr[QB][NKK];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qrow0 + qb * 32 + l32;
+  bf16x8 qr[NKK];
+  {
     const bool ok = qi < n_q;
     const uint16_t *src = (const uint16_t *)a.q + (int64_t)(ok ? qi : 0) * a.q_stride + head_off + hf * 8;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 x = *(const u32x4 *)(src + kk * 16);
       if (!ok) x = u32x4{0u, 0u, 0u, 0u};
-      qr[qb][kk] = __builtin_bit_cast(bf16x8, x);
+      qr[kk] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
@@ -209,155 +186,236 @@ __global__ void __launch_bounds__(kThreads, QB == 1 ? 2 : 1) attn_dual_bf16_kern
   const int nt_hist = (int)((a.hist_n + BK - 1) / BK);
   const int nt = nt_loc + nt_hist;
 
-  f32x16 o[QB][NDB];
-  float m[QB], l[QB], l_loc[QB];
+  // per-lane geometry of this wave's DMA instructions (same for K and V tiles)
+  constexpr int NW = BK * D * 2 / 4096;
+  int drow[NW], dcol8[NW];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-    l_loc[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[qb][db][v] = 0.f;
+  for (int ii = 0; ii < NW; ++ii) {
+    constexpr int CPR = D / 8;
+    const int r = (w + 4 * ii) * (1024 / (2 * D)) + lane / CPR;
+    drow[ii] = r;
+    dcol8[ii] = 8 * ((lane % CPR) ^ kv_swz<D>(r));
   }
+  auto tile_j0 = [&](int t) -> int64_t { return (int64_t)(t >= nt_loc ? t - nt_loc : t) * BK; };
+  auto dma_k = [&](int t, int buf) {
+    dma_tile<D, BK, false>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, kbuf[buf], w, drow, dcol8);
+  };
+  auto dma_v = [&](int t, int buf) {
+    dma_tile<D, BK, true>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, vbuf[buf], w, drow, dcol8);
+  };
+  auto n_valid_of = [&](int t) -> int {
+    const int64_t nseg = t >= nt_loc ? a.hist_n : n_loc;
+    const int64_t rem = nseg - tile_j0(t);
+    return (int)(rem < BK ? rem : BK);
+  };
 
-  u32x4 kreg[KLD];
-  u32x4 vreg[4];
-  const int vg = tid % (BK / 4);     // 4-key group handled by this thread (V staging)
-  const int vc = tid / (BK / 4);     // 16-byte chunk along d (V staging)
-  // position of this thread's key group inside its 16-key run: groups {0,1,2,3} -> {0,2,1,3}
-  const int vg3 = vg & 3;
-  const int vpos = 4 * ((vg & ~3) | ((vg3 == 1) ? 2 : (vg3 == 2) ? 1 : vg3));
-
-  // ---- main pass -------------------------------------------------------------------------------
-  load_tile<D, BK>(a, 0, nt_loc, tid, head_off, vg, vc, kreg, vreg);
-  store_tile<D, BK, KST, VST>(k_lds[0], v_lds[0], tid, vc, vpos, kreg, vreg);
-  __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nt) load_tile<D, BK>(a, t + 1, nt_loc, tid, head_off, vg, vc, kreg, vreg);
-    const bool in_hist = t >= nt_loc;
-    const int64_t j0 = (int64_t)(in_hist ? t - nt_loc : t) * BK;
-    const int64_t nseg = in_hist ? a.hist_n : n_loc;
-    const int n_valid = (int)((nseg - j0) < BK ? (nseg - j0) : BK);
-
-    // S^T[key][query] = K Q^T
-    f32x16 s[QB][NB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[qb][b][v] = 0.f;
+  // S^T[key][query] = K Q^T for one tile (K operand: one 16-byte read per MFMA, read one MFMA
+  // ahead so that LDS latency hides behind the previous MFMA).
+  auto kread = [&](int buf, int i) -> bf16x8 {
+    const int kk = i / NB, b = i % NB;
+    return *(const bf16x8 *)(kbuf[buf] + kv_off<D>(32 * b + l32, 16 * kk + 8 * hf));
+  };
+  auto qk = [&](f32x16 (&s)[NB], int buf) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 kop = *(const bf16x8 *)&k_lds[buf][(32 * b + l32) * KST + 16 * kk + 8 * hf];
+      for (int v = 0; v < 16; ++v) s[b][v] = 0.f;
+    bf16x8 kcur = kread(buf, 0);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][b] = mfma_bf16_32x32x16(kop, qr[qb][kk], s[qb][b]);
+    for (int i = 0; i < NKK * NB; ++i) {
+      const bf16x8 knext = kread(buf, i + 1 < NKK * NB ? i + 1 : i);
+      s[i % NB] = mfma_bf16_32x32x16(kcur, qr[i / NB], s[i % NB]);
+      kcur = knext;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
+  float m = -INFINITY, l = 0.f, l_loc = 0.f;
+
+  // O^T[d][query] += V^T P^T for tile u; V^T operands by transposing reads of the row-major V tile:
+  // rows 32b + 16h2 + 4hf + (0..3) and the same + 8, matching the key order of p[b][h2].
+  // MFMA i of a tile covers column block db = i / (2 NB), key block b = (i / 2) % NB, half h2 = i % 2.
+  constexpr int NPV = NDB * NB * 2;
+  const int g = lane >> 4, sl = lane & 15;
+  auto vread = [&](int u, int i) -> bf16x8 {
+    const uint8_t *vt = vbuf[u & 1];
+    const int db = i / (2 * NB), b = (i / 2) % NB, h2 = i % 2;
+    const int col = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
+    const int row = 32 * b + 16 * h2 + 4 * (g >> 1) + (sl >> 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(vt + kv_off<D>(row, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(vt + kv_off<D>(row + 8, col)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pv = [&](int u, const bf16x8 (&p)[NB][2]) {
+    bf16x8 vcur = vread(u, 0);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const bf16x8 vnext = vread(u, i + 1 < NPV ? i + 1 : i);
+      const int db = i / (2 * NB), b = (i / 2) % NB, h2 = i % 2;
+      o[db] = mfma_bf16_32x32x16(vcur, p[b][h2], o[db]);
+      vcur = vnext;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Store A_loc / lse_loc once the local tiles are all in the accumulator; the history then keeps
+  // adding to the same state with its exp-sum kept apart.
+  auto snapshot_local = [&]() {
+    const float tot = l + swap_halves(l);
+    const float inv = 1.0f / tot;
+    const float lse = (m + __log2f(tot)) * kLn2;
+    write_rows<D>(o, inv, a.a_loc, qi, n_q, out_stride, head_off, hf);
+    write_lse(a.lse_loc, lse, head, qi, n_q, hf);
+    if (nt_hist == 0) {
+      write_rows<D>(o, inv, a.a_full, qi, n_q, out_stride, head_off, hf);
+      write_lse(a.lse_full, lse, head, qi, n_q, hf);
+      write_lse(a.lse_hist, -INFINITY, head, qi, n_q, hf);
+    }
+    l_loc = l;
+    l = 0.f;
+  };
+
+  // Step t (software-pipelined by one tile): loads for the next step, the scores of tile t, then
+  // the value product of tile t-1 (MFMA) interleaved with the softmax of tile t (VALU), which are
+  // independent; a rare rescale of the accumulator when the running max grew by more than 2^8.
+  auto step = [&](auto has_pv, int t, const bf16x8 (&pp)[NB][2], bf16x8 (&pc)[NB][2]) {
+    if constexpr (PIPE) {
+      if (t + 1 < nt) dma_k(t + 1, (t + 1) & 1);
+      dma_v(t, t & 1);
+    } else {
+      if (t + 1 < nt) {
+        dma_k(t + 1, (t + 1) & 1);
+        dma_v(t + 1, (t + 1) & 1);
       }
+    }
+    f32x16 sc[NB];
+    qk(sc, t & 1);
+    const int n_valid = n_valid_of(t);
     if (n_valid < BK) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = 32 * b + 8 * (v >> 2) + 4 * hf + (v & 3);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][b][v] = key < n_valid ? s[qb][b][v] : -INFINITY;
+          sc[b][v] = key < n_valid ? sc[b][v] : -INFINITY;
         }
     }
-    // online softmax (log2 domain, lazy max update)
-    bf16x8 pk[QB][NB][2];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[b][v]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float mnew = mx * sl2;
+    const bool need = mnew > m + kRescaleThreshold;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
+    const float mt = need ? mnew : m;
+    const float mneg = -mt;
+    float sum = 0.f;
+    // The 32 probabilities of this tile are produced in NPV slices, one after each MFMA of the
+    // previous tile's value product, so the VALU work overlaps the matrix pipe.
+    constexpr int EPS = NB * 16 / NPV;       // elements per slice
+    static_assert(EPS >= 2 && EPS * NPV == NB * 16, "slices must cover the tile");
+    uint32_t pw[NB * 8];
+    bf16x8 vcur;
+    if constexpr (decltype(has_pv)::value) vcur = vread(t - 1, 0);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][b][v]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mnew = mx * sl2;
-      const bool need = mnew > m[qb] + kRescaleThreshold;
-      if (__ballot(need) != 0ull) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m[qb] - mnew) : 1.0f;
-        m[qb] = need ? mnew : m[qb];
-        l[qb] *= alpha;
-        l_loc[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[qb][db][v] *= alpha;
+    for (int i = 0; i < NPV; ++i) {
+      bf16x8 vnext;
+      if constexpr (decltype(has_pv)::value) {
+        vnext = vread(t - 1, i + 1 < NPV ? i + 1 : i);
+        const int db = i / (2 * NB), b = (i / 2) % NB, h2 = i % 2;
+        o[db] = mfma_bf16_32x32x16(vcur, pp[b][h2], o[db]);
       }
-      const float mneg = -m[qb];
-      float sum = 0.f;
+      const float mneg_i = mneg;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][8 * h2 + e], sl2, mneg));
-            sum += p[e];
-          }
-          u32x4 u;
-          u[0] = pack_bf16x2(p[0], p[1]);
-          u[1] = pack_bf16x2(p[2], p[3]);
-          u[2] = pack_bf16x2(p[4], p[5]);
-          u[3] = pack_bf16x2(p[6], p[7]);
-          pk[qb][b][h2] = __builtin_bit_cast(bf16x8, u);
-        }
+      for (int e = 0; e < EPS; e += 2) {
+        const int f = i * EPS + e;            // flattened element: block f / 16, index f % 16
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[f / 16][f % 16], sl2, mneg_i));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[f / 16][f % 16 + 1], sl2, mneg_i));
+        sum += p0 + p1;
+        pw[f / 2] = pack_bf16x2(p0, p1);
       }
-      l[qb] += sum;
+      if constexpr (decltype(has_pv)::value) vcur = vnext;
     }
-    // O^T[d][query] += V^T P^T
+#ifdef ISPA_IGLP
+    __builtin_amdgcn_iglp_opt(ISPA_IGLP);
+#endif
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        u32x4 u;
+        u[0] = pw[b * 8 + h2 * 4 + 0];
+        u[1] = pw[b * 8 + h2 * 4 + 1];
+        u[2] = pw[b * 8 + h2 * 4 + 2];
+        u[3] = pw[b * 8 + h2 * 4 + 3];
+        pc[b][h2] = __builtin_bit_cast(bf16x8, u);
+      }
+    // the accumulator now holds tiles 0..t-1 at the previous max
+    if constexpr (PIPE) {
+      if (t - 1 == nt_loc - 1) snapshot_local();
+    }
+    if (__ballot(need) != 0ull) {
+      l *= alpha;
+      l_loc *= alpha;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16x8 vop =
-              *(const bf16x8 *)&v_lds[buf][(32 * db + l32) * VST + 32 * b + 16 * h2 + 8 * hf];
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma_bf16_32x32x16(vop, pk[qb][b][h2], o[qb][db]);
-        }
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    }
+    m = mt;
+    l += sum;
+    if constexpr (!PIPE) {
+      pv(t, pc);
+      if (t == nt_loc - 1) snapshot_local();
+    }
+    ISPA_WAIT_VMCNT(0);   // this wave's loads of K(t+1) and V(t) have landed
+    __syncthreads();      // ... and everyone's; all reads of this step's buffers are done
+  };
 
-    if (t == nt_loc - 1) {
-      // local branch complete: store A_loc / lse_loc, then keep the local exp-sum apart.
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float tot = l[qb] + swap_halves(l[qb]);
-        const float inv = 1.0f / tot;
-        const float lse = (m[qb] + __log2f(tot)) * kLn2;
-        const int qi = qrow0 + qb * 32 + l32;
-        write_rows<D>(o[qb], inv, a.a_loc, qi, n_q, out_stride, head_off, hf);
-        write_lse(a.lse_loc, lse, head, qi, n_q, hf);
-        if (nt_hist == 0) {
-          write_rows<D>(o[qb], inv, a.a_full, qi, n_q, out_stride, head_off, hf);
-          write_lse(a.lse_full, lse, head, qi, n_q, hf);
-          write_lse(a.lse_hist, -INFINITY, head, qi, n_q, hf);
-        }
-        l_loc[qb] = l[qb];
-        l[qb] = 0.f;
-      }
-    }
-    if (t + 1 < nt) store_tile<D, BK, KST, VST>(k_lds[buf ^ 1], v_lds[buf ^ 1], tid, vc, vpos, kreg, vreg);
+  using no_pv = std::integral_constant<bool, false>;
+  using with_pv = std::integral_constant<bool, true>;
+  bf16x8 pa[NB][2], pb[NB][2];
+  if constexpr (PIPE) {
+    dma_k(0, 0);
+    ISPA_WAIT_VMCNT(0);
     __syncthreads();
-  }
-  if (nt_hist > 0) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float th = l[qb] + swap_halves(l[qb]);
-      const float tl = l_loc[qb] + swap_halves(l_loc[qb]);
-      const float tot = th + tl;
-      const int qi = qrow0 + qb * 32 + l32;
-      write_rows<D>(o[qb], 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
-      write_lse(a.lse_full, (m[qb] + __log2f(tot)) * kLn2, head, qi, n_q, hf);
-      write_lse(a.lse_hist, th > 0.f ? (m[qb] + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
+    step(no_pv{}, 0, pb, pa);
+    int t = 1;
+    for (; t + 1 < nt; t += 2) {
+      step(with_pv{}, t, pa, pb);
+      step(with_pv{}, t + 1, pb, pa);
     }
+    if (t < nt) {
+      step(with_pv{}, t, pa, pb);
+      pv(t, pb);
+    } else {
+      pv(t - 1, pa);
+    }
+    if (nt - 1 == nt_loc - 1) snapshot_local();
+  } else {
+    dma_k(0, 0);
+    dma_v(0, 0);
+    ISPA_WAIT_VMCNT(0);
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) step(no_pv{}, t, pb, pa);
+  }
+
+  if (nt_hist > 0) {
+    const float th = l + swap_halves(l);
+    const float tl = l_loc + swap_halves(l_loc);
+    const float tot = th + tl;
+    write_rows<D>(o, 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
+    write_lse(a.lse_full, (m + __log2f(tot)) * kLn2, head, qi, n_q, hf);
+    write_lse(a.lse_hist, th > 0.f ? (m + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
   }
 }
 
@@ -466,21 +524,14 @@ __global__ void __launch_bounds__(128) attn_dual_f32_kernel(AttnArgs a, int n_qt
 
 }  // namespace
 
-// Queries per workgroup of the bf16 kernel: 128 * QB.
-#ifndef ISPA_ATTN_QB
-#define ISPA_ATTN_QB 1
-#endif
-
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s) {
-  constexpr int QB = ISPA_ATTN_QB;
-  const int bq = 128 * QB;
-  const int n_qt = (a.n_q + bq - 1) / bq;
+  const int n_qt = (a.n_q + 127) / 128;
   const int grid = n_qt * a.n_heads;
   if (grid == 0) return hipSuccess;
   if (head_dim == 128)
-    hipLaunchKernelGGL((attn_dual_bf16_kernel<128, QB>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
+    hipLaunchKernelGGL((attn_dual_bf16_kernel<128>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
   else
-    hipLaunchKernelGGL((attn_dual_bf16_kernel<64, QB>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
+    hipLaunchKernelGGL((attn_dual_bf16_kernel<64>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
   return hipGetLastError();
 }
 
