@@ -9,7 +9,7 @@ L-Layers (errors copied to the host and ranked there). Inputs are seeded synthet
 resident in HBM when the timed region starts.
 
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s (attention 4 n_q n_keys H d_h per
-call, statistics 4 N d^2 per chunk, solve 13/3 d^3, error 6 d^3 per layer) over the measured step
+call, statistics 4 N d^2 per chunk, solve 13/3 d^3, error 4 d^3 per layer) over the measured step
 time; the attention kernel's own rate, its fraction of the bf16 MFMA peak, and the absorb time per
 layer are reported beside it, with the oracle timed on the host cores on a bounded sample.
 """
@@ -109,7 +109,7 @@ def cpu_baseline(wl):
         oab.layer_error_stats(st["G"], st["C"], st["H"], w, dw)
         t_abs += time.perf_counter() - t0
         n_rows = sum(c["a_loc"].shape[0] for c in chunks)
-        f_abs += 4.0 * n_rows * d * d + 13.0 / 3.0 * d ** 3 + 6.0 * d ** 3
+        f_abs += 4.0 * n_rows * d * d + 13.0 / 3.0 * d ** 3 + 4.0 * d ** 3
     return {
         "value": round((f_att + f_abs) / (t_att + t_abs) / 1e12, 6),
         "unit": "TFLOP/s",
@@ -214,7 +214,7 @@ def main():
     flops_attn = sum(attn_flops(n_q, nk, H, dh) for nk in seg_keys) * n_layers
     flops_stats = 4.0 * n_q * len(wl.chunks) * d * d * n_layers
     flops_solve = 13.0 / 3.0 * d ** 3 * n_layers
-    flops_err = 6.0 * d ** 3 * n_layers
+    flops_err = 4.0 * d ** 3 * n_layers
     flops_step = flops_attn + flops_stats + flops_solve + flops_err
 
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731

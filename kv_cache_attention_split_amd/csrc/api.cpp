@@ -457,18 +457,21 @@ ispa_status ispa_layer_error(int32_t d, int32_t batch, const float *const *G, co
       }
       ISPA_TRY(launch_add(a, b, o, d, cnt, s));
     }
-    GemmShape sh{};
-    sh.M = d; sh.N = d; sh.K = d;
-    sh.lda = d; sh.ldb = d; sh.ldc = d; sh.lde = d;
-    sh.ta = 0; sh.tb = 0; sh.dot = 1;
-    sh.alpha = 1.f; sh.beta = 0.f;
-    // term 0: <W, F W>   term 1: <W', X W>   term 2: <W', G W'>   (W' = W + dW)
+    // eps = <F, W W^T> - 2 <X, W' W^T> + <G, W' W'^T>  (W' = W + dW; each <., .> equals the
+    // corresponding <W_a, S W_b> of the residual expansion). The first and last products are
+    // symmetric, so only their lower tiles are formed.
     for (int term = 0; term < 3; ++term) {
+      GemmShape sh{};
+      sh.M = d; sh.N = d; sh.K = d;
+      sh.lda = d; sh.ldb = d; sh.ldc = d; sh.lde = d;
+      sh.ta = 0; sh.tb = 1; sh.dot = 1;
+      sh.sym = term != 1;
+      sh.alpha = 1.f; sh.beta = 0.f;
       GemmBatch b{};
       for (int i = 0; i < cnt; ++i) {
-        b.A[i] = term == 0 ? F[p0 + i] : term == 1 ? X[p0 + i] : G[p0 + i];
+        b.A[i] = term == 0 ? Wuse[i] : Wp(i);
         b.B[i] = term == 2 ? Wp(i) : Wuse[i];
-        b.E[i] = term == 0 ? Wuse[i] : Wp(i);
+        b.E[i] = term == 0 ? F[p0 + i] : term == 1 ? X[p0 + i] : G[p0 + i];
       }
       ISPA_TRY(launch_gemm_f32(b, cnt, sh, part + ((int64_t)term * batch + p0) * part_d, part_d, s));
     }

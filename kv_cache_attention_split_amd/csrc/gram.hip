@@ -16,7 +16,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int BT = 128;          // output tile
-constexpr int BR = 32;           // rows per stage
+#ifndef ISPA_GRAM_BR
+#define ISPA_GRAM_BR 32
+#endif
+constexpr int BR = ISPA_GRAM_BR;  // rows per stage
 constexpr int RB = BT * 2;       // bytes of one tile row (128 bf16)
 
 struct GramArgs {
@@ -97,11 +100,12 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
   const int d = g.d;
   const int64_t last_row = g.n_rows - 1;
 
-  // staging: thread handles 16-byte chunks e = tid + 256 q (q = 0, 1) of each operand tile:
+  // staging: thread handles 16-byte chunks e = tid + 256 q (q < NQ) of each operand tile:
   // row r = e / 16, chunk c = e % 16. Columns past d are clamped (their outputs are not stored).
-  int srow[2], scol_p[2], scol_q[2], soff[2];
+  constexpr int NQ = BR * 16 / kThreads;
+  int srow[NQ], scol_p[NQ], scol_q[NQ], soff[NQ];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     const int e = tid + kThreads * q;
     const int r = e >> 4, c = e & 15;
     srow[q] = r;
@@ -110,30 +114,30 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
     scol_q[q] = cq < d ? cq : d - 8;
     soff[q] = r * RB + ((c ^ (4 * (r & 3))) << 4);
   }
-  u32x4 ra[4], rb[4];   // [operand * 2 + q]
-  auto load = [&](u32x4 (&r)[4], int64_t n0) {
+  u32x4 ra[2 * NQ], rb[2 * NQ];   // [operand * NQ + q]
+  auto load = [&](u32x4 (&r)[2 * NQ], int64_t n0) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       int64_t n = n0 + srow[q];
       n = n < last_row ? n : last_row;
       r[q] = *(const u32x4 *)(P + n * d + scol_p[q]);
-      r[2 + q] = *(const u32x4 *)(Q + n * d + scol_q[q]);
+      r[NQ + q] = *(const u32x4 *)(Q + n * d + scol_q[q]);
     }
   };
-  auto store = [&](const u32x4 (&r)[4], int buf, int64_t n0) {
+  auto store = [&](const u32x4 (&r)[2 * NQ], int buf, int64_t n0) {
     if (n0 + BR - 1 <= last_row) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         *(u32x4 *)(tile_ptr(buf, 0) + soff[q]) = r[q];
-        *(u32x4 *)(tile_ptr(buf, 1) + soff[q]) = r[2 + q];
+        *(u32x4 *)(tile_ptr(buf, 1) + soff[q]) = r[NQ + q];
       }
     } else {   // tail stage: rows past the chunk end contribute zeros
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         const bool ok = n0 + srow[q] <= last_row;
         const u32x4 z = {0u, 0u, 0u, 0u};
         *(u32x4 *)(tile_ptr(buf, 0) + soff[q]) = ok ? r[q] : z;
-        *(u32x4 *)(tile_ptr(buf, 1) + soff[q]) = ok ? r[2 + q] : z;
+        *(u32x4 *)(tile_ptr(buf, 1) + soff[q]) = ok ? r[NQ + q] : z;
       }
     }
   };

@@ -43,6 +43,8 @@ hipError_t launch_gram_bf16(int64_t n_rows, int d, const uint16_t *a_loc, const 
 //   lower: skip 128x128 output tiles lying strictly above the diagonal (col0 > row0 + 127)
 //   dot mode (E != NULL): instead of storing C, write per-tile partial sums
 //     sum_{tile} E[i*lde + j] * (alpha * (AB)[i][j]) in fp64 to part[p * tiles + tile]
+//   sym (dot mode, AB and E both symmetric): tiles above the diagonal are skipped (their partial
+//     is 0) and strictly-lower tiles count twice, so the partials still sum to <E, AB>
 // ------------------------------------------------------------------------------------------------
 constexpr int kMaxGemmBatch = 48;
 
@@ -58,6 +60,7 @@ struct GemmShape {
   int M, N, K;
   int lda, ldb, ldc, lde;
   int ta, tb, lower, sub, dot;
+  int sym;        // dot mode with a symmetric product and E: lower tiles only, off-diagonal ones x2
   float alpha, beta;
 };
 

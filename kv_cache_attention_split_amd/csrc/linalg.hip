@@ -28,6 +28,10 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
   const int tile = blockIdx.x;
   const int ti = tile / tn, tj = tile % tn;
   const int m0 = ti * GT, n0 = tj * GT;
+  if (sh.dot && sh.sym && tj > ti) {
+    if (threadIdx.x == 0) ((double *)bt.C[blockIdx.y])[tile] = 0.0;
+    return;
+  }
   if (sh.lower && n0 > m0 + GT - 1) return;
   const float *A = bt.A[p];
   const float *A2 = bt.A2[p];
@@ -37,72 +41,54 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wm = w >> 1, wn = w & 1;
 
-  f32x4 ra[2], rb[2];
+  // Staging: waves 0-1 stage the A tile, waves 2-3 the B tile. Each thread owns one 4 x 4 block
+  // (4 rows of the tile x 4 k) per stage. A row-major operand ([row][k]) is loaded as 4 float4 along
+  // k; a transposed one ([k][row]) as 4 float4 along rows and transposed in registers. Either way
+  // the LDS tile is [row][k] and is written with 16-byte stores; lanes 4q..4q+3 cover one row's
+  // 16 k, so a 16-lane group writes 256 distinct bytes.
+  const int sop = tid >> 7;                 // 0: A, 1: B
+  const int st_t = tid & 127;
+  const int kblk = st_t & 3, rblk = st_t >> 2;
+  const bool s_trans = sop == 0 ? (sh.ta != 0) : (sh.tb == 0);
+  const float *s_src = sop == 0 ? A : B;
+  const float *s_src2 = sop == 0 ? A2 : nullptr;
+  const int s_ld = sop == 0 ? sh.lda : sh.ldb;
+  const int s_rows = sop == 0 ? sh.M : sh.N;
+  const int s_r0 = (sop == 0 ? m0 : n0) + 4 * rblk;
+  const bool s_sub = sop == 0 && sh.sub;
+  f32x4 rg[4];
   auto load = [&](int k0) {
+    const int kc = k0 + 4 * kblk;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + kThreads * q;
-      // A operand
-      if (!sh.ta) {
-        const int row = idx >> 2, kq = idx & 3;
-        const int gi = m0 + row, gk = k0 + 4 * kq;
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (gi < sh.M && gk < sh.K) {
-          x = *(const f32x4 *)(A + (int64_t)gi * sh.lda + gk);
-          if (sh.sub) {
-            const f32x4 y = *(const f32x4 *)(A2 + (int64_t)gi * sh.lda + gk);
-            x -= y;
-          }
+    for (int e = 0; e < 4; ++e) {
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!s_trans) {
+        const int r = s_r0 + e;
+        if (r < s_rows && kc < sh.K) {
+          x = *(const f32x4 *)(s_src + (int64_t)r * s_ld + kc);
+          if (s_sub) x -= *(const f32x4 *)(s_src2 + (int64_t)r * s_ld + kc);
         }
-        ra[q] = x;
       } else {
-        const int kr = idx >> 5, iq = idx & 31;
-        const int gi = m0 + 4 * iq, gk = k0 + kr;
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (gi < sh.M && gk < sh.K) x = *(const f32x4 *)(A + (int64_t)gk * sh.lda + gi);
-        ra[q] = x;
+        const int k = kc + e;
+        if (s_r0 < s_rows && k < sh.K) x = *(const f32x4 *)(s_src + (int64_t)k * s_ld + s_r0);
       }
-      // B operand
-      if (sh.tb) {
-        const int row = idx >> 2, kq = idx & 3;
-        const int gj = n0 + row, gk = k0 + 4 * kq;
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (gj < sh.N && gk < sh.K) x = *(const f32x4 *)(B + (int64_t)gj * sh.ldb + gk);
-        rb[q] = x;
-      } else {
-        const int kr = idx >> 5, jq = idx & 31;
-        const int gj = n0 + 4 * jq, gk = k0 + kr;
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (gj < sh.N && gk < sh.K) x = *(const f32x4 *)(B + (int64_t)gk * sh.ldb + gj);
-        rb[q] = x;
-      }
+      rg[e] = x;
     }
   };
   auto store = [&](int buf) {
-    float *As = lds[buf][0];
-    float *Bs = lds[buf][1];
+    float *S = lds[buf][sop];
+    if (!s_trans) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = tid + kThreads * q;
-      if (!sh.ta) {
-        const int row = idx >> 2, kq = idx & 3;
-        *(f32x4 *)&As[row * GST + 4 * kq] = ra[q];
-      } else {
-        const int kr = idx >> 5, iq = idx & 31;
-        As[(4 * iq + 0) * GST + kr] = ra[q][0];
-        As[(4 * iq + 1) * GST + kr] = ra[q][1];
-        As[(4 * iq + 2) * GST + kr] = ra[q][2];
-        As[(4 * iq + 3) * GST + kr] = ra[q][3];
-      }
-      if (sh.tb) {
-        const int row = idx >> 2, kq = idx & 3;
-        *(f32x4 *)&Bs[row * GST + 4 * kq] = rb[q];
-      } else {
-        const int kr = idx >> 5, jq = idx & 31;
-        Bs[(4 * jq + 0) * GST + kr] = rb[q][0];
-        Bs[(4 * jq + 1) * GST + kr] = rb[q][1];
-        Bs[(4 * jq + 2) * GST + kr] = rb[q][2];
-        Bs[(4 * jq + 3) * GST + kr] = rb[q][3];
+      for (int e = 0; e < 4; ++e) *(f32x4 *)&S[(4 * rblk + e) * GST + 4 * kblk] = rg[e];
+    } else {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        f32x4 y;
+        y[0] = rg[0][f];
+        y[1] = rg[1][f];
+        y[2] = rg[2][f];
+        y[3] = rg[3][f];
+        *(f32x4 *)&S[(4 * rblk + f) * GST + 4 * kblk] = y;
       }
     }
   };
@@ -198,7 +184,8 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
   __syncthreads();
   if (tid == 0) {
     double *part = (double *)bt.C[p];   // dot mode: C holds this problem's partial array
-    part[tile] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    const double wgt = (sh.sym && ti != tj) ? 2.0 : 1.0;
+    part[tile] = wgt * (((wsum[0] + wsum[1]) + wsum[2]) + wsum[3]);
   }
 }
 
@@ -247,19 +234,18 @@ __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int6
     float piv = colst[j * NB + j];
     if (!(piv > 0.f)) piv = 1.f;   // recorded below; keeps the rest finite
     const float ip = 1.f / piv;
+    // entries of rows / columns <= j are zeroed, so the rank-1 update of the whole sub-block
+    // leaves them unchanged; the upper triangle is updated too (harmless, only the lower is read)
     float cr[R], cc[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      cr[i] = colst[j * NB + r0 + i] * ip;
-      cc[i] = colst[j * NB + c0 + i];
+      cr[i] = (r0 + i > j) ? colst[j * NB + r0 + i] * ip : 0.f;
+      cc[i] = (c0 + i > j) ? colst[j * NB + c0 + i] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int r = r0 + i, c = c0 + k;
-        if (r > j && c > j && c <= r) a[i][k] = fmaf(-cr[i], cc[k], a[i][k]);
-      }
+      for (int k = 0; k < R; ++k) a[i][k] = fmaf(-cr[i], cc[k], a[i][k]);
   }
   if (tid == 0) {
     for (int j = 0; j < NB; ++j)
@@ -288,17 +274,17 @@ __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int6
     float piv = colst[j * NB + j];
     if (!(piv > 0.f)) piv = 1.f;
     const float ip = 1.f / piv;
+    // row j of Y is zero beyond column j (Y is lower triangular); rows <= j get u = 0
     float u[R], yr[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      u[i] = colst[j * NB + r0 + i] * ip;
+      u[i] = (r0 + i > j) ? colst[j * NB + r0 + i] * ip : 0.f;
       yr[i] = rowst[j * NB + c0 + i];
     }
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
-      for (int k = 0; k < R; ++k)
-        if (r0 + i > j && c0 + k <= j) y[i][k] = fmaf(-u[i], yr[k], y[i][k]);
+      for (int k = 0; k < R; ++k) y[i][k] = fmaf(-u[i], yr[k], y[i][k]);
   }
   // L = U D^1/2 (lower part of the block), Linv = D^-1/2 Y
 #pragma unroll
