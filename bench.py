@@ -304,7 +304,7 @@ def main():
         "stats_tflops": round(flops_stats / stats_ms / 1e9, 1),
         "solve_info_nonzero": int(sum(1 for x in info_h if x != 0)),
         "selected_l_layers": sel,
-        "roofline": {"kernel": "attn_dual_bf16_kernel", "bound": "mfma",
+        "roofline": {"kernel": "attn_dual_bf16_pp_kernel", "bound": "mfma",
                      "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "avg_launch_ms": round(att_avg_ms, 5),

@@ -44,7 +44,8 @@ typedef enum {
 typedef enum { ISPA_F32 = 0, ISPA_BF16 = 1 } ispa_dtype;
 
 /* One KV-cache segment of a layer: keys and values [n, H, d_h] in the call's dtype.
- * row_stride (elements) is the distance between consecutive tokens, >= H*d_h. n may be 0 (then k and
+ * row_stride (elements) is the distance between consecutive tokens, >= H*d_h and < 2^23 (larger
+ * strides return ISPA_E_UNSUPPORTED). n may be 0 (then k and
  * v may be NULL). */
 typedef struct {
   const void *k;

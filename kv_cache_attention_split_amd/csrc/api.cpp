@@ -32,7 +32,7 @@ ispa_status check_segment(const ispa_kv_segment &s, int64_t min_stride, int64_t 
   if (s.k == nullptr || s.v == nullptr) return ISPA_E_ARG;
   if (!aligned16(s.k) || !aligned16(s.v)) return ISPA_E_ARG;
   if (s.row_stride < min_stride || s.row_stride % align_elems != 0) return ISPA_E_ARG;
-  if (s.row_stride > (int64_t(1) << 24)) return ISPA_E_UNSUPPORTED;   // 32-bit in-tile row offsets
+  if (s.row_stride >= (int64_t(1) << 23)) return ISPA_E_UNSUPPORTED;   // 24-bit in-tile row offsets
   return ISPA_OK;
 }
 

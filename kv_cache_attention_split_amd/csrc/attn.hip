@@ -113,6 +113,18 @@ __device__ __forceinline__ void dma_tile(const SegRun &run, int64_t j0, int head
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 #define ISPA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
 
+// Workgroup barrier that orders LDS accesses only: waits for this wave's LDS operations, not for its
+// outstanding global->LDS copies (those are waited for explicitly with ISPA_WAIT_VMCNT before the
+// barrier that publishes them). The empty asm statements keep the compiler from moving memory
+// accesses across it.
+#define ISPA_LDS_BARRIER()                 \
+  do {                                     \
+    asm volatile("" ::: "memory");         \
+    __builtin_amdgcn_s_waitcnt(0xc07f);    \
+    __builtin_amdgcn_s_barrier();          \
+    asm volatile("" ::: "memory");         \
+  } while (0)
+
 // Store one normalised 32-query block of the O^T accumulator as bf16 rows of A. Lane (l32, hf)
 // holds query l32 and, per 32-wide column block db, columns 8g + 4hf + {0..3}.
 template <int D>
@@ -420,6 +432,221 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
 }
 
 // ------------------------------------------------------------------------------------------------
+// Ping-pong kernel: 8 waves (two per SIMD), 256 queries per workgroup. Waves 0-3 (group A) and
+// 4-7 (group B) run the same loop, B one barrier behind A; every iteration has a matrix phase
+// (scores of tile i, value product of tile i-1) and a vector phase (softmax of tile i), separated by
+// workgroup barriers, so on each SIMD one wave's MFMAs run while the other wave's softmax runs.
+// Both groups read the same K/V tiles one phase apart; group A issues the global->LDS copies two
+// phases before the tiles are needed.
+// ------------------------------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, int n_qt) {
+  constexpr int BK = 64;
+  constexpr int TB = BK * D * 2;
+  constexpr int NKK = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int NB = BK / 32;
+  constexpr int NPV = NDB * NB * 2;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][TB];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int grp = w >> 2, wl = w & 3;
+  const int vid = xcd_remap(blockIdx.x, n_qt * a.n_heads);
+  const int head = vid / n_qt, qt = vid % n_qt;
+  const int head_off = head * D;
+  const int qi = qt * 256 + w * 32 + l32;
+  const int n_q = a.n_q;
+  const int out_stride = a.n_heads * D;
+  const float sl2 = a.scale_log2;
+
+  bf16x8 qr[NKK];
+  {
+    const bool ok = qi < n_q;
+    const uint16_t *src = (const uint16_t *)a.q + (int64_t)(ok ? qi : 0) * a.q_stride + head_off + hf * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 x = *(const u32x4 *)(src + kk * 16);
+      if (!ok) x = u32x4{0u, 0u, 0u, 0u};
+      qr[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  const int64_t n_loc = a.sink_n + a.cur_n;
+  const int nt_loc = (int)((n_loc + BK - 1) / BK);
+  const int nt_hist = (int)((a.hist_n + BK - 1) / BK);
+  const int nt = nt_loc + nt_hist;
+
+  constexpr int NW = BK * D * 2 / 4096;   // copy instructions per group-A wave per tile
+  int drow[NW], dcol8[NW];
+#pragma unroll
+  for (int ii = 0; ii < NW; ++ii) {
+    constexpr int CPR = D / 8;
+    const int r = (wl + 4 * ii) * (1024 / (2 * D)) + lane / CPR;
+    drow[ii] = r;
+    dcol8[ii] = 8 * ((lane % CPR) ^ kv_swz<D>(r));
+  }
+  auto tile_j0 = [&](int t) -> int64_t { return (int64_t)(t >= nt_loc ? t - nt_loc : t) * BK; };
+  auto dma_k = [&](int t, int buf) {
+    dma_tile<D, BK, false>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, kbuf[buf], wl, drow, dcol8);
+  };
+  auto dma_v = [&](int t, int buf) {
+    dma_tile<D, BK, true>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, vbuf[buf], wl, drow, dcol8);
+  };
+  auto n_valid_of = [&](int t) -> int {
+    const int64_t nseg = t >= nt_loc ? a.hist_n : n_loc;
+    const int64_t rem = nseg - tile_j0(t);
+    return (int)(rem < BK ? rem : BK);
+  };
+  auto kread = [&](int buf, int i) -> bf16x8 {
+    const int kk = i / NB, b = i % NB;
+    return *(const bf16x8 *)(kbuf[buf] + kv_off<D>(32 * b + l32, 16 * kk + 8 * hf));
+  };
+  const int g = lane >> 4, sl = lane & 15;
+  auto vread = [&](int u, int i) -> bf16x8 {
+    const uint8_t *vt = vbuf[u & 1];
+    const int db = i / (2 * NB), b = (i / 2) % NB, h2 = i % 2;
+    const int col = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
+    const int row = 32 * b + 16 * h2 + 4 * (g >> 1) + (sl >> 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(vt + kv_off<D>(row, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(vt + kv_off<D>(row + 8, col)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
+  float m = -INFINITY, l = 0.f, l_loc = 0.f;
+  f32x16 sc[NB];
+  bf16x8 pk[NB][2];
+
+  auto snapshot_local = [&]() {
+    const float tot = l + swap_halves(l);
+    const float inv = 1.0f / tot;
+    const float lse = (m + __log2f(tot)) * kLn2;
+    write_rows<D>(o, inv, a.a_loc, qi, n_q, out_stride, head_off, hf);
+    write_lse(a.lse_loc, lse, head, qi, n_q, hf);
+    if (nt_hist == 0) {
+      write_rows<D>(o, inv, a.a_full, qi, n_q, out_stride, head_off, hf);
+      write_lse(a.lse_full, lse, head, qi, n_q, hf);
+      write_lse(a.lse_hist, -INFINITY, head, qi, n_q, hf);
+    }
+    l_loc = l;
+    l = 0.f;
+  };
+
+  // prologue: K(0) for everyone; group B then falls one barrier behind
+  if (grp == 0) {
+    dma_k(0, 0);
+    ISPA_WAIT_VMCNT(0);
+  }
+  ISPA_LDS_BARRIER();
+  if (grp == 1) ISPA_LDS_BARRIER();
+
+  for (int i = 0; i <= nt; ++i) {
+    // ---- matrix phase: scores of tile i, value product of tile i-1 ----
+    if (grp == 0) {
+      if (i + 1 < nt) dma_k(i + 1, (i + 1) & 1);
+      if (i < nt) dma_v(i, i & 1);
+    }
+    if (i < nt) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sc[b][v] = 0.f;
+      bf16x8 kcur = kread(i & 1, 0);
+#pragma unroll
+      for (int j = 0; j < NKK * NB; ++j) {
+        const bf16x8 knext = kread(i & 1, j + 1 < NKK * NB ? j + 1 : j);
+        sc[j % NB] = mfma_bf16_32x32x16(kcur, qr[j / NB], sc[j % NB]);
+        kcur = knext;
+      }
+    }
+    if (i > 0) {
+      bf16x8 vcur = vread(i - 1, 0);
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) {
+        const bf16x8 vnext = vread(i - 1, j + 1 < NPV ? j + 1 : j);
+        const int db = j / (2 * NB), b = (j / 2) % NB, h2 = j % 2;
+        o[db] = mfma_bf16_32x32x16(vcur, pk[b][h2], o[db]);
+        vcur = vnext;
+      }
+    }
+    ISPA_LDS_BARRIER();   // copies in flight stay in flight across this barrier
+    // ---- vector phase: softmax of tile i ----
+    if (i - 1 == nt_loc - 1) snapshot_local();   // accumulator holds tiles 0 .. nt_loc-1
+    if (i < nt) {
+      const int n_valid = n_valid_of(i);
+      if (n_valid < BK) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = 32 * b + 8 * (v >> 2) + 4 * hf + (v & 3);
+            sc[b][v] = key < n_valid ? sc[b][v] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[b][v]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float mnew = mx * sl2;
+      const bool need = mnew > m + kRescaleThreshold;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
+      m = need ? mnew : m;
+      const float mneg = -m;
+      float sum = 0.f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][8 * h2 + e], sl2, mneg));
+            sum += p[e];
+          }
+          u32x4 u;
+          u[0] = pack_bf16x2(p[0], p[1]);
+          u[1] = pack_bf16x2(p[2], p[3]);
+          u[2] = pack_bf16x2(p[4], p[5]);
+          u[3] = pack_bf16x2(p[6], p[7]);
+          pk[b][h2] = __builtin_bit_cast(bf16x8, u);
+        }
+      if (__ballot(need) != 0ull) {
+        l *= alpha;
+        l_loc *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      }
+      l += sum;
+    }
+    if (grp == 0) ISPA_WAIT_VMCNT(0);   // this step's copies (K(i+1), V(i)) have landed
+    ISPA_LDS_BARRIER();
+  }
+  if (grp == 0) ISPA_LDS_BARRIER();     // matches group B's extra prologue barrier
+
+  if (nt_hist > 0) {
+    const float th = l + swap_halves(l);
+    const float tl = l_loc + swap_halves(l_loc);
+    const float tot = th + tl;
+    write_rows<D>(o, 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
+    write_lse(a.lse_full, (m + __log2f(tot)) * kLn2, head, qi, n_q, hf);
+    write_lse(a.lse_hist, th > 0.f ? (m + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // fp32 kernel: VALU, one query per thread. Same single pass and the same local/history split.
 // ------------------------------------------------------------------------------------------------
 template <int D>
@@ -524,7 +751,18 @@ __global__ void __launch_bounds__(128) attn_dual_f32_kernel(AttnArgs a, int n_qt
 
 }  // namespace
 
+#ifndef ISPA_ATTN_PP
+#define ISPA_ATTN_PP 1
+#endif
+
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s) {
+  if (ISPA_ATTN_PP && head_dim == 128) {
+    const int n_qt = (a.n_q + 255) / 256;
+    const int grid = n_qt * a.n_heads;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128>), dim3(grid), dim3(512), 0, s, a, n_qt);
+    return hipGetLastError();
+  }
   const int n_qt = (a.n_q + 127) / 128;
   const int grid = n_qt * a.n_heads;
   if (grid == 0) return hipSuccess;

@@ -72,6 +72,9 @@ def test_attn_argument_errors(L):
     assert attn(L, scale=0.0) == _abi.ISPA_E_ARG
     assert attn(L, scale=float("nan")) == _abi.ISPA_E_ARG
     assert attn(L, n_q=-1) == _abi.ISPA_E_ARG
+    # row strides of 2^23 elements or more are outside the kernels' 24-bit in-tile offsets
+    assert attn(L, hist=seg(stride=1 << 23)) == _abi.ISPA_E_UNSUPPORTED
+    assert attn(L, sink=seg(stride=(1 << 23) + 8)) == _abi.ISPA_E_UNSUPPORTED
     # empty local context (softmax over an empty set)
     assert attn(L, sink=seg(n=0), cur=seg(n=0)) == _abi.ISPA_E_ARG
     # misaligned pointers, short or misaligned strides
