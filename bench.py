@@ -81,6 +81,25 @@ class Layer:
         return self.k[a:b], self.v[a:b]
 
 
+# HBM bytes per attention launch of the warmup step (average over its 4 chunk shapes), from
+# rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
+# attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only
+# while the source is unchanged.
+ATTN_TRAFFIC = {"sha256": "e126010e4f6c9cdbb1384b2307dc0b9a8b6a84c7d00c819fa233fb80e4fcdcbf",
+                "bytes_per_launch": 159219272}
+
+
+def attn_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "kv_cache_attention_split_amd", "csrc", "attn.hip")
+    try:
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return ATTN_TRAFFIC["bytes_per_launch"] if digest == ATTN_TRAFFIC["sha256"] else None
+
+
 def cpu_baseline(wl):
     """The oracle (fp64 NumPy) on a bounded sample of the same workload, timed on the host cores."""
     import ispa_inputs as inputs
@@ -88,16 +107,16 @@ def cpu_baseline(wl):
     from oracle import attention as oatt
     cores = len(os.sched_getaffinity(0))
     H, dh, d = wl.n_heads, wl.head_dim, wl.d
-    # (a) attention of 2048 query rows of chunk 4 (all heads, 18720 keys)
+    # (a) attention of 6144 query rows of chunk 4 (all heads, 18720 keys)
     inp = inputs.attention_inputs(wl.cfg, 0, 3)
-    rows = np.arange(2048)
+    rows = np.arange(6144)
     t0 = time.perf_counter()
     oatt.dual_stream(inp, rows=rows)
     t_att = time.perf_counter() - t0
     n_keys = sum(inp[k].shape[0] for k in ("sink_k", "cur_k", "hist_k"))
     f_att = attn_flops(len(rows), n_keys, H, dh)
-    # (b) Layer Absorb of 4 layers: statistics over the 4 warmup chunks, solve, error
-    n_abs_layers = 4
+    # (b) Layer Absorb of 8 layers: statistics over the 4 warmup chunks, solve, error
+    n_abs_layers = 8
     t_abs = 0.0
     f_abs = 0.0
     for layer in range(n_abs_layers):
@@ -306,7 +325,7 @@ def main():
         "selected_l_layers": sel,
         "roofline": {"kernel": "attn_dual_bf16_pp_kernel", "bound": "mfma",
                      "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic(),
                      "avg_launch_ms": round(att_avg_ms, 5),
                      "flops_per_launch": att_flops_per_launch},
         "setup_s": round(t_setup, 1),
