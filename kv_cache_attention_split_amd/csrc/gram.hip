@@ -8,19 +8,40 @@
 // exactly symmetric. X is computed in full. Each output element is owned by one workgroup, which
 // reduces over all rows of the chunk in a fixed order and adds its result to the running sum with a
 // plain read-modify-write: no atomics, so the sums are deterministic.
+//
+// Operand rows reach LDS through a ring of four 32-row stages filled by global_load_lds (no staging
+// registers, no LDS store instructions): while stage s is multiplied, stages s+1..s+3 are in flight.
+// Rows past the end of the chunk are copied from a 16-byte block of zeros, so the loop always runs
+// whole turns of the ring and a partial stage adds exact zeros.
 #include "ispa_internal.hpp"
 #include "device_common.hpp"
 
 namespace ispa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BT = 128;          // output tile
-#ifndef ISPA_GRAM_BR
-#define ISPA_GRAM_BR 32
-#endif
-constexpr int BR = ISPA_GRAM_BR;  // rows per stage
-constexpr int RB = BT * 2;       // bytes of one tile row (128 bf16)
+constexpr int kThreads = 256;                 // 4 waves, each a 64x64 quarter of the tile
+constexpr int BT = 128;                       // output tile
+constexpr int BR = 32;                        // rows per stage
+constexpr int NS = 4;                         // stages in the ring
+constexpr int RB = BT * 2;                    // bytes of one tile row (128 bf16)
+constexpr int kPart = BR * RB;                // one operand's share of a stage (8 KB)
+constexpr int kStage = 2 * kPart;             // 16 KB
+constexpr int kCopies = kStage / 1024 / 4;    // 1 KB copy instructions per wave per stage
+
+static __device__ __attribute__((aligned(16))) uint32_t g_zero_row[4];
+
+// s_waitcnt with vmcnt = n and no wait on the other counters
+#define ISPA_GRAM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
+// Workgroup barrier that waits for this wave's LDS reads but not for its copies in flight (those are
+// waited for explicitly, before the barrier that publishes them). The empty asm statements keep the
+// compiler from moving memory accesses across it.
+#define ISPA_GRAM_LDS_BARRIER()          \
+  do {                                   \
+    asm volatile("" ::: "memory");       \
+    __builtin_amdgcn_s_waitcnt(0xc07f);  \
+    __builtin_amdgcn_s_barrier();        \
+    asm volatile("" ::: "memory");       \
+  } while (0)
 
 struct GramArgs {
   const uint16_t *a_loc, *a_full;
@@ -40,45 +61,49 @@ __device__ __forceinline__ void tri_decode(int idx, int T, int &ti, int &tj) {
   tj = r + idx;
 }
 
-// Operand tiles are kept row-major in LDS ([row of the chunk][128 columns], 256 bytes per row) with
-// the 16-byte chunks of row r stored at position c ^ (4 (r mod 4)). ds_read_b64_tr_b16 then yields
-// MFMA operands directly: in each 16-lane group, source lane s addresses row k0 + s/4, columns
+// A stage holds each operand row-major ([row of the chunk][128 columns], 256 bytes per row) with the
+// 16-byte chunks of row r stored at position c ^ (4 (r mod 4)). ds_read_b64_tr_b16 then yields MFMA
+// operands directly: in each 16-lane group, source lane s addresses row k0 + s/4, columns
 // n0 + 4 (s mod 4) .. +3, and result lane i receives column n0 + i of rows k0 .. k0+3. The swizzle
 // spreads the 4 rows of one read over distinct banks.
-__device__ __forceinline__ int swz_off(int r, int col) {   // byte offset of (r, col) in a tile
+__device__ __forceinline__ int swz_off(int r, int col) {   // byte offset of (r, col) in a stage part
   const int c = col >> 3;
   return r * RB + (((c ^ (4 * (r & 3))) << 4) | ((col & 7) << 1));
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bf16x8 read_operand(const uint8_t *tile, int cb, int kb, int lane) {
+__device__ __forceinline__ bf16x8 read_operand(const uint8_t *part, int cb, int kb, int lane) {
   const int g = lane >> 4, s = lane & 15;
   const int n0 = cb + 16 * (g & 1);
   const int k0 = kb + 8 * (g >> 1);
   const int col = n0 + 4 * (s & 3);
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(tile + swz_off(k0 + (s >> 2), col)));
+      (__attribute__((address_space(3))) s16x4 *)(part + swz_off(k0 + (s >> 2), col)));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(tile + swz_off(k0 + 4 + (s >> 2), col)));
+      (__attribute__((address_space(3))) s16x4 *)(part + swz_off(k0 + 4 + (s >> 2), col)));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
 
+struct StageOps {
+  bf16x8 a[2][2], b[2][2];   // [16-row step][32-column block]
+};
+
 __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
-  // [buf][operand] tiles of BR x 128 bf16; after the main loop the same space holds the fp32 result
-  // tile (128 x 129 floats)
-  constexpr int kTileBytes = BR * RB;
-  constexpr int kLdsBytes = BT * (BT + 1) * 4 > 4 * kTileBytes ? BT * (BT + 1) * 4 : 4 * kTileBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
-  auto tile_ptr = [&](int buf, int op) { return smem + (2 * buf + op) * kTileBytes; };
+  // Four separate arrays (not one indexed ring): the compiler then tracks the copies into each stage
+  // on their own and waits only for the ones a read may touch.
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[kStage];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wm = w >> 1, wn = w & 1;
 
-  int n_tiles = g.n_upper * (g.with_f ? 2 : 1) + g.T * g.T;
+  const int n_tiles = g.n_upper * (g.with_f ? 2 : 1) + g.T * g.T;
   int idx = xcd_remap(blockIdx.x, n_tiles);
   int mat, ti, tj;   // mat: 0 = G, 1 = F, 2 = X
   if (idx < g.n_upper) {
@@ -98,47 +123,48 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
   float *out = (mat == 0) ? g.G : (mat == 1) ? g.F : g.X;
   const int i0 = ti * BT, j0 = tj * BT;
   const int d = g.d;
-  const int64_t last_row = g.n_rows - 1;
+  const int64_t n_rows = g.n_rows;
+  const int nst = (int)((n_rows + BR - 1) / BR);
 
-  // staging: thread handles 16-byte chunks e = tid + 256 q (q < NQ) of each operand tile:
-  // row r = e / 16, chunk c = e % 16. Columns past d are clamped (their outputs are not stored).
-  constexpr int NQ = BR * 16 / kThreads;
-  int srow[NQ], scol_p[NQ], scol_q[NQ], soff[NQ];
+  // Copy instruction ii of wave w fills 1 KB block blk = w + 4 ii of a stage: blocks 0-7 are the left
+  // operand, 8-15 the right one, 4 rows each. Lane l lands at byte 16 l of the block, i.e. row
+  // 4 (blk mod 8) + l / 16, stored chunk l mod 16, which holds source chunk (l mod 16) ^ (4 (l / 16)).
+  // Columns past d are clamped (their outputs are not stored).
+  const uint8_t *src[kCopies];
+  int crow[kCopies];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int e = tid + kThreads * q;
-    const int r = e >> 4, c = e & 15;
-    srow[q] = r;
-    const int cp = i0 + 8 * c, cq = j0 + 8 * c;
-    scol_p[q] = cp < d ? cp : d - 8;
-    scol_q[q] = cq < d ? cq : d - 8;
-    soff[q] = r * RB + ((c ^ (4 * (r & 3))) << 4);
+  for (int ii = 0; ii < kCopies; ++ii) {
+    const int blk = w + 4 * ii;
+    const int op = blk >> 3;
+    const int r = 4 * (blk & 7) + (lane >> 4);
+    const int c = (lane & 15) ^ (4 * (lane >> 4));
+    int col = (op ? j0 : i0) + 8 * c;
+    col = col < d ? col : d - 8;
+    crow[ii] = r;
+    src[ii] = (const uint8_t *)((op ? Q : P) + (int64_t)r * d + col);
   }
-  u32x4 ra[2 * NQ], rb[2 * NQ];   // [operand * NQ + q]
-  auto load = [&](u32x4 (&r)[2 * NQ], int64_t n0) {
+  const int64_t stage_bytes = (int64_t)BR * d * 2;
+  uint64_t zero_row = (uint64_t)(uintptr_t)g_zero_row;
+  asm volatile("" : "+s"(zero_row));   // keep the address in registers, not reloaded per stage
+
+  auto copy_stage = [&](int s, uint8_t *slot) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      int64_t n = n0 + srow[q];
-      n = n < last_row ? n : last_row;
-      r[q] = *(const u32x4 *)(P + n * d + scol_p[q]);
-      r[NQ + q] = *(const u32x4 *)(Q + n * d + scol_q[q]);
+    for (int ii = 0; ii < kCopies; ++ii) {
+      const int64_t n = (int64_t)s * BR + crow[ii];
+      const uint8_t *p = src[ii] + (int64_t)s * stage_bytes;
+      p = n < n_rows ? p : (const uint8_t *)(uintptr_t)zero_row;
+      __builtin_amdgcn_global_load_lds((const void *)p,
+                                       (__attribute__((address_space(3))) void *)(slot + 1024 * (w + 4 * ii)),
+                                       16, 0, 0);
     }
   };
-  auto store = [&](const u32x4 (&r)[2 * NQ], int buf, int64_t n0) {
-    if (n0 + BR - 1 <= last_row) {
+  auto read_stage = [&](const uint8_t *slot, StageOps &o) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        *(u32x4 *)(tile_ptr(buf, 0) + soff[q]) = r[q];
-        *(u32x4 *)(tile_ptr(buf, 1) + soff[q]) = r[NQ + q];
-      }
-    } else {   // tail stage: rows past the chunk end contribute zeros
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const bool ok = n0 + srow[q] <= last_row;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *(u32x4 *)(tile_ptr(buf, 0) + soff[q]) = ok ? r[q] : z;
-        *(u32x4 *)(tile_ptr(buf, 1) + soff[q]) = ok ? r[NQ + q] : z;
-      }
+      for (int bi = 0; bi < 2; ++bi) o.a[t][bi] = read_operand(slot, wm * 64 + bi * 32, 16 * t, lane);
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj) o.b[t][bj] = read_operand(slot + kPart, wn * 64 + bj * 32, 16 * t, lane);
     }
   };
 
@@ -150,105 +176,94 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
 
-  auto compute = [&](int buf) {
-    const uint8_t *As = tile_ptr(buf, 0);
-    const uint8_t *Bs = tile_ptr(buf, 1);
+  // Stage s: its operands are already in registers (`ocur`); stage s+1 is read into `onx` while
+  // stage s is multiplied, and the slot of stage s is refilled with stage s+4.
+  auto stage = [&](int s, uint8_t *cur, const uint8_t *nxt, const StageOps &ocur, StageOps &onx) {
+    ISPA_GRAM_WAIT_VMCNT(kCopies * (NS - 2));   // this wave's copies of stage s+1 have landed
+    ISPA_GRAM_LDS_BARRIER();                    // ... everyone's; all reads of stage s are done
+    copy_stage(s + NS, cur);
+    read_stage(nxt, onx);
 #pragma unroll
-    for (int t = 0; t < BR / 16; ++t) {
-      bf16x8 av[2], bv[2];
-#pragma unroll
-      for (int bi = 0; bi < 2; ++bi) av[bi] = read_operand(As, wm * 64 + bi * 32, 16 * t, lane);
-#pragma unroll
-      for (int bj = 0; bj < 2; ++bj) bv[bj] = read_operand(Bs, wn * 64 + bj * 32, 16 * t, lane);
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma_bf16_32x32x16(av[bi], bv[bj], acc[bi][bj]);
+        for (int bj = 0; bj < 2; ++bj)
+          acc[bi][bj] = mfma_bf16_32x32x16(ocur.a[t][bi], ocur.b[t][bj], acc[bi][bj]);
+    // issue order: one MFMA, the copies, then the LDS reads two at a time between the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, kCopies, 0);
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   };
 
-  // Two stages of global loads stay in flight: while stage s is multiplied out of LDS, stage s+1
-  // sits in one register set and stage s+2 is being fetched into the other. Loads are issued
-  // unconditionally (clamped rows), so no branch separates them from their use.
-  const int nst = (int)((g.n_rows + BR - 1) / BR);
-  load(ra, 0);
-  load(rb, BR);
-  store(ra, 0, 0);
-  __syncthreads();
-  int st = 0;
-  for (; st + 1 < nst; st += 2) {
-    load(ra, (int64_t)(st + 2) * BR);
-    compute(0);
-    store(rb, 1, (int64_t)(st + 1) * BR);
-    __syncthreads();
-    load(rb, (int64_t)(st + 3) * BR);
-    compute(1);
-    if (st + 2 < nst) store(ra, 0, (int64_t)(st + 2) * BR);
-    __syncthreads();
+  StageOps oa, ob;
+  copy_stage(0, ring0);
+  copy_stage(1, ring1);
+  copy_stage(2, ring2);
+  copy_stage(3, ring3);
+  ISPA_GRAM_WAIT_VMCNT(kCopies * (NS - 1));
+  ISPA_GRAM_LDS_BARRIER();
+  read_stage(ring0, oa);
+  for (int s = 0; s < nst; s += NS) {
+    stage(s, ring0, ring1, oa, ob);
+    stage(s + 1, ring1, ring2, ob, oa);
+    stage(s + 2, ring2, ring3, oa, ob);
+    stage(s + 3, ring3, ring0, ob, oa);
   }
-  if (st < nst) compute(0);
-  __syncthreads();
+  ISPA_GRAM_WAIT_VMCNT(0);   // no copy may land in LDS after the workgroup has ended
 
-  // Stage the 128x128 result in LDS (reusing the operand buffers), then add it to the running sums
-  // with coalesced 16-byte read-modify-writes: the tile itself, and for off-diagonal symmetric tiles
-  // its mirror. Each thread issues all of its loads before any add, so the round trips overlap.
-  float *cs = (float *)smem;
-  constexpr int CST = BT + 1;   // odd stride: both row-wise and column-wise reads spread over banks
+  // Add the tile to the running sums straight from the accumulators: lane (l32, hf) of block
+  // (bi, bj) holds rows 8 q + 4 hf + e (q, e < 4) of column l32. Each thread issues its loads before
+  // any add, so the round trips overlap.
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < 2; ++bj) {
+      const int cl = j0 + wn * 64 + bj * 32 + l32;
+      const int clc = cl < d ? cl : d - 1;
+      float cur[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int rr = wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-        const int cc = wn * 64 + bj * 32 + l32;
-        cs[rr * CST + cc] = acc[bi][bj][v];
+        const int rw = i0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        const int rwc = rw < d ? rw : d - 1;
+        cur[v] = out[(int64_t)rwc * d + clc];
       }
-  __syncthreads();
-  // thread -> (row rr = e / 32, 4-column group c4 = e % 32) for e = tid + 256 k, k < 16
-  constexpr int NV = BT * BT / 4 / kThreads;   // 16 float4 per thread
-  const int c4 = tid & 31;
-  const int rbase = tid >> 5;                  // 0..7; rows rbase + 8k
-  {
-    f32x4 cur[NV];
-    const int gc = j0 + 4 * c4;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int gr = i0 + rbase + 8 * k;
-      const int grc = gr < d ? gr : d - 1;
-      const int gcc = gc < d ? gc : d - 4;
-      cur[k] = *(const f32x4 *)&out[(int64_t)grc * d + gcc];
+      for (int v = 0; v < 16; ++v) {
+        const int rw = i0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        if (rw < d && cl < d) out[(int64_t)rw * d + cl] = cur[v] + acc[bi][bj][v];
+      }
     }
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int rr = rbase + 8 * k;
-      const int gr = i0 + rr;
-      f32x4 add;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) add[q] = cs[rr * CST + 4 * c4 + q];
-      if (gr < d && gc < d) *(f32x4 *)&out[(int64_t)gr * d + gc] = cur[k] + add;
-    }
-  }
   if (mat != 2 && ti != tj) {
-    // mirror: out[j0 + rr][i0 + cc] += tile[cc][rr]
-    f32x4 cur[NV];
-    const int gc = i0 + 4 * c4;
+    // mirror of an off-diagonal G or F tile: out[c][r] += tile[r][c]; the four rows e of one q are
+    // four consecutive columns of the mirror, written as one 16-byte access
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int gr = j0 + rbase + 8 * k;
-      const int grc = gr < d ? gr : d - 1;
-      const int gcc = gc < d ? gc : d - 4;
-      cur[k] = *(const f32x4 *)&out[(int64_t)grc * d + gcc];
-    }
+    for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int rr = rbase + 8 * k;
-      const int gr = j0 + rr;
-      f32x4 add;
+      for (int bj = 0; bj < 2; ++bj) {
+        const int mr = j0 + wn * 64 + bj * 32 + l32;
+        const int mrc = mr < d ? mr : d - 1;
+        f32x4 cur[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) add[q] = cs[(4 * c4 + q) * CST + rr];
-      if (gr < d && gc < d) *(f32x4 *)&out[(int64_t)gr * d + gc] = cur[k] + add;
-    }
+        for (int q = 0; q < 4; ++q) {
+          const int mc = i0 + wm * 64 + bi * 32 + 8 * q + 4 * hf;
+          const int mcc = mc < d ? mc : d - 4;
+          cur[q] = *(const f32x4 *)&out[(int64_t)mrc * d + mcc];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int mc = i0 + wm * 64 + bi * 32 + 8 * q + 4 * hf;
+          f32x4 add;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) add[e] = acc[bi][bj][4 * q + e];
+          if (mr < d && mc < d) *(f32x4 *)&out[(int64_t)mr * d + mc] = cur[q] + add;
+        }
+      }
   }
 }
 
@@ -268,7 +283,7 @@ hipError_t launch_gram_bf16(int64_t n_rows, int d, const uint16_t *a_loc, const 
   g.n_upper = g.T * (g.T + 1) / 2;
   g.with_f = F != nullptr;
   const int n_tiles = g.n_upper * (g.with_f ? 2 : 1) + g.T * g.T;
-  if (n_rows == 0 || n_tiles == 0) return hipSuccess;
+  if (n_rows == 0 || n_tiles == 0 || d < 8) return hipSuccess;
   hipLaunchKernelGGL(gram_bf16_kernel, dim3(n_tiles), dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
