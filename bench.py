@@ -41,7 +41,10 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (HBM counter calibration)")
     ap.add_argument("--attn-only-cfg", type=int, default=None,
-                    help="time only ispa_attn_dual on workload 2, 4 (chunk 4) or 5 and print its rate")
+                    help="time only ispa_attn_dual on workload 2, 4 (chunk 4) or 5 (dual, local-only and "
+                         "single-pass forms, warm and cold cache) and print one JSON line")
+    ap.add_argument("--gram-only-cfg", type=int, default=None,
+                    help="time only the statistics update of one chunk at workload 3's or 4's width")
     return ap.parse_args()
 
 
@@ -143,42 +146,106 @@ def cpu_baseline(wl):
     }
 
 
-def attn_only(cfg, steps, warmup, torch):
+def _time_calls(call, n, warmup, torch, cold_scratch=None):
+    """Median per-call time in ms from HIP events on the current stream. With `cold_scratch`, a
+    512 MiB write runs before every call so that the inputs are no longer in the caches."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for i in range(n):
+        if cold_scratch is not None:
+            cold_scratch.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
+
+
+def attn_report(cfg, steps, warmup, torch):
+    """Attention on one workload in three forms, warm and cold cache:
+    dual   = the dual-stream call (A_loc, A_full, three LSE rows);
+    local  = local-only call (sink + current keys, A_loc and lse_loc only);
+    single = one local-only call over all keys (sink and history joined into one segment), i.e.
+             single-pass full attention with no merge and one output; dual / single - 1 is the
+             overhead of the dual stream."""
     import ispa_inputs as inputs
     import kv_cache_attention_split_amd as ispa
     wl = inputs.CONFIGS[cfg]
     chunk = 3 if cfg in (3, 4) else 0
     inp = inputs.attention_inputs(cfg, 0, chunk)
     dev = {k: bf16_dev(inp[k], torch) for k in ("q", "sink_k", "sink_v", "cur_k", "cur_v", "hist_k", "hist_v")}
+    joined_k = torch.cat([dev["sink_k"], dev["hist_k"]], dim=0)
+    joined_v = torch.cat([dev["sink_v"], dev["hist_v"]], dim=0)
+    empty = dev["hist_k"][:0]
     n_q = inp["q"].shape[0]
     H, dh = wl.n_heads, wl.head_dim
     a_loc = torch.empty((n_q, H * dh), dtype=torch.bfloat16, device="cuda")
     a_full = torch.empty_like(a_loc)
     lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
-    n_keys = sum(inp[k].shape[0] for k in ("sink_k", "cur_k", "hist_k"))
+    n_sc = inp["sink_k"].shape[0] + inp["cur_k"].shape[0]
+    n_all = n_sc + inp["hist_k"].shape[0]
+    scratch = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+    calls = {
+        "dual": (n_all, lambda: ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"],
+                                                    dev["hist_k"], dev["hist_v"], wl.scale, a_loc, a_full,
+                                                    lse[0], lse[1], lse[2])),
+        "local": (n_sc, lambda: ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"],
+                                                    empty, empty, wl.scale, a_loc, None, lse[0])),
+        "single": (n_all, lambda: ispa.ispa_attn_dual(dev["q"], joined_k, joined_v, dev["cur_k"], dev["cur_v"],
+                                                      empty, empty, wl.scale, a_loc, None, lse[0])),
+    }
+    # clocks ramp up over the first tenths of a second of load: run every form for about half a
+    # second before timing, then time the forms in interleaved rounds and keep the median round
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:
+        for _, call in calls.values():
+            call()
+        torch.cuda.synchronize()
+    rounds = {mode: ([], []) for mode in calls}
+    for _ in range(3):
+        for mode, (nk, call) in calls.items():
+            rounds[mode][0].append(_time_calls(call, steps, warmup, torch))
+            rounds[mode][1].append(_time_calls(call, steps, warmup, torch, cold_scratch=scratch))
     res = {}
-    for mode in ("dual", "local"):
-        full = mode == "dual"
-
-        def call():
-            ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"],
-                                dev["hist_k"], dev["hist_v"], wl.scale, a_loc, a_full if full else None,
-                                lse[0], lse[1] if full else None, lse[2] if full else None)
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            call()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        nk = n_keys if full else inp["sink_k"].shape[0] + inp["cur_k"].shape[0]
+    for mode, (nk, call) in calls.items():
         fl = attn_flops(n_q, nk, H, dh)
-        res[mode] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
-                     "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
-    print(json.dumps({"workload": wl.name, "attention": res}), flush=True)
+        warm = float(np.median(rounds[mode][0]))
+        cold = float(np.median(rounds[mode][1]))
+        res[mode] = {"keys": nk, "warm_ms": round(warm, 4), "cold_ms": round(cold, 4),
+                     "tflops_warm": round(fl / warm / 1e9, 1), "frac_warm": round(fl / warm / 1e9 / PEAK_BF16_TFLOPS, 4),
+                     "tflops_cold": round(fl / cold / 1e9, 1)}
+    out = {"workload": wl.name, "n_q": n_q, "heads": H, "head_dim": dh, "attention": res,
+           "dual_overhead_vs_single_pass": round(res["dual"]["warm_ms"] / res["single"]["warm_ms"] - 1.0, 4),
+           "full_over_local_time": round(res["dual"]["warm_ms"] / res["local"]["warm_ms"], 3)}
+    print(json.dumps(out), flush=True)
+
+
+def gram_report(cfg, steps, warmup, torch):
+    """Statistics update of one 4680-row chunk at a workload's width d: warm median time and rate
+    (4 N d^2 FLOP: G and F as half products, X in full)."""
+    import ispa_inputs as inputs
+    import kv_cache_attention_split_amd as ispa
+    wl = inputs.CONFIGS[cfg]
+    d, n = wl.d, inputs.CHUNK_TOKENS
+    g = torch.Generator(device="cuda").manual_seed(1234 + cfg)
+    a_loc = (0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16)
+    a_full = (0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16)
+    st = [torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)]
+    call = lambda: ispa.ispa_absorb_accumulate(a_loc, a_full, st[0], st[1], st[2])   # noqa: E731
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:
+        call()
+        torch.cuda.synchronize()
+    ms = float(np.median([_time_calls(call, steps, warmup, torch) for _ in range(3)]))
+    fl = 4.0 * n * d * d
+    print(json.dumps({"workload": wl.name, "statistics": {"rows": n, "d": d, "ms": round(ms, 4),
+                                                          "tflops": round(fl / ms / 1e9, 1),
+                                                          "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}}),
+          flush=True)
 
 
 def main():
@@ -192,7 +259,10 @@ def main():
     import kv_cache_attention_split_amd as ispa
 
     if args.attn_only_cfg is not None:
-        attn_only(args.attn_only_cfg, args.steps, args.warmup, torch)
+        attn_report(args.attn_only_cfg, max(args.steps, 20), max(args.warmup, 5), torch)
+        return
+    if args.gram_only_cfg is not None:
+        gram_report(args.gram_only_cfg, max(args.steps, 20), max(args.warmup, 5), torch)
         return
 
     if args.calibrate_copy:

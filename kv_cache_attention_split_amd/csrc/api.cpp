@@ -314,9 +314,25 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
       }
     }
 
-    // forward substitution: L Y = B, block rows top to bottom
+    // forward substitution L Y = B, left-looking by block rows (top to bottom):
+    //   Y_k = Linv_k (B_k - L[k, :k] Y[:k]); each update is one wide GEMM with K = k0, so B is
+    //   read and written once per block row instead of once per earlier block
     for (int k = 0; k < nt; ++k) {
       const int k0 = k * nb;
+      if (k0 > 0) {
+        GemmBatch b{};
+        GemmShape sh{};
+        sh.M = nb; sh.N = d; sh.K = k0;
+        sh.lda = d; sh.ldb = d; sh.ldc = d;
+        sh.ta = 0; sh.tb = 0;
+        sh.alpha = -1.f; sh.beta = 1.f;
+        for (int i = 0; i < cnt; ++i) {
+          b.A[i] = Lp(i) + (int64_t)k0 * d;     // L[k0 + r][kk], kk < k0
+          b.B[i] = Bp(i);                       // Y[kk][c], kk < k0
+          b.C[i] = Bp(i) + (int64_t)k0 * d;
+        }
+        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      }
       {
         GemmBatch b{};
         GemmShape sh{};
@@ -328,29 +344,29 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
           b.A[i] = Vp(i) + k * linv_blk;
           b.B[i] = Bp(i) + (int64_t)k0 * d;
           b.C[i] = Bp(i) + (int64_t)k0 * d;
-        }
-        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
-      }
-      const int rem = d - k0 - nb;
-      if (rem <= 0) continue;
-      {
-        GemmBatch b{};
-        GemmShape sh{};
-        sh.M = rem; sh.N = d; sh.K = nb;
-        sh.lda = d; sh.ldb = d; sh.ldc = d;
-        sh.ta = 0; sh.tb = 0;
-        sh.alpha = -1.f; sh.beta = 1.f;
-        for (int i = 0; i < cnt; ++i) {
-          b.A[i] = Lp(i) + (int64_t)(k0 + nb) * d + k0;
-          b.B[i] = Bp(i) + (int64_t)k0 * d;
-          b.C[i] = Bp(i) + (int64_t)(k0 + nb) * d;
         }
         ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
       }
     }
-    // back substitution: L^T dW = Y, block rows bottom to top
+    // back substitution L^T dW = Y, left-looking by block rows (bottom to top):
+    //   X_k = Linv_k^T (Y_k - L[k+1:, k]^T X[k+1:])
     for (int k = nt - 1; k >= 0; --k) {
       const int k0 = k * nb;
+      const int rem = d - k0 - nb;
+      if (rem > 0) {
+        GemmBatch b{};
+        GemmShape sh{};
+        sh.M = nb; sh.N = d; sh.K = rem;
+        sh.lda = d; sh.ldb = d; sh.ldc = d;
+        sh.ta = 1; sh.tb = 0;
+        sh.alpha = -1.f; sh.beta = 1.f;
+        for (int i = 0; i < cnt; ++i) {
+          b.A[i] = Lp(i) + (int64_t)(k0 + nb) * d + k0;   // opA[r][kk] = L[k0 + nb + kk][k0 + r]
+          b.B[i] = Bp(i) + (int64_t)(k0 + nb) * d;        // X[k0 + nb + kk][c]
+          b.C[i] = Bp(i) + (int64_t)k0 * d;
+        }
+        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      }
       {
         GemmBatch b{};
         GemmShape sh{};
@@ -362,21 +378,6 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
           b.A[i] = Vp(i) + k * linv_blk;
           b.B[i] = Bp(i) + (int64_t)k0 * d;
           b.C[i] = Bp(i) + (int64_t)k0 * d;
-        }
-        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
-      }
-      if (k0 == 0) continue;
-      {
-        GemmBatch b{};
-        GemmShape sh{};
-        sh.M = k0; sh.N = d; sh.K = nb;
-        sh.lda = d; sh.ldb = d; sh.ldc = d;
-        sh.ta = 1; sh.tb = 0;
-        sh.alpha = -1.f; sh.beta = 1.f;
-        for (int i = 0; i < cnt; ++i) {
-          b.A[i] = Lp(i) + (int64_t)k0 * d;     // opA[r][kk] = L[k0 + kk][r], r < k0
-          b.B[i] = Bp(i) + (int64_t)k0 * d;
-          b.C[i] = Bp(i);
         }
         ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
       }

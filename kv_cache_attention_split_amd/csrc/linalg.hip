@@ -219,28 +219,54 @@ __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int6
 #pragma unroll
     for (int k = 0; k < R; ++k) a[i][k] = L[(int64_t)(k0 + r0 + i) * d + k0 + c0 + k];
 
+  // R consecutive floats of LDS (R-aligned) as vector reads
+  auto lds_row = [&](const float *p, float (&v)[R]) {
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q) {
+      const f32x4 x = ((const f32x4 *)p)[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+    }
+  };
+  auto lds_store_row = [&](float *p, const float (&v)[R]) {
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = v[4 * q + e];
+      ((f32x4 *)p)[q] = x;
+    }
+  };
+
   // factorisation: at step j the owners of column j publish it; every thread then applies
   // A[r][c] -= A[r][j] A[c][j] / A[j][j] to its lower-triangle elements with r, c > j.
+  // All reads and the selects below are unconditional: no per-element branches or waits.
   for (int j = 0; j < NB; ++j) {
     if (tx == j / R) {
+      const int kk = j - c0;
+      float col[R];
 #pragma unroll
-      for (int k = 0; k < R; ++k)
-        if (c0 + k == j) {
+      for (int i = 0; i < R; ++i) {
+        float v = a[i][0];
 #pragma unroll
-          for (int i = 0; i < R; ++i) colst[j * NB + r0 + i] = a[i][k];
-        }
+        for (int k = 1; k < R; ++k) v = (k == kk) ? a[i][k] : v;
+        col[i] = v;
+      }
+      lds_store_row(&colst[j * NB + r0], col);
     }
     __syncthreads();
-    float piv = colst[j * NB + j];
-    if (!(piv > 0.f)) piv = 1.f;   // recorded below; keeps the rest finite
-    const float ip = 1.f / piv;
     // entries of rows / columns <= j are zeroed, so the rank-1 update of the whole sub-block
     // leaves them unchanged; the upper triangle is updated too (harmless, only the lower is read)
     float cr[R], cc[R];
+    lds_row(&colst[j * NB + r0], cr);
+    lds_row(&colst[j * NB + c0], cc);
+    float piv = colst[j * NB + j];
+    if (!(piv > 0.f)) piv = 1.f;   // recorded below; keeps the rest finite
+    const float ip = 1.f / piv;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      cr[i] = (r0 + i > j) ? colst[j * NB + r0 + i] * ip : 0.f;
-      cc[i] = (c0 + i > j) ? colst[j * NB + c0 + i] : 0.f;
+      cr[i] = (r0 + i > j) ? cr[i] * ip : 0.f;
+      cc[i] = (c0 + i > j) ? cc[i] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < R; ++i)
@@ -263,24 +289,27 @@ __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int6
     for (int k = 0; k < R; ++k) y[i][k] = (r0 + i == c0 + k) ? 1.f : 0.f;
   for (int j = 0; j < NB - 1; ++j) {
     if (ty == j / R) {
+      const int ii = j - r0;
+      float row[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i)
-        if (r0 + i == j) {
+      for (int k = 0; k < R; ++k) {
+        float v = y[0][k];
 #pragma unroll
-          for (int k = 0; k < R; ++k) rowst[j * NB + c0 + k] = y[i][k];
-        }
+        for (int i = 1; i < R; ++i) v = (i == ii) ? y[i][k] : v;
+        row[k] = v;
+      }
+      lds_store_row(&rowst[j * NB + c0], row);
     }
     __syncthreads();
+    // row j of Y is zero beyond column j (Y is lower triangular); rows <= j get u = 0
+    float u[R], yr[R];
+    lds_row(&colst[j * NB + r0], u);
+    lds_row(&rowst[j * NB + c0], yr);
     float piv = colst[j * NB + j];
     if (!(piv > 0.f)) piv = 1.f;
     const float ip = 1.f / piv;
-    // row j of Y is zero beyond column j (Y is lower triangular); rows <= j get u = 0
-    float u[R], yr[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      u[i] = (r0 + i > j) ? colst[j * NB + r0 + i] * ip : 0.f;
-      yr[i] = rowst[j * NB + c0 + i];
-    }
+    for (int i = 0; i < R; ++i) u[i] = (r0 + i > j) ? u[i] * ip : 0.f;
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
