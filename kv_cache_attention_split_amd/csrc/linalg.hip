@@ -238,25 +238,24 @@ __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int6
     }
   };
 
-  // factorisation: at step j the owners of column j publish it; every thread then applies
-  // A[r][c] -= A[r][j] A[c][j] / A[j][j] to its lower-triangle elements with r, c > j.
-  // All reads and the selects below are unconditional: no per-element branches or waits.
-  for (int j = 0; j < NB; ++j) {
-    if (tx == j / R) {
-      const int kk = j - c0;
-      float col[R];
+  // factorisation: at step j every thread applies A[r][c] -= A[r][j] A[c][j] / A[j][j] to its
+  // sub-block (entries of rows / columns <= j get a zero factor, so they stay unchanged; the upper
+  // triangle is updated too, harmlessly, since only the lower is read). Look-ahead: the owners of
+  // column j+1 update that column first and publish it to LDS before the rest of the update, so
+  // that the LDS write is in flight while the other FMAs run and one barrier per step suffices
+  // (each column has its own LDS row). The step loop is unrolled by R so that column j is the
+  // fixed register j mod R of its owners.
+  if (tx == 0) {
+    float col[R];
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        float v = a[i][0];
+    for (int i = 0; i < R; ++i) col[i] = a[i][0];
+    lds_store_row(&colst[r0], col);
+  }
+  for (int jb = 0; jb < NB; jb += R)
 #pragma unroll
-        for (int k = 1; k < R; ++k) v = (k == kk) ? a[i][k] : v;
-        col[i] = v;
-      }
-      lds_store_row(&colst[j * NB + r0], col);
-    }
-    __syncthreads();
-    // entries of rows / columns <= j are zeroed, so the rank-1 update of the whole sub-block
-    // leaves them unchanged; the upper triangle is updated too (harmless, only the lower is read)
+  for (int kk = 0; kk < R; ++kk) {
+    const int j = jb + kk;
+    __syncthreads();   // column j is in LDS
     float cr[R], cc[R];
     lds_row(&colst[j * NB + r0], cr);
     lds_row(&colst[j * NB + c0], cc);
@@ -268,11 +267,24 @@ __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int6
       cr[i] = (r0 + i > j) ? cr[i] * ip : 0.f;
       cc[i] = (c0 + i > j) ? cc[i] : 0.f;
     }
+    const int kn = (kk + 1) % R;                          // register of column j+1 (constant once unrolled)
+    const bool own_next = (tx == (j + 1) / R) && (j + 1 < NB);
+    if (own_next) {
+      float col[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        a[i][kn] = fmaf(-cr[i], cc[kn], a[i][kn]);
+        col[i] = a[i][kn];
+      }
+      lds_store_row(&colst[(j + 1) * NB + r0], col);
+    }
+    cc[kn] = own_next ? 0.f : cc[kn];                    // that column is done
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int k = 0; k < R; ++k) a[i][k] = fmaf(-cr[i], cc[k], a[i][k]);
   }
+  __syncthreads();
   if (tid == 0) {
     for (int j = 0; j < NB; ++j)
       if (!(colst[j * NB + j] > 0.f)) {
@@ -281,26 +293,25 @@ __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int6
       }
   }
   // inverse of the unit-lower factor U[r][j] = colst[j][r] / piv_j by a forward sweep:
-  // Y = I; for each j, rows i > j: Y[i][c] -= U[i][j] Y[j][c].
+  // Y = I; for each j, rows i > j: Y[i][c] -= U[i][j] Y[j][c]. Same look-ahead: the owners of
+  // row j+1 of Y update and publish it first.
   float y[R][R];
 #pragma unroll
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int k = 0; k < R; ++k) y[i][k] = (r0 + i == c0 + k) ? 1.f : 0.f;
-  for (int j = 0; j < NB - 1; ++j) {
-    if (ty == j / R) {
-      const int ii = j - r0;
-      float row[R];
+  if (ty == 0) {
+    float row[R];
 #pragma unroll
-      for (int k = 0; k < R; ++k) {
-        float v = y[0][k];
+    for (int k = 0; k < R; ++k) row[k] = y[0][k];
+    lds_store_row(&rowst[c0], row);
+  }
+  for (int jb = 0; jb < NB; jb += R)
 #pragma unroll
-        for (int i = 1; i < R; ++i) v = (i == ii) ? y[i][k] : v;
-        row[k] = v;
-      }
-      lds_store_row(&rowst[j * NB + c0], row);
-    }
-    __syncthreads();
+  for (int ii = 0; ii < R; ++ii) {
+    const int j = jb + ii;
+    if (j == NB - 1) break;     // uniform: the last row has nothing below it
+    __syncthreads();            // row j of Y is in LDS
     // row j of Y is zero beyond column j (Y is lower triangular); rows <= j get u = 0
     float u[R], yr[R];
     lds_row(&colst[j * NB + r0], u);
@@ -310,6 +321,18 @@ __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int6
     const float ip = 1.f / piv;
 #pragma unroll
     for (int i = 0; i < R; ++i) u[i] = (r0 + i > j) ? u[i] * ip : 0.f;
+    const int in = (ii + 1) % R;                          // register row of row j+1 (constant once unrolled)
+    const bool own_next = (ty == (j + 1) / R) && (j + 1 < NB - 1);
+    if (own_next) {
+      float row[R];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        y[in][k] = fmaf(-u[in], yr[k], y[in][k]);
+        row[k] = y[in][k];
+      }
+      lds_store_row(&rowst[(j + 1) * NB + c0], row);
+    }
+    u[in] = own_next ? 0.f : u[in];                      // that row is done
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
