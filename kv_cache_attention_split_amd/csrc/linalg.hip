@@ -17,22 +17,28 @@ namespace ispa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int GT = 128;        // GEMM output tile
-constexpr int GK = 16;         // GEMM k per stage
-constexpr int GST = GK + 4;    // LDS row stride (floats): 16 rows x 16 B reads hit all 64 banks once
+constexpr int GT = 128;        // GEMM output tile of the wide launches (and of the dot partials)
 
+// GEMM tile GTT x GTT, k step GK per stage; 4 waves, each a (GTT/2)^2 quarter. GTT = 128 with
+// GK = 16 for wide launches; GTT = 64 with GK = 32 when a launch has too few 128-tiles to fill the
+// chip (4x the workgroups, same staging shape).
+template <int GTT, int GK>
 __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmShape sh) {
-  __shared__ __attribute__((aligned(16))) float lds[2][2][GT * GST];   // [buf][A/B][row][k]
+  constexpr int GST = GK + 4;    // LDS row stride (floats): rows of 16-byte reads spread over the banks
+  constexpr int WT = GTT / 2;    // wave tile
+  constexpr int NBK = WT / 32;   // 32x32 blocks per wave dimension
+  constexpr int KPL = GK / 2;    // k values per lane per stage
+  __shared__ __attribute__((aligned(16))) float lds[2][2][GTT * GST];   // [buf][A/B][row][k]
   const int p = blockIdx.y;
-  const int tn = (sh.N + GT - 1) / GT;
+  const int tn = (sh.N + GTT - 1) / GTT;
   const int tile = blockIdx.x;
   const int ti = tile / tn, tj = tile % tn;
-  const int m0 = ti * GT, n0 = tj * GT;
+  const int m0 = ti * GTT, n0 = tj * GTT;
   if (sh.dot && sh.sym && tj > ti) {
     if (threadIdx.x == 0) ((double *)bt.C[blockIdx.y])[tile] = 0.0;
     return;
   }
-  if (sh.lower && n0 > m0 + GT - 1) return;
+  if (sh.lower && n0 > m0 + GTT - 1) return;
   const float *A = bt.A[p];
   const float *A2 = bt.A2[p];
   const float *B = bt.B[p];
@@ -48,7 +54,7 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
   // 16 k, so a 16-lane group writes 256 distinct bytes.
   const int sop = tid >> 7;                 // 0: A, 1: B
   const int st_t = tid & 127;
-  const int kblk = st_t & 3, rblk = st_t >> 2;
+  const int kblk = st_t % (GK / 4), rblk = st_t / (GK / 4);   // GTT/4 x GK/4 blocks = 128
   const bool s_trans = sop == 0 ? (sh.ta != 0) : (sh.tb == 0);
   const float *s_src = sop == 0 ? A : B;
   const float *s_src2 = sop == 0 ? A2 : nullptr;
@@ -93,11 +99,11 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[NBK][NBK];
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < NBK; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < NBK; ++bj)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
 
@@ -112,28 +118,28 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
     if (st + 1 < nst) load((st + 1) * GK);
     const float *As = lds[buf][0];
     const float *Bs = lds[buf][1];
-    // k slot mapping inside a stage: MFMA s, wave half hf -> k = 8 hf + s
-    f32x4 av[2][2], bv[2][2];
+    // k slot mapping inside a stage: MFMA s, wave half hf -> k = KPL hf + s
+    f32x4 av[NBK][KPL / 4], bv[NBK][KPL / 4];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      const float *r = &As[(wm * 64 + bi * 32 + l32) * GST + 8 * hf];
-      av[bi][0] = *(const f32x4 *)r;
-      av[bi][1] = *(const f32x4 *)(r + 4);
+    for (int bi = 0; bi < NBK; ++bi) {
+      const float *r = &As[(wm * WT + bi * 32 + l32) * GST + KPL * hf];
+#pragma unroll
+      for (int q = 0; q < KPL / 4; ++q) av[bi][q] = *(const f32x4 *)(r + 4 * q);
     }
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj) {
-      const float *r = &Bs[(wn * 64 + bj * 32 + l32) * GST + 8 * hf];
-      bv[bj][0] = *(const f32x4 *)r;
-      bv[bj][1] = *(const f32x4 *)(r + 4);
+    for (int bj = 0; bj < NBK; ++bj) {
+      const float *r = &Bs[(wn * WT + bj * 32 + l32) * GST + KPL * hf];
+#pragma unroll
+      for (int q = 0; q < KPL / 4; ++q) bv[bj][q] = *(const f32x4 *)(r + 4 * q);
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < KPL; ++s) {
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi) {
+      for (int bi = 0; bi < NBK; ++bi) {
         const f32x4 &a4 = av[bi][s >> 2];
         const float a = a4[s & 3];
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj) {
+        for (int bj = 0; bj < NBK; ++bj) {
           const f32x4 &b4 = bv[bj][s >> 2];
           const float b = b4[s & 3];
           acc[bi][bj] = mfma_f32_32x32x2(a, b, acc[bi][bj]);
@@ -147,13 +153,13 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
   if (!sh.dot) {
     float *C = bt.C[p];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < NBK; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj)
+      for (int bj = 0; bj < NBK; ++bj)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-          const int col = n0 + wn * 64 + bj * 32 + l32;
+          const int row = m0 + wm * WT + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+          const int col = n0 + wn * WT + bj * 32 + l32;
           if (row < sh.M && col < sh.N) {
             float *c = C + (int64_t)row * sh.ldc + col;
             float val = sh.alpha * acc[bi][bj][v];
@@ -167,13 +173,13 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
   const float *E = bt.E[p];
   double s = 0.0;
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < NBK; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < NBK; ++bj)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-        const int col = n0 + wn * 64 + bj * 32 + l32;
+        const int row = m0 + wm * WT + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        const int col = n0 + wn * WT + bj * 32 + l32;
         if (row < sh.M && col < sh.N)
           s += (double)E[(int64_t)row * sh.lde + col] * (double)(sh.alpha * acc[bi][bj][v]);
       }
@@ -450,8 +456,16 @@ hipError_t launch_gemm_f32(const GemmBatch &b, int count, const GemmShape &sh, d
   if (sh.dot) {
     for (int p = 0; p < count; ++p) bb.C[p] = (float *)(part + (int64_t)p * part_stride);
   }
-  dim3 grid(gemm_tiles(sh.M, sh.N), count);
-  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(kThreads), 0, s, bb, sh);
+  // fewer than two 128-tiles per CU: 64-tiles (dot launches keep 128-tiles: their partial
+  // count is gemm_tiles)
+  const int t128 = gemm_tiles(sh.M, sh.N);
+  if (!sh.dot && (int64_t)t128 * count < 512) {
+    dim3 grid(((sh.M + 63) / 64) * ((sh.N + 63) / 64), count);
+    hipLaunchKernelGGL((gemm_f32_kernel<64, 32>), grid, dim3(kThreads), 0, s, bb, sh);
+  } else {
+    dim3 grid(t128, count);
+    hipLaunchKernelGGL((gemm_f32_kernel<128, 16>), grid, dim3(kThreads), 0, s, bb, sh);
+  }
   return hipGetLastError();
 }
 
