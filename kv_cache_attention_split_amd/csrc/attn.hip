@@ -436,8 +436,10 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
 // 4-7 (group B) run the same loop, B one barrier behind A; every iteration has a matrix phase
 // (scores of tile i, value product of tile i-1) and a vector phase (softmax of tile i), separated by
 // workgroup barriers, so on each SIMD one wave's MFMAs run while the other wave's softmax runs.
-// Both groups read the same K/V tiles one phase apart; group A issues the global->LDS copies two
-// phases before the tiles are needed.
+// Both groups read the same K/V tiles one phase apart; group A issues the global->LDS copies at the
+// end of its matrix phase, after that phase's LDS reads: the compiler turns every LDS-read wait into
+// a full wait while a global->LDS copy is in flight, which would serialise the operand reads. With
+// no copy in flight the reads run four operands ahead of the MFMAs (scheduling groups below).
 // ------------------------------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, int n_qt) {
@@ -551,32 +553,52 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
 
   for (int i = 0; i <= nt; ++i) {
     // ---- matrix phase: scores of tile i, value product of tile i-1 ----
-    if (grp == 0) {
-      if (i + 1 < nt) dma_k(i + 1, (i + 1) & 1);
-      if (i < nt) dma_v(i, i & 1);
-    }
     if (i < nt) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) sc[b][v] = 0.f;
-      bf16x8 kcur = kread(i & 1, 0);
+      // operands two ahead of the MFMAs
+      bf16x8 k0 = kread(i & 1, 0), k1 = kread(i & 1, 1);
 #pragma unroll
       for (int j = 0; j < NKK * NB; ++j) {
-        const bf16x8 knext = kread(i & 1, j + 1 < NKK * NB ? j + 1 : j);
-        sc[j % NB] = mfma_bf16_32x32x16(kcur, qr[j / NB], sc[j % NB]);
-        kcur = knext;
+        const bf16x8 k2 = kread(i & 1, j + 2 < NKK * NB ? j + 2 : NKK * NB - 1);
+        sc[j % NB] = mfma_bf16_32x32x16(k0, qr[j / NB], sc[j % NB]);
+        k0 = k1;
+        k1 = k2;
       }
+      // keep four operand reads in flight ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int g = 0; g < NKK * NB / 2 - 2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     if (i > 0) {
-      bf16x8 vcur = vread(i - 1, 0);
+      bf16x8 v0 = vread(i - 1, 0), v1 = vread(i - 1, 1);
 #pragma unroll
       for (int j = 0; j < NPV; ++j) {
-        const bf16x8 vnext = vread(i - 1, j + 1 < NPV ? j + 1 : j);
+        const bf16x8 v2 = vread(i - 1, j + 2 < NPV ? j + 2 : NPV - 1);
         const int db = j / (2 * NB), b = (j / 2) % NB, h2 = j % 2;
-        o[db] = mfma_bf16_32x32x16(vcur, pk[b][h2], o[db]);
-        vcur = vnext;
+        o[db] = mfma_bf16_32x32x16(v0, pk[b][h2], o[db]);
+        v0 = v1;
+        v1 = v2;
       }
+      // each V operand is two ds_read_b64_tr_b16: eight reads (four operands) ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int g = 0; g < NPV / 2 - 2; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    // copies issued after this phase's LDS reads (see the kernel comment)
+    if (grp == 0) {
+      if (i + 1 < nt) dma_k(i + 1, (i + 1) & 1);
+      if (i < nt) dma_v(i, i & 1);
     }
     ISPA_LDS_BARRIER();   // copies in flight stay in flight across this barrier
     // ---- vector phase: softmax of tile i ----
@@ -631,7 +653,9 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
       }
       l += sum;
     }
-    if (grp == 0) ISPA_WAIT_VMCNT(0);   // this step's copies (K(i+1), V(i)) have landed
+    // this step's copies (K(i+1), V(i)) have landed; executed by both groups (a no-op for B) so that
+    // no path enters the next matrix phase with a copy pending
+    ISPA_WAIT_VMCNT(0);
     ISPA_LDS_BARRIER();
   }
   if (grp == 0) ISPA_LDS_BARRIER();     // matches group B's extra prologue barrier
