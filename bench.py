@@ -88,8 +88,8 @@ class Layer:
 # rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
 # attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only
 # while the source is unchanged.
-ATTN_TRAFFIC = {"sha256": "e126010e4f6c9cdbb1384b2307dc0b9a8b6a84c7d00c819fa233fb80e4fcdcbf",
-                "bytes_per_launch": 159219272}
+ATTN_TRAFFIC = {"sha256": "6884d8344dd03cabe85622cee041f3cdf9140b186a812f0a96dbb7841aacb814",
+                "bytes_per_launch": 158820095}
 
 
 def attn_traffic():
