@@ -12,6 +12,8 @@ the HIP path: it is plain NumPy in float64 (plus pure-Python loops and exact rat
   * `oracle.absorb`     section 2, stage 2 "Layer Absorb": the ridge objective and its closed form
     (first and second display equations of that stage), and "Dynamic Layer Selection" (rank layers
     by reconstruction error, lowest first).
+  * `oracle.steady`     section 2, stage 3 "Memory-Efficient Inference": the L-Layer steady state
+    (updated weights W + dW at the model precision, the output projection, history eviction).
   * `oracle.brute`      tiny-size brute force (loops, `fractions.Fraction`) used to pin the above.
 
 Every function is pinned by a `-m "not gpu"` test against closed forms, identities fixed by the
@@ -19,4 +21,4 @@ mathematics, textbook routines or brute force. Readings the pages leave open (Gr
 normalisation, the warmup protocol, the key distribution) are fixed by the workload definitions and
 carry no pin from the pages: parity unpinned for those readings only.
 """
-from . import attention, absorb, brute  # noqa: F401
+from . import attention, absorb, brute, steady  # noqa: F401
