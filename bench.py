@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--attn-only-cfg", type=int, default=None,
                     help="time only ispa_attn_dual on workload 2, 4 (chunk 4) or 5 (dual, local-only and "
                          "single-pass forms, warm and cold cache) and print one JSON line")
+    ap.add_argument("--steady", action="store_true",
+                    help="time the steady state after the warmup: L-Layer vs F-Layer chunk at 9/30/60 frames")
     ap.add_argument("--gram-only-cfg", type=int, default=None,
                     help="time only the statistics update of one chunk at workload 3's or 4's width")
     return ap.parse_args()
@@ -248,6 +250,74 @@ def gram_report(cfg, steps, warmup, torch):
           flush=True)
 
 
+def steady_report(steps, warmup, torch):
+    """After the warmup (ISPA stage 3): time of one chunk of an L-Layer (local-only attention over sink
+    + current chunk, projection with W + dW) against an F-Layer (full attention over the whole cache,
+    projection with W), at 9, 30 and 60 frames of history (workload 5's tensors), and the per-chunk
+    model time with K of N layers converted."""
+    import ispa_inputs as inputs
+    import kv_cache_attention_split_amd as ispa
+    wl5 = inputs.CONFIGS[5]
+    wl3 = inputs.CONFIGS[3]
+    inp = inputs.attention_inputs(5, 0, 0)
+    dev = {k: bf16_dev(inp[k], torch) for k in ("q", "sink_k", "sink_v", "cur_k", "cur_v", "hist_k", "hist_v")}
+    n_q = inp["q"].shape[0]
+    H, dh = wl5.n_heads, wl5.head_dim
+    d = H * dh
+    empty = dev["hist_k"][:0]
+    a = torch.empty((n_q, d), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(a)
+    lse = torch.empty((H, n_q), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    w = (torch.randn((d, d), device="cuda", generator=g) / d ** 0.5).float()
+    dw = (1e-2 * torch.randn((d, d), device="cuda", generator=g) / d ** 0.5).float()
+    w_new = torch.empty((d, d), dtype=torch.bfloat16, device="cuda")
+    w_old = torch.empty((d, d), dtype=torch.bfloat16, device="cuda")
+    ispa.ispa_apply_delta(w, dw, w_new)
+    ispa.ispa_apply_delta(w, torch.zeros_like(dw), w_old)
+    t_apply = _time_calls(lambda: ispa.ispa_apply_delta(w, dw, w_new), steps, warmup, torch)
+    frame = inputs.FRAME_TOKENS
+    n_sc = inp["sink_k"].shape[0] + inp["cur_k"].shape[0]
+
+    def local_layer():
+        ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"], empty, empty,
+                            wl5.scale, a, None, lse)
+        ispa.ispa_project(a, w_new, y)
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:
+        local_layer()
+        torch.cuda.synchronize()
+    t_proj = _time_calls(lambda: ispa.ispa_project(a, w_new, y), steps, warmup, torch)
+    t_l = _time_calls(local_layer, steps, warmup, torch)
+    rows = []
+    for frames in (9, 30, 60):
+        nh = frames * frame
+        jk = torch.cat([dev["sink_k"], dev["hist_k"][:nh]], dim=0)
+        jv = torch.cat([dev["sink_v"], dev["hist_v"][:nh]], dim=0)
+
+        def full_layer():
+            ispa.ispa_attn_dual(dev["q"], jk, jv, dev["cur_k"], dev["cur_v"], empty, empty, wl5.scale, a, None, lse)
+            ispa.ispa_project(a, w_old, y)
+
+        t_f = _time_calls(full_layer, steps, warmup, torch)
+        n_layers, k = wl3.n_layers, wl3.k_select
+        rows.append({"history_frames": frames, "keys_full": n_sc + nh, "keys_local": n_sc,
+                     "f_layer_ms": round(t_f, 4), "l_layer_ms": round(t_l, 4),
+                     "chunk_ms_all_f": round(n_layers * t_f, 3),
+                     "chunk_ms_with_l": round((n_layers - k) * t_f + k * t_l, 3),
+                     "speedup": round(n_layers * t_f / ((n_layers - k) * t_f + k * t_l), 3),
+                     "kv_tokens_kept_fraction": round(((n_layers - k) * (n_sc + nh) + k * n_sc)
+                                                      / (n_layers * (n_sc + nh)), 4)})
+        del jk, jv
+    fl = 2.0 * n_q * d * d
+    print(json.dumps({"workload": "wan1.3b steady state (after the warmup)", "n_q": n_q, "d": d,
+                      "layers": wl3.n_layers, "l_layers": wl3.k_select,
+                      "projection": {"ms": round(t_proj, 4), "tflops": round(fl / t_proj / 1e9, 1),
+                                     "frac": round(fl / t_proj / 1e9 / PEAK_BF16_TFLOPS, 4)},
+                      "apply_delta_ms": round(t_apply, 4), "per_history": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -260,6 +330,9 @@ def main():
 
     if args.attn_only_cfg is not None:
         attn_report(args.attn_only_cfg, max(args.steps, 20), max(args.warmup, 5), torch)
+        return
+    if args.steady:
+        steady_report(max(args.steps, 20), max(args.warmup, 5), torch)
         return
     if args.gram_only_cfg is not None:
         gram_report(args.gram_only_cfg, max(args.steps, 20), max(args.warmup, 5), torch)

@@ -166,6 +166,46 @@ ispa_status ispa_layer_error(int32_t d, int32_t batch,
 ispa_status ispa_rank_layers(const double *eps, int32_t n_layers, int32_t k,
                              int32_t *selected, uint8_t *is_l_layer);
 
+/* ---------------------------------------------------------------------------------------------
+ * L-Layer steady state (ISPA page, section 2 stage 3 "Memory-Efficient Inference": after the warmup
+ * the selected layers drop their history keys and values, attend to the sink tokens and the current
+ * chunk only, and project with the updated weights W_new = W + dW; the other layers keep the full
+ * cache and W). The attention of an L-Layer is ispa_attn_dual with an empty history and
+ * a_full = NULL; the three calls below are the weight update, the projection and the eviction plan.
+ * ------------------------------------------------------------------------------------------- */
+
+/* W_new = W + dW as bf16 in nn.Linear orientation.
+ *
+ *   d_in, d_out  matrix sizes (>= 1)
+ *   W, dW        device fp32, both [d_in, d_out] (y = A W) or, with w_is_linear_weight, both
+ *                [d_out, d_in] (y = A W^T); dense, 16-byte aligned
+ *   w_new        device bf16 [d_out, d_in], out: round-to-nearest-even of the fp32 sum W + dW
+ *                (one fp32 addition per element), always in the nn.Linear orientation
+ * Asynchronous on `stream`; argument errors are returned before any GPU work. */
+ispa_status ispa_apply_delta(int32_t d_in, int32_t d_out, const float *W, const float *dW,
+                             int32_t w_is_linear_weight, void *w_new, void *stream);
+
+/* Output projection y = A W^T of one chunk (bf16 in, fp32 accumulation, bf16 out).
+ *
+ *   n            rows (tokens, >= 0; 0 is a no-op)
+ *   d_in, d_out  d_in a multiple of 32, d_out a multiple of 8
+ *   a            device bf16 [n, d_in], row stride lda elements (lda >= d_in, multiple of 8)
+ *   w            device bf16 [d_out, d_in] dense (nn.Linear orientation, e.g. from ispa_apply_delta)
+ *   y            device bf16 [n, d_out], out, row stride ldy elements (ldy >= d_out, multiple of 8)
+ * All pointers 16-byte aligned. Asynchronous on `stream`. */
+ispa_status ispa_project(int64_t n, int32_t d_in, int32_t d_out, const void *a, int64_t lda,
+                         const void *w, void *y, int64_t ldy, void *stream);
+
+/* History kept by every layer after the warmup (host-only, no GPU work). With the cache laid out
+ * [sink | history | current], an L-Layer keeps 0 history tokens and an F-Layer n_hist.
+ *
+ *   is_l_layer      host uint8 [n_layers] (e.g. from ispa_rank_layers)
+ *   hist_kept       host int64 [n_layers], out
+ *   evicted_tokens  host int64, out: key/value tokens freed over all layers (may be NULL)
+ * Negative counts are ISPA_E_ARG. */
+ispa_status ispa_kv_plan(int32_t n_layers, const uint8_t *is_l_layer, int64_t n_sink, int64_t n_hist,
+                         int64_t n_cur, int64_t *hist_kept, int64_t *evicted_tokens);
+
 /* Human-readable name of a status code (static storage). */
 const char *ispa_status_string(ispa_status s);
 

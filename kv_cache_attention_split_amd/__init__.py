@@ -19,7 +19,8 @@ from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVSegment, lib, lib_
 __all__ = [
     "ispa_attn_dual", "ispa_absorb_accumulate", "ispa_absorb_accumulate_workspace",
     "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_layer_error",
-    "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_status_string", "ispa_version",
+    "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_apply_delta", "ispa_project",
+    "ispa_kv_plan", "ispa_status_string", "ispa_version",
     "IspaError", "lib_path",
 ]
 
@@ -161,6 +162,40 @@ def ispa_rank_layers(eps: Sequence[float], k: int):
     st = lib().ispa_rank_layers(e, n, int(k), sel, flag)
     _check(st, "ispa_rank_layers")
     return [int(sel[i]) for i in range(k)], [int(flag[i]) for i in range(n)]
+
+
+def ispa_apply_delta(W, dW, w_new, w_is_linear_weight: bool = False, stream=None) -> None:
+    """w_new (bf16 [d_out, d_in]) = W + dW rounded to bf16; W, dW fp32 [d_in, d_out] (y = A W), or
+    [d_out, d_in] with w_is_linear_weight."""
+    r, c = (int(x) for x in W.shape)
+    d_in, d_out = (c, r) if w_is_linear_weight else (r, c)
+    if tuple(dW.shape) != (r, c) or tuple(w_new.shape) != (d_out, d_in):
+        raise ValueError("ispa_apply_delta: W, dW must match and w_new must be [d_out, d_in]")
+    st = lib().ispa_apply_delta(d_in, d_out, _ptr(W), _ptr(dW), int(bool(w_is_linear_weight)),
+                                _ptr(w_new), _stream_handle(stream))
+    _check(st, "ispa_apply_delta")
+
+
+def ispa_project(a, w, y, stream=None) -> None:
+    """y [n, d_out] = a [n, d_in] @ w^T, w [d_out, d_in]; bf16 tensors, rows may be strided."""
+    n, d_in = (int(x) for x in a.shape)
+    d_out = int(w.shape[0])
+    if tuple(w.shape) != (d_out, d_in) or tuple(y.shape) != (n, d_out):
+        raise ValueError("ispa_project: shapes must be a [n, d_in], w [d_out, d_in], y [n, d_out]")
+    st = lib().ispa_project(n, d_in, d_out, _ptr(a), int(a.stride(0)) if n else d_in, _ptr(w), _ptr(y),
+                            int(y.stride(0)) if n else d_out, _stream_handle(stream))
+    _check(st, "ispa_project")
+
+
+def ispa_kv_plan(is_l_layer: Sequence[int], n_sink: int, n_hist: int, n_cur: int):
+    """Host-only: (history tokens kept per layer, evicted key/value tokens in total)."""
+    n = len(is_l_layer)
+    flags = (ctypes.c_uint8 * max(1, n))(*[1 if f else 0 for f in is_l_layer])
+    kept = (ctypes.c_int64 * max(1, n))()
+    ev = ctypes.c_int64(0)
+    st = lib().ispa_kv_plan(n, flags, int(n_sink), int(n_hist), int(n_cur), kept, ctypes.byref(ev))
+    _check(st, "ispa_kv_plan")
+    return [int(kept[i]) for i in range(n)], int(ev.value)
 
 
 def ispa_status_string(status: int) -> str:

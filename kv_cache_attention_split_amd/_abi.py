@@ -49,6 +49,9 @@ SIGNATURES = {
     "ispa_layer_error_workspace": (c_sz, [c_i32, c_i32]),
     "ispa_layer_error": (c_int, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ispa_rank_layers": (c_int, [c_vp, c_i32, c_i32, c_vp, c_vp]),
+    "ispa_apply_delta": (c_int, [c_i32, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]),
+    "ispa_project": (c_int, [c_i64, c_i32, c_i32, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp]),
+    "ispa_kv_plan": (c_int, [c_i32, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "ispa_status_string": (ctypes.c_char_p, [c_int]),
     "ispa_version": (c_i32, []),
 }

@@ -504,4 +504,40 @@ ispa_status ispa_rank_layers(const double *eps, int32_t n_layers, int32_t k, int
   return ISPA_OK;
 }
 
+// ------------------------------------------------------------------------------------------------
+ispa_status ispa_apply_delta(int32_t d_in, int32_t d_out, const float *W, const float *dW,
+                             int32_t w_is_linear_weight, void *w_new, void *stream) {
+  if (d_in <= 0 || d_out <= 0) return ISPA_E_ARG;
+  if (W == nullptr || dW == nullptr || w_new == nullptr) return ISPA_E_ARG;
+  if (!aligned16(W) || !aligned16(dW) || !aligned16(w_new)) return ISPA_E_ARG;
+  return hip_status(launch_apply_delta(W, dW, d_in, d_out, w_is_linear_weight ? 1 : 0,
+                                       (uint16_t *)w_new, (hipStream_t)stream));
+}
+
+ispa_status ispa_project(int64_t n, int32_t d_in, int32_t d_out, const void *a, int64_t lda,
+                         const void *w, void *y, int64_t ldy, void *stream) {
+  if (n < 0 || d_in <= 0 || d_out <= 0) return ISPA_E_ARG;
+  if (d_in % 32 != 0 || d_out % 8 != 0) return ISPA_E_UNSUPPORTED;
+  if (n == 0) return ISPA_OK;
+  if (a == nullptr || w == nullptr || y == nullptr) return ISPA_E_ARG;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(y)) return ISPA_E_ARG;
+  if (lda < d_in || lda % 8 != 0 || ldy < d_out || ldy % 8 != 0) return ISPA_E_ARG;
+  if ((n + 127) / 128 * ((d_out + 127) / 128) > INT32_MAX) return ISPA_E_UNSUPPORTED;
+  return hip_status(launch_project_bf16(n, d_in, d_out, (const uint16_t *)a, lda, (const uint16_t *)w,
+                                        (uint16_t *)y, ldy, (hipStream_t)stream));
+}
+
+ispa_status ispa_kv_plan(int32_t n_layers, const uint8_t *is_l_layer, int64_t n_sink, int64_t n_hist,
+                         int64_t n_cur, int64_t *hist_kept, int64_t *evicted_tokens) {
+  if (n_layers < 0 || n_sink < 0 || n_hist < 0 || n_cur < 0) return ISPA_E_ARG;
+  if (n_layers > 0 && (is_l_layer == nullptr || hist_kept == nullptr)) return ISPA_E_ARG;
+  int64_t evicted = 0;
+  for (int32_t i = 0; i < n_layers; ++i) {
+    hist_kept[i] = is_l_layer[i] ? 0 : n_hist;
+    if (is_l_layer[i]) evicted += n_hist;
+  }
+  if (evicted_tokens != nullptr) *evicted_tokens = evicted;
+  return ISPA_OK;
+}
+
 }  // extern "C"

@@ -101,4 +101,16 @@ hipError_t launch_add(const CPtrBatch &a, const CPtrBatch &b, const PtrBatch &ou
 hipError_t launch_copy(const CPtrBatch &in, const PtrBatch &out, int d, int count, hipStream_t s);
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t s);
 
+// ------------------------------------------------------------------------------------------------
+// L-Layer steady state
+// ------------------------------------------------------------------------------------------------
+// out [d_out, d_in] bf16 = W + dW (fp32 sum, round to nearest even); W, dW are [d_out, d_in] when
+// linear != 0, else [d_in, d_out] (transposed on the way)
+hipError_t launch_apply_delta(const float *W, const float *dW, int d_in, int d_out, int linear,
+                              uint16_t *out, hipStream_t s);
+// y [n, d_out] (row stride ldy) = a [n, d_in] (row stride lda) . w^T, w [d_out, d_in]; all bf16,
+// fp32 accumulation; d_in % 32 == 0
+hipError_t launch_project_bf16(int64_t n, int d_in, int d_out, const uint16_t *a, int64_t lda,
+                               const uint16_t *w, uint16_t *y, int64_t ldy, hipStream_t s);
+
 }  // namespace ispa

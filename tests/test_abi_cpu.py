@@ -158,3 +158,41 @@ def test_rank_layers_errors(L):
     assert L.ispa_rank_layers(e, 3, -1, sel, None) == _abi.ISPA_E_ARG
     assert L.ispa_rank_layers(None, 3, 1, sel, None) == _abi.ISPA_E_ARG
     assert L.ispa_rank_layers(e, 3, 0, None, None) == _abi.ISPA_OK
+
+
+def test_steady_state_argument_errors(L):
+    ok, arg, uns = _abi.ISPA_OK, _abi.ISPA_E_ARG, _abi.ISPA_E_UNSUPPORTED
+    # weight update
+    assert L.ispa_apply_delta(0, 8, FAKE, FAKE2, 0, FAKE, None) == arg
+    assert L.ispa_apply_delta(8, 8, None, FAKE2, 0, FAKE, None) == arg
+    assert L.ispa_apply_delta(8, 8, FAKE, FAKE2, 0, None, None) == arg
+    assert L.ispa_apply_delta(8, 8, MISALIGNED, FAKE2, 0, FAKE, None) == arg
+    # projection
+    assert L.ispa_project(0, 64, 64, None, 64, None, None, 64, None) == ok      # empty: no-op
+    assert L.ispa_project(-1, 64, 64, FAKE, 64, FAKE2, FAKE, 64, None) == arg
+    assert L.ispa_project(10, 48, 64, FAKE, 48, FAKE2, FAKE, 64, None) == uns  # d_in % 32
+    assert L.ispa_project(10, 64, 60, FAKE, 64, FAKE2, FAKE, 64, None) == uns  # d_out % 8
+    assert L.ispa_project(10, 64, 64, FAKE, 60, FAKE2, FAKE, 64, None) == arg  # lda < d_in
+    assert L.ispa_project(10, 64, 64, FAKE, 68, FAKE2, FAKE, 64, None) == arg  # lda % 8
+    assert L.ispa_project(10, 64, 64, FAKE, 64, FAKE2, FAKE, 56, None) == arg  # ldy < d_out
+    assert L.ispa_project(10, 64, 64, MISALIGNED, 64, FAKE2, FAKE, 64, None) == arg
+    assert L.ispa_project(10, 64, 64, FAKE, 64, None, FAKE, 64, None) == arg
+    # eviction plan (host only)
+    kept = (ctypes.c_int64 * 3)()
+    assert L.ispa_kv_plan(3, None, 1, 2, 3, kept, None) == arg
+    flags = (ctypes.c_uint8 * 3)(1, 0, 1)
+    assert L.ispa_kv_plan(3, flags, 1, -2, 3, kept, None) == arg
+    assert L.ispa_kv_plan(0, None, 1, 2, 3, None, None) == ok
+
+
+def test_kv_plan_matches_oracle():
+    from oracle import steady as ost
+    rng = np.random.default_rng(4)
+    for _ in range(20):
+        n = int(rng.integers(0, 40))
+        flags = rng.integers(0, 2, size=n).tolist()
+        ns, nh, nc = (int(x) for x in rng.integers(0, 100000, size=3))
+        kept, ev = ispa.ispa_kv_plan(flags, ns, nh, nc)
+        ref = ost.layer_plan([bool(f) for f in flags], ns, nh, nc)
+        assert kept == ref["hist_kept"]
+        assert ev == ref["evicted_tokens"]
