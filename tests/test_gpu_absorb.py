@@ -34,8 +34,11 @@ def _accumulate(chunks, dtype, d, with_f=True):
     return G, X, F
 
 
+# ragged shapes: 333 and 517 rows end inside a 32-row stage, 40 rows fill less than two stages,
+# d = 1088 ends inside a 128-column tile
 @pytest.mark.parametrize("d,n,dtype", [(1536, 4680, "bf16"), (192, 333, "bf16"), (128, 128, "f32"),
-                                       (320, 517, "f32")])
+                                       (320, 517, "f32"), (1024, 333, "bf16"), (1024, 40, "bf16"),
+                                       (1088, 517, "bf16")])
 def test_statistics_full_compare(d, n, dtype):
     _log(f"case: statistics d={d} rows={n} {dtype}")
     rows = inputs.absorb_rows(3, 0, 3, d=d, n_rows=n, dtype=dtype)
@@ -48,6 +51,29 @@ def test_statistics_full_compare(d, n, dtype):
     if dtype == "bf16":
         torch = torch_mod()
         assert torch.equal(G, G.T) and torch.equal(F, F.T)
+
+
+def test_statistics_without_f_wide_rows():
+    d, n = 1088, 300
+    _log(f"case: statistics d={d} rows={n} bf16, F not requested")
+    rows = inputs.absorb_rows(3, 2, 1, d=d, n_rows=n, dtype="bf16")
+    G, X, F = _accumulate([(rows["a_loc"], rows["a_full"])], "bf16", d, with_f=False)
+    ref = oab.grams(rows["a_loc"], rows["a_full"])
+    assert rel_fro(to_host64(G), ref["G"]) <= 1e-5
+    assert rel_fro(to_host64(X), ref["X"]) <= 1e-5
+    assert not F.any(), "F written although not requested"
+
+
+def test_statistics_wide_repeatable_bitwise():
+    """No atomics: two runs over the same rows give identical bits."""
+    d, n = 1536, 4680
+    _log(f"case: statistics d={d} rows={n} bf16, two runs compared bitwise")
+    rows = inputs.absorb_rows(3, 0, 2, d=d, n_rows=n, dtype="bf16")
+    first = _accumulate([(rows["a_loc"], rows["a_full"])], "bf16", d)
+    second = _accumulate([(rows["a_loc"], rows["a_full"])], "bf16", d)
+    torch = torch_mod()
+    for a, b in zip(first, second):
+        assert torch.equal(a, b)
 
 
 def test_statistics_four_chunks_and_zero_gap():
