@@ -23,6 +23,10 @@ N(0,1) while neighbouring frames are correlated. Queries and values are iid N(0,
 N(0, 1/d). bf16 workloads round every drawn value to bf16 (round to nearest even) and the rounded
 values are the inputs of both sides.
 
+TempCache merge cases (`static_history_case`) draw a history whose static token positions repeat
+the same keys in every frame (the exact-duplicate case of the FAST-AR page's Lemma 5.1), with the
+grouping of the history tokens in compressed form (`csr_from_labels`).
+
 Seeds: numpy SeedSequence([base, cfg, layer, stream]) with stream 1 = key chain, 2 = values,
 3 = weight, 16 + c = queries of chunk c, 32 + c = synthetic absorb rows of chunk c.
 """
@@ -30,7 +34,7 @@ from __future__ import annotations
 
 import dataclasses
 import os
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -264,6 +268,66 @@ def attention_case(seed: int, n_heads: int, head_dim: int, n_q: int, n_sink: int
         out[name + "_v"] = v[a:b]
     out["scale"] = (1.0 / float(np.sqrt(head_dim))) if scale is None else float(scale)
     out["dtype"] = dtype
+    return out
+
+
+def csr_from_labels(labels) -> Tuple[np.ndarray, np.ndarray]:
+    """Groups given as one label per token (labels 0 .. G-1, each used) -> (offsets [G+1] int32,
+    members [n] int32): group g holds the tokens with label g in increasing token order."""
+    lab = np.asarray(labels, dtype=np.int64)
+    n_groups = int(lab.max()) + 1 if lab.size else 0
+    counts = np.bincount(lab, minlength=n_groups)
+    offsets = np.zeros(n_groups + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    members = np.argsort(lab, kind="stable").astype(np.int32)
+    return offsets, members
+
+
+def static_history_case(seed: int, n_heads: int, head_dim: int, n_q: int, n_sink: int, n_cur: int,
+                        n_frames: int, frame_tokens: int, static_frac: float, dtype: str = "bf16",
+                        scale: Optional[float] = None) -> Dict[str, object]:
+    """An attention case whose history holds exact duplicate keys (video with a static region).
+
+    The history is n_frames frames of frame_tokens tokens. A fixed random subset of
+    round(static_frac * frame_tokens) token positions is static: its keys are the same in every
+    frame; its values still differ per frame. All other keys, all values and the queries are iid
+    N(0,1). Returns the case dict of `attention_case` plus "hist_labels" [n_hist] (one label per
+    history token: static position p -> p's rank among the static positions, other tokens ->
+    consecutive labels after those) and "hist_groups" = csr_from_labels(hist_labels).
+    """
+    rng = np.random.default_rng(np.random.SeedSequence([SEED_BASE, 1100, seed]))
+    n_hist = n_frames * frame_tokens
+    n_static = int(round(static_frac * frame_tokens))
+    static_pos = np.sort(rng.choice(frame_tokens, size=n_static, replace=False))
+    is_static = np.zeros(frame_tokens, dtype=bool)
+    is_static[static_pos] = True
+    rank = np.cumsum(is_static) - 1
+    static_keys = _normal(rng, (n_static, n_heads, head_dim))
+    hist_k = _normal(rng, (n_hist, n_heads, head_dim))
+    labels = np.empty(n_hist, dtype=np.int64)
+    nxt = n_static
+    for f in range(n_frames):
+        for p in range(frame_tokens):
+            t = f * frame_tokens + p
+            if is_static[p]:
+                hist_k[t] = static_keys[rank[p]]
+                labels[t] = rank[p]
+            else:
+                labels[t] = nxt
+                nxt += 1
+    sink_k = _normal(rng, (n_sink, n_heads, head_dim))
+    cur_k = _normal(rng, (n_cur, n_heads, head_dim))
+    v = _normal(rng, (n_sink + n_cur + n_hist, n_heads, head_dim))
+    q = _normal(rng, (n_q, n_heads, head_dim))
+    if dtype == "bf16":
+        sink_k, cur_k, hist_k, v, q = (round_bf16(x) for x in (sink_k, cur_k, hist_k, v, q))
+    out: Dict[str, object] = {"q": q, "sink_k": sink_k, "cur_k": cur_k, "hist_k": hist_k,
+                              "sink_v": v[:n_sink], "cur_v": v[n_sink:n_sink + n_cur],
+                              "hist_v": v[n_sink + n_cur:]}
+    out["scale"] = (1.0 / float(np.sqrt(head_dim))) if scale is None else float(scale)
+    out["dtype"] = dtype
+    out["hist_labels"] = labels
+    out["hist_groups"] = csr_from_labels(labels)
     return out
 
 
