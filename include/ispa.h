@@ -85,6 +85,73 @@ ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, flo
                            void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Dual-stream attention with a per-key additive logit bias (FAST-AR summary page, section 2 part A
+ * "TempCache", Lemma 5.1: a group of m identical keys is replaced by one key whose value is the
+ * group's mean value and whose logit is raised by ln m, with no change to the attention output or
+ * its LSE). The logit of key j of a segment S in head h becomes
+ *   softmax_scale * q_i . k_j + b_S[h * head_stride + j]
+ * in every sum above (outputs and all three LSEs), so a cache merged by ispa_kv_merge, with its
+ * ln(count) as the bias, gives the same A_loc, A_full and LSEs as the unmerged cache.
+ *
+ *   bias          NULL = no bias (the call is then ispa_attn_dual); otherwise
+ *     .sink, .cur, .hist   device fp32 per segment, 4-byte aligned, or NULL (zero bias for that
+ *                          segment); natural-log units; values must be finite with |b| <= 1e30
+ *                          (a large negative value such as -1e30 masks a key)
+ *     .*_head_stride       per segment: 0 = one bias per key shared by all heads ([n]); > 0 =
+ *                          elements between heads ([H, head_stride], head_stride >= n)
+ * Other arguments, outputs and errors as for ispa_attn_dual; a bad bias (misaligned pointer,
+ * negative or too small head stride) is ISPA_E_ARG.
+ * ------------------------------------------------------------------------------------------- */
+typedef struct {
+  const float *sink;
+  const float *cur;
+  const float *hist;
+  int64_t sink_head_stride;
+  int64_t cur_head_stride;
+  int64_t hist_head_stride;
+} ispa_kv_bias;
+
+ispa_status ispa_attn_dual_biased(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                  const void *q, int64_t n_q, int64_t q_row_stride,
+                                  ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                                  const ispa_kv_bias *bias,
+                                  void *a_loc, void *a_full,
+                                  float *lse_loc, float *lse_hist, float *lse_full,
+                                  void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * TempCache exact merge of one cache segment (FAST-AR summary page, section 2 part A "TempCache",
+ * Lemma 5.1). Groups of token rows become single rows: for group g with members
+ * members[offsets[g]], .., members[offsets[g+1] - 1] (token indices into the segment),
+ *   k_out[g] = mean of the members' key rows,   v_out[g] = mean of their value rows,
+ *   bias_out[g] = ln(offsets[g+1] - offsets[g])
+ * over all H*d_h columns; sums in fp32 in member order, one correctly rounded division, one rounding
+ * to dt (nearest even for bf16). With the merged rows as a segment and bias_out as its bias,
+ * ispa_attn_dual_biased reproduces attention over the original rows exactly when every group's keys
+ * are identical (the lemma), and approximately for near-identical keys. Finding the groups (the
+ * page's similarity search) is the caller's.
+ *
+ *   dt          ISPA_BF16 or ISPA_F32 (type of k, v, k_out, v_out)
+ *   width       elements per token row, H*d_h; a multiple of 8 (else ISPA_E_UNSUPPORTED)
+ *   k, v        device [n, width] rows, row stride in_stride (>= width, multiple of 8), 16-byte aligned
+ *   n           rows of the input segment (>= 0)
+ *   offsets     device int32 [n_groups + 1], non-decreasing, offsets[0] = 0
+ *   members     device int32 [offsets[n_groups]], each in [0, n)
+ *   n_groups    0 .. 2^26 (0 is a no-op)
+ *   k_out, v_out  device out [n_groups, width], row stride out_stride (>= width, multiple of 8),
+ *               16-byte aligned; must not overlap k, v
+ *   bias_out    device fp32 out [n_groups], or NULL
+ * The device arrays offsets and members are not read on the host: a member outside [0, n) is skipped
+ * (contributes zero, never read), and a group with no members gets zero rows and bias -inf (which the biased attention
+ * does not accept). Errors: ISPA_E_ARG (sizes, NULL or misaligned pointers), ISPA_E_UNSUPPORTED,
+ * ISPA_E_HIP.
+ * ------------------------------------------------------------------------------------------- */
+ispa_status ispa_kv_merge(ispa_dtype dt, int32_t width, const void *k, const void *v, int64_t n,
+                          int64_t in_stride, const int32_t *offsets, const int32_t *members,
+                          int64_t n_groups, void *k_out, void *v_out, int64_t out_stride,
+                          float *bias_out, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Warmup statistics (ISPA page, section 2 stage 2 "Layer Absorb": the closed form needs
  * A_loc^T A_loc and A_loc^T (A_full - A_loc) over the warmup rows; stage 1 says these rows are the
  * warmup chunks' attention outputs).

@@ -13,11 +13,11 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
-from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVSegment, lib, lib_path,  # noqa: F401
+from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVBias, KVSegment, lib, lib_path,  # noqa: F401
                    status_string)
 
 __all__ = [
-    "ispa_attn_dual", "ispa_absorb_accumulate", "ispa_absorb_accumulate_workspace",
+    "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_absorb_accumulate", "ispa_absorb_accumulate_workspace",
     "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_layer_error",
     "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_apply_delta", "ispa_project",
     "ispa_kv_plan", "ispa_status_string", "ispa_version",
@@ -90,6 +90,76 @@ def ispa_attn_dual(q, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v, softmax_scal
         _seg(sink_k, sink_v, H, dh), _seg(cur_k, cur_v, H, dh), _seg(hist_k, hist_v, H, dh),
         _ptr(a_loc), _ptr(a_full), _ptr(lse_loc), _ptr(lse_hist), _ptr(lse_full), _stream_handle(stream))
     _check(st, "ispa_attn_dual")
+
+
+def _bias_arg(t, n: int, n_heads: int):
+    """(pointer, head stride) of a segment bias: None, [n] (all heads) or [H, stride >= n] fp32."""
+    if t is None or n == 0:
+        return None, None
+    torch = _torch()
+    if t.dtype != torch.float32 or t.stride(-1) != 1:
+        raise ValueError("a bias must be float32 with unit stride over the keys")
+    if t.dim() == 1:
+        if t.shape[0] != n:
+            raise ValueError(f"bias of {t.shape[0]} keys for a segment of {n}")
+        return _ptr(t), 0
+    if t.dim() != 2 or t.shape[0] != n_heads or t.shape[1] != n:
+        raise ValueError(f"a per-head bias must be [{n_heads}, {n}]")
+    return _ptr(t), int(t.stride(0))
+
+
+def ispa_attn_dual_biased(q, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v, softmax_scale: float,
+                          a_loc, a_full=None, lse_loc=None, lse_hist=None, lse_full=None,
+                          sink_bias=None, cur_bias=None, hist_bias=None, stream=None) -> None:
+    """Dual-stream attention with a per-key additive logit bias (see ispa_attn_dual_biased in
+    include/ispa.h). Each *_bias is None, float32 [n] (shared by the heads) or [H, n] (a view with
+    unit stride over the keys)."""
+    n_q, H, dh = (int(x) for x in q.shape)
+    if q.stride(2) != 1 or q.stride(1) != dh:
+        raise ValueError("q rows must be contiguous over (H, d_h)")
+    for o in (a_loc, a_full):
+        if o is not None and (tuple(o.shape) != (n_q, H * dh) or not o.is_contiguous() or o.dtype != q.dtype):
+            raise ValueError("outputs must be contiguous [n_q, H*d_h] of q's dtype")
+    torch = _torch()
+    for o in (lse_loc, lse_hist, lse_full):
+        if o is not None and (tuple(o.shape) != (H, n_q) or not o.is_contiguous() or o.dtype != torch.float32):
+            raise ValueError("LSE outputs must be contiguous float32 [H, n_q]")
+    segs = [_seg(sink_k, sink_v, H, dh), _seg(cur_k, cur_v, H, dh), _seg(hist_k, hist_v, H, dh)]
+    args = [_bias_arg(b, int(sg.n), H) for b, sg in zip((sink_bias, cur_bias, hist_bias), segs)]
+    bias = KVBias(args[0][0], args[1][0], args[2][0], args[0][1] or 0, args[1][1] or 0, args[2][1] or 0)
+    st = lib().ispa_attn_dual_biased(
+        _dtype_code(q), H, dh, ctypes.c_float(softmax_scale), _ptr(q), n_q, int(q.stride(0)),
+        segs[0], segs[1], segs[2], ctypes.byref(bias),
+        _ptr(a_loc), _ptr(a_full), _ptr(lse_loc), _ptr(lse_hist), _ptr(lse_full), _stream_handle(stream))
+    _check(st, "ispa_attn_dual_biased")
+
+
+def ispa_kv_merge(k, v, offsets, members, k_out, v_out, bias_out=None, stream=None) -> None:
+    """TempCache merge of one segment (see ispa_kv_merge in include/ispa.h): k, v [n, H, d_h];
+    offsets int32 [G+1], members int32 [offsets[G]] on the device; k_out, v_out [G, H, d_h] of k's
+    dtype; bias_out float32 [G] or None."""
+    n = int(k.shape[0])
+    width = int(k.shape[1] * k.shape[2])
+    n_groups = int(offsets.shape[0]) - 1
+    torch = _torch()
+    for t in (k, v):
+        if t.dtype != k.dtype or tuple(t.shape[1:]) != tuple(k.shape[1:]) or t.stride(2) != 1 or \
+                t.stride(1) != k.shape[2] or t.stride(0) != k.stride(0) or t.shape[0] != n:
+            raise ValueError("k and v must be matching [n, H, d_h] with contiguous rows")
+    for t in (k_out, v_out):
+        if t.dtype != k.dtype or tuple(t.shape) != (n_groups,) + tuple(k.shape[1:]) or t.stride(2) != 1 or \
+                t.stride(1) != k.shape[2] or t.stride(0) != k_out.stride(0):
+            raise ValueError("k_out and v_out must be [G, H, d_h] of k's dtype with contiguous rows")
+    for t in (offsets, members):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("offsets and members must be contiguous int32")
+    if bias_out is not None and (bias_out.dtype != torch.float32 or tuple(bias_out.shape) != (n_groups,)):
+        raise ValueError("bias_out must be float32 [G]")
+    st = lib().ispa_kv_merge(
+        _dtype_code(k), width, _ptr(k), _ptr(v), n, int(k.stride(0)) if n else width, _ptr(offsets),
+        _ptr(members), n_groups, _ptr(k_out), _ptr(v_out), int(k_out.stride(0)) if n_groups else width,
+        _ptr(bias_out), _stream_handle(stream))
+    _check(st, "ispa_kv_merge")
 
 
 def ispa_absorb_accumulate_workspace(n_rows: int, d: int) -> int:

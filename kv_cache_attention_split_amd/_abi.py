@@ -28,6 +28,12 @@ class KVSegment(ctypes.Structure):
                 ("n", ctypes.c_int64), ("row_stride", ctypes.c_int64)]
 
 
+class KVBias(ctypes.Structure):
+    _fields_ = [("sink", ctypes.c_void_p), ("cur", ctypes.c_void_p), ("hist", ctypes.c_void_p),
+                ("sink_head_stride", ctypes.c_int64), ("cur_head_stride", ctypes.c_int64),
+                ("hist_head_stride", ctypes.c_int64)]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -42,6 +48,10 @@ c_int = ctypes.c_int
 SIGNATURES = {
     "ispa_attn_dual": (c_int, [c_int, c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, KVSegment, KVSegment,
                                KVSegment, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "ispa_attn_dual_biased": (c_int, [c_int, c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, KVSegment, KVSegment,
+                                      KVSegment, ctypes.POINTER(KVBias), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "ispa_kv_merge": (c_int, [c_int, c_i32, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64,
+                              c_vp, c_vp]),
     "ispa_absorb_accumulate_workspace": (c_sz, [c_i64, c_i32]),
     "ispa_absorb_accumulate": (c_int, [c_int, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ispa_absorb_solve_workspace": (c_sz, [c_i32, c_i32]),

@@ -102,10 +102,22 @@ const char *ispa_status_string(ispa_status s) {
 }
 
 // ------------------------------------------------------------------------------------------------
-ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+namespace {
+
+bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
+
+ispa_status check_bias(const float *b, int64_t n, int64_t head_stride) {
+  if (b == nullptr || n == 0) return ISPA_OK;
+  if (!aligned4(b)) return ISPA_E_ARG;
+  if (head_stride < 0 || (head_stride != 0 && head_stride < n)) return ISPA_E_ARG;
+  return ISPA_OK;
+}
+
+ispa_status attn_dual_impl(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
                            const void *q, int64_t n_q, int64_t q_row_stride, ispa_kv_segment sink,
-                           ispa_kv_segment cur, ispa_kv_segment hist, void *a_loc, void *a_full,
-                           float *lse_loc, float *lse_hist, float *lse_full, void *stream) {
+                           ispa_kv_segment cur, ispa_kv_segment hist, const ispa_kv_bias *bias,
+                           void *a_loc, void *a_full, float *lse_loc, float *lse_hist, float *lse_full,
+                           void *stream) {
   if (dt != ISPA_BF16 && dt != ISPA_F32) return ISPA_E_UNSUPPORTED;
   if (n_heads <= 0 || n_q < 0) return ISPA_E_ARG;
   if (head_dim != 64 && head_dim != 128) return ISPA_E_UNSUPPORTED;
@@ -119,6 +131,12 @@ ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, flo
   if ((st = check_segment(sink, width, align_elems)) != ISPA_OK) return st;
   if ((st = check_segment(cur, width, align_elems)) != ISPA_OK) return st;
   if (a_full != nullptr && (st = check_segment(hist, width, align_elems)) != ISPA_OK) return st;
+  if (bias != nullptr) {
+    if ((st = check_bias(bias->sink, sink.n, bias->sink_head_stride)) != ISPA_OK) return st;
+    if ((st = check_bias(bias->cur, cur.n, bias->cur_head_stride)) != ISPA_OK) return st;
+    if (a_full != nullptr && (st = check_bias(bias->hist, hist.n, bias->hist_head_stride)) != ISPA_OK)
+      return st;
+  }
   if (n_q == 0) return ISPA_OK;
   if (q == nullptr || !aligned16(q) || q_row_stride < width || q_row_stride % align_elems != 0)
     return ISPA_E_ARG;
@@ -149,9 +167,56 @@ ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, flo
   a.n_q = (int32_t)n_q;
   a.n_heads = n_heads;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.sink_b = bias != nullptr && sink.n > 0 ? bias->sink : nullptr;
+  a.cur_b = bias != nullptr && cur.n > 0 ? bias->cur : nullptr;
+  a.hist_b = bias != nullptr && want_full && hist.n > 0 ? bias->hist : nullptr;
+  a.sink_bhs = bias != nullptr ? bias->sink_head_stride : 0;
+  a.cur_bhs = bias != nullptr ? bias->cur_head_stride : 0;
+  a.hist_bhs = bias != nullptr ? bias->hist_head_stride : 0;
+  a.bias_to_score = 1.0f / softmax_scale;
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = dt == ISPA_BF16 ? launch_attn_bf16(a, head_dim, s) : launch_attn_f32(a, head_dim, s);
   return hip_status(e);
+}
+
+}  // namespace
+
+ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                           const void *q, int64_t n_q, int64_t q_row_stride, ispa_kv_segment sink,
+                           ispa_kv_segment cur, ispa_kv_segment hist, void *a_loc, void *a_full,
+                           float *lse_loc, float *lse_hist, float *lse_full, void *stream) {
+  return attn_dual_impl(dt, n_heads, head_dim, softmax_scale, q, n_q, q_row_stride, sink, cur, hist,
+                        nullptr, a_loc, a_full, lse_loc, lse_hist, lse_full, stream);
+}
+
+ispa_status ispa_attn_dual_biased(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                  const void *q, int64_t n_q, int64_t q_row_stride, ispa_kv_segment sink,
+                                  ispa_kv_segment cur, ispa_kv_segment hist, const ispa_kv_bias *bias,
+                                  void *a_loc, void *a_full, float *lse_loc, float *lse_hist,
+                                  float *lse_full, void *stream) {
+  return attn_dual_impl(dt, n_heads, head_dim, softmax_scale, q, n_q, q_row_stride, sink, cur, hist,
+                        bias, a_loc, a_full, lse_loc, lse_hist, lse_full, stream);
+}
+
+// ------------------------------------------------------------------------------------------------
+ispa_status ispa_kv_merge(ispa_dtype dt, int32_t width, const void *k, const void *v, int64_t n,
+                          int64_t in_stride, const int32_t *offsets, const int32_t *members,
+                          int64_t n_groups, void *k_out, void *v_out, int64_t out_stride,
+                          float *bias_out, void *stream) {
+  if (dt != ISPA_BF16 && dt != ISPA_F32) return ISPA_E_UNSUPPORTED;
+  if (width <= 0 || n < 0 || n_groups < 0) return ISPA_E_ARG;
+  if (width % 8 != 0) return ISPA_E_UNSUPPORTED;
+  if (n_groups > (int64_t)1 << 26 || n > INT32_MAX) return ISPA_E_ARG;   // grid of 64 threads per group
+  if (n_groups == 0) return ISPA_OK;
+  if (offsets == nullptr || ((uintptr_t)offsets & 3) != 0) return ISPA_E_ARG;
+  if (n > 0 && (k == nullptr || v == nullptr || !aligned16(k) || !aligned16(v))) return ISPA_E_ARG;
+  if (n > 0 && (members == nullptr || ((uintptr_t)members & 3) != 0)) return ISPA_E_ARG;
+  if (n > 0 && (in_stride < width || in_stride % 8 != 0)) return ISPA_E_ARG;
+  if (k_out == nullptr || v_out == nullptr || !aligned16(k_out) || !aligned16(v_out)) return ISPA_E_ARG;
+  if (out_stride < width || out_stride % 8 != 0) return ISPA_E_ARG;
+  if (bias_out != nullptr && ((uintptr_t)bias_out & 3) != 0) return ISPA_E_ARG;
+  return hip_status(launch_kv_merge(dt == ISPA_BF16, width, k, v, n, in_stride, offsets, members,
+                                    n_groups, k_out, v_out, out_stride, bias_out, (hipStream_t)stream));
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -67,6 +67,17 @@ __device__ __forceinline__ int kv_off(int r, int col) {   // byte offset of elem
   return r * (D * 2) + ((((col >> 3) ^ kv_swz<D>(r))) << 4) + ((col & 7) << 1);
 }
 
+// read in place of the bias of a segment that has none
+static __device__ __attribute__((aligned(16))) float g_zero_bias[4];
+
+// Bias pointer of key j (< the run's length) of the local run (sink then current) or the history
+// run, for head `head`; the zero word when that segment has no bias.
+__device__ __forceinline__ const float *bias_ptr(const AttnArgs &a, bool hist, int64_t j, int head) {
+  if (hist) return a.hist_b != nullptr ? a.hist_b + head * a.hist_bhs + j : g_zero_bias;
+  if (j < a.sink_n) return a.sink_b != nullptr ? a.sink_b + head * a.sink_bhs + j : g_zero_bias;
+  return a.cur_b != nullptr ? a.cur_b + head * a.cur_bhs + (j - a.sink_n) : g_zero_bias;
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
@@ -157,7 +168,7 @@ __device__ __forceinline__ void write_lse(float *out, float val, int head, int q
 #define ISPA_ATTN_WGS 2
 #endif
 
-template <int D>
+template <int D, bool BIAS>
 __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel(AttnArgs a, int n_qt) {
   constexpr int BK = ISPA_ATTN_BK;    // keys per tile
   constexpr bool PIPE = ISPA_ATTN_PIPE;
@@ -309,6 +320,20 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
     }
     f32x16 sc[NB];
     qk(sc, t & 1);
+    if constexpr (BIAS) {
+      // sc += b / tau, read straight from global memory (key 32b + 8(v/4) + 4hf + v%4 of the tile)
+      const bool hist = t >= nt_loc;
+      const int64_t nseg = hist ? a.hist_n : n_loc;
+      const int64_t j0 = tile_j0(t);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int64_t j = j0 + 32 * b + 8 * (v >> 2) + 4 * hf + (v & 3);
+          j = j < nseg ? j : nseg - 1;
+          sc[b][v] = __builtin_fmaf(*bias_ptr(a, hist, j, head), a.bias_to_score, sc[b][v]);
+        }
+    }
     const int n_valid = n_valid_of(t);
     if (n_valid < BK) {
 #pragma unroll
@@ -441,7 +466,7 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
 // a full wait while a global->LDS copy is in flight, which would serialise the operand reads. With
 // no copy in flight the reads run four operands ahead of the MFMAs (scheduling groups below).
 // ------------------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool BIAS>
 __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, int n_qt) {
   constexpr int BK = 64;
   constexpr int TB = BK * D * 2;
@@ -452,6 +477,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
 
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][TB];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][TB];
+  __shared__ __attribute__((aligned(256))) float bbuf[2][BIAS ? BK : 1];   // bias of tiles, beside K
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -502,6 +528,15 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     const int64_t rem = nseg - tile_j0(t);
     return (int)(rem < BK ? rem : BK);
   };
+  // bias of tile t (one wave, 4 bytes per lane = key j0 + lane; keys past the end repeat the last)
+  auto dma_b = [&](int t, int buf) {
+    const bool hist = t >= nt_loc;
+    const int64_t nseg = hist ? a.hist_n : n_loc;
+    int64_t j = tile_j0(t) + lane;
+    j = j < nseg ? j : nseg - 1;
+    __builtin_amdgcn_global_load_lds((const void *)bias_ptr(a, hist, j, head),
+                                     (__attribute__((address_space(3))) void *)bbuf[buf], 4, 0, 0);
+  };
   auto kread = [&](int buf, int i) -> bf16x8 {
     const int kk = i / NB, b = i % NB;
     return *(const bf16x8 *)(kbuf[buf] + kv_off<D>(32 * b + l32, 16 * kk + 8 * hf));
@@ -546,6 +581,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   // prologue: K(0) for everyone; group B then falls one barrier behind
   if (grp == 0) {
     dma_k(0, 0);
+    if (BIAS && wl == 0) dma_b(0, 0);
     ISPA_WAIT_VMCNT(0);
   }
   ISPA_LDS_BARRIER();
@@ -554,10 +590,23 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   for (int i = 0; i <= nt; ++i) {
     // ---- matrix phase: scores of tile i, value product of tile i-1 ----
     if (i < nt) {
+      if constexpr (BIAS) {
+        // the score accumulators start at b / tau instead of 0, so the softmax below sees
+        // tau q.k + b (lane element v of block b is key 32b + 8(v/4) + 4hf + v%4)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sc[b][v] = 0.f;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 x = *(const f32x4 *)(bbuf[i & 1] + 32 * b + 8 * q4 + 4 * hf);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[b][4 * q4 + e] = x[e] * a.bias_to_score;
+          }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sc[b][v] = 0.f;
+      }
       // operands two ahead of the MFMAs
       bf16x8 k0 = kread(i & 1, 0), k1 = kread(i & 1, 1);
 #pragma unroll
@@ -567,7 +616,8 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
         k0 = k1;
         k1 = k2;
       }
-      // keep four operand reads in flight ahead of the MFMAs
+      // keep four operand reads in flight ahead of the MFMAs (the bias reads, if any, go first)
+      if constexpr (BIAS) __builtin_amdgcn_sched_group_barrier(0x100, NB * 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int g = 0; g < NKK * NB / 2 - 2; ++g) {
@@ -597,7 +647,10 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     }
     // copies issued after this phase's LDS reads (see the kernel comment)
     if (grp == 0) {
-      if (i + 1 < nt) dma_k(i + 1, (i + 1) & 1);
+      if (i + 1 < nt) {
+        dma_k(i + 1, (i + 1) & 1);
+        if (BIAS && wl == 0) dma_b(i + 1, (i + 1) & 1);
+      }
       if (i < nt) dma_v(i, i & 1);
     }
     ISPA_LDS_BARRIER();   // copies in flight stay in flight across this barrier
@@ -673,12 +726,13 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
 // ------------------------------------------------------------------------------------------------
 // fp32 kernel: VALU, one query per thread. Same single pass and the same local/history split.
 // ------------------------------------------------------------------------------------------------
-template <int D>
+template <int D, bool BIAS>
 __global__ void __launch_bounds__(128) attn_dual_f32_kernel(AttnArgs a, int n_qt) {
   constexpr int BK = 32;
   constexpr int NT = 128;
   __shared__ float k_lds[BK][D];
   __shared__ float v_lds[BK][D];
+  __shared__ float b_lds[BK];
   const int tid = threadIdx.x;
   const int head = blockIdx.x / n_qt, qt = blockIdx.x % n_qt;
   const int qi = qt * NT + tid;
@@ -727,6 +781,11 @@ __global__ void __launch_bounds__(128) attn_dual_f32_kernel(AttnArgs a, int n_qt
       k_lds[r][c] = row_ptr(hist, j, false)[c];
       v_lds[r][c] = row_ptr(hist, j, true)[c];
     }
+    if (BIAS && tid < BK) {
+      int64_t j = j0 + tid;
+      j = j < nseg ? j : nseg - 1;
+      b_lds[tid] = *bias_ptr(a, hist, j, head) * a.bias_to_score;
+    }
     __syncthreads();
     float s[BK];
     float mx = -INFINITY;
@@ -734,6 +793,7 @@ __global__ void __launch_bounds__(128) attn_dual_f32_kernel(AttnArgs a, int n_qt
       float acc = 0.f;
 #pragma unroll
       for (int c = 0; c < D; ++c) acc = fmaf(q[c], k_lds[r][c], acc);
+      if (BIAS) acc += b_lds[r];
       s[r] = r < n_valid ? acc * a.scale_log2 : -INFINITY;
       mx = fmaxf(mx, s[r]);
     }
@@ -773,39 +833,51 @@ __global__ void __launch_bounds__(128) attn_dual_f32_kernel(AttnArgs a, int n_qt
   }
 }
 
-}  // namespace
-
 #ifndef ISPA_ATTN_PP
 #define ISPA_ATTN_PP 1
 #endif
 
-hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s) {
+template <bool BIAS>
+hipError_t launch_attn_bf16_t(const AttnArgs &a, int head_dim, hipStream_t s) {
   if (ISPA_ATTN_PP && head_dim == 128) {
     const int n_qt = (a.n_q + 255) / 256;
     const int grid = n_qt * a.n_heads;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128>), dim3(grid), dim3(512), 0, s, a, n_qt);
+    hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, BIAS>), dim3(grid), dim3(512), 0, s, a, n_qt);
     return hipGetLastError();
   }
   const int n_qt = (a.n_q + 127) / 128;
   const int grid = n_qt * a.n_heads;
   if (grid == 0) return hipSuccess;
   if (head_dim == 128)
-    hipLaunchKernelGGL((attn_dual_bf16_kernel<128>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
+    hipLaunchKernelGGL((attn_dual_bf16_kernel<128, BIAS>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
   else
-    hipLaunchKernelGGL((attn_dual_bf16_kernel<64>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
+    hipLaunchKernelGGL((attn_dual_bf16_kernel<64, BIAS>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_f32(const AttnArgs &a, int head_dim, hipStream_t s) {
+template <bool BIAS>
+hipError_t launch_attn_f32_t(const AttnArgs &a, int head_dim, hipStream_t s) {
   const int n_qt = (a.n_q + 127) / 128;
   const int grid = n_qt * a.n_heads;
   if (grid == 0) return hipSuccess;
   if (head_dim == 128)
-    hipLaunchKernelGGL((attn_dual_f32_kernel<128>), dim3(grid), dim3(128), 0, s, a, n_qt);
+    hipLaunchKernelGGL((attn_dual_f32_kernel<128, BIAS>), dim3(grid), dim3(128), 0, s, a, n_qt);
   else
-    hipLaunchKernelGGL((attn_dual_f32_kernel<64>), dim3(grid), dim3(128), 0, s, a, n_qt);
+    hipLaunchKernelGGL((attn_dual_f32_kernel<64, BIAS>), dim3(grid), dim3(128), 0, s, a, n_qt);
   return hipGetLastError();
+}
+
+bool has_bias(const AttnArgs &a) { return a.sink_b != nullptr || a.cur_b != nullptr || a.hist_b != nullptr; }
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s) {
+  return has_bias(a) ? launch_attn_bf16_t<true>(a, head_dim, s) : launch_attn_bf16_t<false>(a, head_dim, s);
+}
+
+hipError_t launch_attn_f32(const AttnArgs &a, int head_dim, hipStream_t s) {
+  return has_bias(a) ? launch_attn_f32_t<true>(a, head_dim, s) : launch_attn_f32_t<false>(a, head_dim, s);
 }
 
 }  // namespace ispa

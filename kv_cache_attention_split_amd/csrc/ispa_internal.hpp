@@ -24,9 +24,19 @@ struct AttnArgs {
   float *lse_loc, *lse_hist, *lse_full;
   int32_t n_q, n_heads;
   float scale_log2;                 // softmax_scale * log2(e)
+  // Optional per-key additive logit bias, natural-log units, one pointer per segment (NULL = zero):
+  // key j of segment S in head h gets S_b[h * S_bhs + j]. bias_to_score = 1 / softmax_scale
+  // turns it into raw-score units, so that (q.k + b / tau) * tau = tau q.k + b.
+  const float *sink_b, *cur_b, *hist_b;
+  int64_t sink_bhs, cur_bhs, hist_bhs;
+  float bias_to_score;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s);
+// TempCache merge: per group, mean key and value rows (fp32 sums in member order) and ln(count).
+hipError_t launch_kv_merge(bool bf16, int width, const void *k, const void *v, int64_t n, int64_t in_stride,
+                           const int32_t *offsets, const int32_t *members, int64_t n_groups, void *k_out,
+                           void *v_out, int64_t out_stride, float *bias_out, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, int head_dim, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------------

@@ -1,0 +1,128 @@
+// TempCache exact merge of a cache segment (FAST-AR summary page, section 2 part A "TempCache",
+// Lemma 5.1: a group of identical keys becomes one key whose value is the group's mean value and
+// whose logit is raised by the log of the group size; attention is then unchanged).
+//
+// kv_merge_kernel: one wave per group. The wave walks the group's member rows in the given order
+// (member indices are wave-uniform, so they are scalar loads) and each lane accumulates 8 columns of
+// the key row and 8 of the value row per pass in fp32, 16-byte loads and stores; the mean is one
+// division, rounded once to the output type. The merged rows are written densely in group order, and
+// the group's log-count goes to the bias output that the biased attention reads.
+//
+// The work is a gather of whole rows: bound by HBM bandwidth (every member row read once, every
+// merged row written once), no reuse to stage in LDS.
+#include "ispa_internal.hpp"
+#include "device_common.hpp"
+
+namespace ispa {
+namespace {
+
+constexpr int kWaves = 4;
+
+struct MergeArgs {
+  const void *k, *v;
+  int64_t n, in_stride;
+  const int32_t *offsets, *members;
+  int64_t n_groups;
+  void *k_out, *v_out;
+  int64_t out_stride;
+  float *bias_out;
+  int width;   // elements per row, multiple of 8
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void *base, int64_t elem, float (&x)[8]) {
+  if constexpr (BF16) {
+    const u32x4 u = *(const u32x4 *)((const uint16_t *)base + elem);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __builtin_bit_cast(float, u[e] << 16);
+      x[2 * e + 1] = __builtin_bit_cast(float, u[e] & 0xffff0000u);
+    }
+  } else {
+    const f32x4 a = *(const f32x4 *)((const float *)base + elem);
+    const f32x4 b = *(const f32x4 *)((const float *)base + elem + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[4 + e] = b[e];
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store8(void *base, int64_t elem, const float (&x)[8]) {
+  if constexpr (BF16) {
+    u32x4 u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    *(u32x4 *)((uint16_t *)base + elem) = u;
+  } else {
+    *(f32x4 *)((float *)base + elem) = f32x4{x[0], x[1], x[2], x[3]};
+    *(f32x4 *)((float *)base + elem + 4) = f32x4{x[4], x[5], x[6], x[7]};
+  }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(64 * kWaves) kv_merge_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar member loads
+  const int64_t g = (int64_t)blockIdx.x * kWaves + wave;
+  if (g >= a.n_groups) return;
+  const int32_t m0 = a.offsets[g], m1 = a.offsets[g + 1];
+  const int count = m1 > m0 ? m1 - m0 : 0;
+  if (lane == 0 && a.bias_out != nullptr) a.bias_out[g] = count > 0 ? logf((float)count) : -INFINITY;
+  const float fc = (float)count;
+  for (int c0 = 8 * lane; c0 < a.width; c0 += 8 * 64) {
+    float sk[8], sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
+    for (int32_t m = m0; m < m1; ++m) {
+      const int32_t row = a.members[m];
+      if (row < 0 || row >= a.n) continue;   // never read outside the segment
+      float xk[8], xv[8];
+      load8<BF16>(a.k, (int64_t)row * a.in_stride + c0, xk);
+      load8<BF16>(a.v, (int64_t)row * a.in_stride + c0, xv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sk[e] += xk[e];
+        sv[e] += xv[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sk[e] = count > 0 ? sk[e] / fc : 0.f;
+      sv[e] = count > 0 ? sv[e] / fc : 0.f;
+    }
+    store8<BF16>(a.k_out, g * a.out_stride + c0, sk);
+    store8<BF16>(a.v_out, g * a.out_stride + c0, sv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_merge(bool bf16, int width, const void *k, const void *v, int64_t n, int64_t in_stride,
+                           const int32_t *offsets, const int32_t *members, int64_t n_groups, void *k_out,
+                           void *v_out, int64_t out_stride, float *bias_out, hipStream_t s) {
+  MergeArgs a;
+  a.k = k;
+  a.v = v;
+  a.n = n;
+  a.in_stride = in_stride;
+  a.offsets = offsets;
+  a.members = members;
+  a.n_groups = n_groups;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.out_stride = out_stride;
+  a.bias_out = bias_out;
+  a.width = width;
+  if (n_groups == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_groups + kWaves - 1) / kWaves)), block(64 * kWaves);
+  if (bf16)
+    hipLaunchKernelGGL(kv_merge_kernel<true>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(kv_merge_kernel<false>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ispa

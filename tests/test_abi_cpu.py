@@ -91,6 +91,58 @@ def test_attn_argument_errors(L):
     assert attn(L, n_q=0) == _abi.ISPA_OK
 
 
+def attn_b(L, bias, **kw):
+    sink, cur, hist = kw.get("sink", seg()), kw.get("cur", seg()), kw.get("hist", seg())
+    return L.ispa_attn_dual_biased(1, 2, 128, ctypes.c_float(0.088), FAKE, kw.get("n_q", 32), 256, sink, cur,
+                                   hist, None if bias is None else ctypes.byref(bias), FAKE,
+                                   kw.get("a_full", FAKE2), None, None, None, None)
+
+
+def test_biased_attn_argument_errors(L):
+    B = _abi.KVBias
+    # the plain attention's checks come first
+    assert L.ispa_attn_dual_biased(1, 2, 96, ctypes.c_float(0.088), FAKE, 32, 256, seg(), seg(), seg(),
+                                   None, FAKE, FAKE2, None, None, None, None) == _abi.ISPA_E_UNSUPPORTED
+    assert attn_b(L, B(FAKE, None, None, -1, 0, 0), n_q=0) == _abi.ISPA_E_ARG    # negative head stride
+    assert attn_b(L, B(FAKE + 2, None, None, 0, 0, 0), n_q=0) == _abi.ISPA_E_ARG  # misaligned bias
+    assert attn_b(L, B(None, FAKE, None, 0, 8, 0), n_q=0) == _abi.ISPA_E_ARG     # head stride < n (16)
+    assert attn_b(L, B(None, None, FAKE, 0, 0, 15), n_q=0) == _abi.ISPA_E_ARG
+    # valid layouts: shared (0) or a head stride >= n, per segment; NULL entries; a history bias is
+    # ignored (not checked) when only the local branch is computed; strides of NULL entries are unread
+    assert attn_b(L, None, n_q=0) == _abi.ISPA_OK
+    assert attn_b(L, B(FAKE, FAKE, FAKE, 0, 0, 0), n_q=0) == _abi.ISPA_OK
+    assert attn_b(L, B(FAKE, None, FAKE, 16, -5, 40), n_q=0) == _abi.ISPA_OK
+    assert attn_b(L, B(None, None, FAKE + 2, 0, 0, 3), n_q=0, a_full=None) == _abi.ISPA_OK
+
+
+def test_kv_merge_argument_errors(L):
+    f = L.ispa_kv_merge
+    ok = dict(dt=1, width=256, k=FAKE, v=FAKE2, n=10, in_stride=256, off=FAKE, mem=FAKE2, G=0, ko=FAKE,
+              vo=FAKE2, out_stride=256, bias=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["dt"], a["width"], a["k"], a["v"], a["n"], a["in_stride"], a["off"], a["mem"], a["G"],
+                 a["ko"], a["vo"], a["out_stride"], a["bias"], None)
+    assert call() == _abi.ISPA_OK                          # no groups: no-op
+    assert call(dt=5) == _abi.ISPA_E_UNSUPPORTED
+    assert call(width=260) == _abi.ISPA_E_UNSUPPORTED      # not a multiple of 8
+    assert call(width=0) == _abi.ISPA_E_ARG
+    assert call(n=-1) == _abi.ISPA_E_ARG
+    assert call(G=-1) == _abi.ISPA_E_ARG
+    assert call(G=(1 << 26) + 1) == _abi.ISPA_E_ARG
+    assert call(G=3, off=None) == _abi.ISPA_E_ARG
+    assert call(G=3, off=FAKE + 2) == _abi.ISPA_E_ARG
+    assert call(G=3, k=MISALIGNED) == _abi.ISPA_E_ARG
+    assert call(G=3, mem=None) == _abi.ISPA_E_ARG
+    assert call(G=3, in_stride=248) == _abi.ISPA_E_ARG
+    assert call(G=3, in_stride=260) == _abi.ISPA_E_ARG
+    assert call(G=3, ko=None) == _abi.ISPA_E_ARG
+    assert call(G=3, vo=MISALIGNED) == _abi.ISPA_E_ARG
+    assert call(G=3, out_stride=128) == _abi.ISPA_E_ARG
+    assert call(G=3, bias=FAKE + 1) == _abi.ISPA_E_ARG
+
+
 def test_accumulate_argument_errors(L):
     f = L.ispa_absorb_accumulate
     assert f(1, 100, 100, FAKE, FAKE2, FAKE, FAKE, FAKE, None, 0, None) == _abi.ISPA_E_UNSUPPORTED
