@@ -45,6 +45,8 @@ def parse():
                          "single-pass forms, warm and cold cache) and print one JSON line")
     ap.add_argument("--steady", action="store_true",
                     help="time the steady state after the warmup: L-Layer vs F-Layer chunk at 9/30/60 frames")
+    ap.add_argument("--tempcache", action="store_true",
+                    help="time the TempCache merge and attention over merged vs original history")
     ap.add_argument("--gram-only-cfg", type=int, default=None,
                     help="time only the statistics update of one chunk at workload 3's or 4's width")
     return ap.parse_args()
@@ -250,6 +252,93 @@ def gram_report(cfg, steps, warmup, torch):
           flush=True)
 
 
+def tempcache_report(steps, warmup, torch):
+    """TempCache exact merge (FAST-AR page, section 2 part A, Lemma 5.1) on workload 5's cache shape:
+    12 heads x 128, 4680 queries, sink and current chunk of 4680 keys, a 60-frame history of 1560
+    tokens per frame in which a fraction of token positions is static (the same key in every frame).
+    Reports the merge kernel (time, HBM rate) and attention over the original history against
+    attention over the merged history with its log-count bias; `bias_overhead` is the biased kernel
+    over the original keys (zero bias) against the plain kernel. Inputs are drawn on the device."""
+    import ispa_inputs as inputs
+    import kv_cache_attention_split_amd as ispa
+    wl = inputs.CONFIGS[5]
+    H, dh = wl.n_heads, wl.head_dim
+    n_q = n_sink = n_cur = inputs.CHUNK_TOKENS
+    frames, ft = 60, inputs.FRAME_TOKENS
+    n_hist = frames * ft
+    g = torch.Generator(device="cuda").manual_seed(77)
+
+    def randn(*shape):
+        return torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
+
+    q, sink_k, sink_v, cur_k, cur_v = (randn(n, H, dh) for n in (n_q, n_sink, n_sink, n_cur, n_cur))
+    hist_v = randn(n_hist, H, dh)
+    a_loc = torch.empty((n_q, H * dh), dtype=torch.bfloat16, device="cuda")
+    a_full = torch.empty_like(a_loc)
+    lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
+    zero_bias = torch.zeros(n_hist, dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(5)
+    reports = []
+    for frac in (0.25, 0.5, 0.75):
+        n_static = int(round(frac * ft))
+        static_pos = np.sort(rng.choice(ft, size=n_static, replace=False))
+        is_static = np.zeros(ft, dtype=bool)
+        is_static[static_pos] = True
+        rank = np.cumsum(is_static) - 1
+        tok = np.arange(n_hist)
+        pos = tok % ft
+        labels = np.where(is_static[pos], rank[pos], 0)
+        dyn = ~is_static[pos]
+        labels[dyn] = n_static + np.arange(int(dyn.sum()))
+        off, mem = inputs.csr_from_labels(labels)
+        G = off.size - 1
+        hist_k = randn(n_hist, H, dh)
+        static_keys = randn(n_static, H, dh)
+        sel = torch.from_numpy(np.nonzero(~dyn)[0]).cuda()
+        hist_k[sel] = static_keys[torch.from_numpy(labels[~dyn]).cuda()]
+        off_d, mem_d = torch.from_numpy(off).cuda(), torch.from_numpy(mem).cuda()
+        mk = torch.empty((G, H, dh), dtype=torch.bfloat16, device="cuda")
+        mv = torch.empty_like(mk)
+        mb = torch.empty(G, dtype=torch.float32, device="cuda")
+        calls = {
+            "merge": lambda: ispa.ispa_kv_merge(hist_k, hist_v, off_d, mem_d, mk, mv, mb),
+            "original": lambda: ispa.ispa_attn_dual(q, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v, wl.scale,
+                                                    a_loc, a_full, lse[0], lse[1], lse[2]),
+            "merged": lambda: ispa.ispa_attn_dual_biased(q, sink_k, sink_v, cur_k, cur_v, mk, mv, wl.scale,
+                                                         a_loc, a_full, lse[0], lse[1], lse[2], hist_bias=mb),
+            "biased_same_keys": lambda: ispa.ispa_attn_dual_biased(q, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v,
+                                                                   wl.scale, a_loc, a_full, lse[0], lse[1], lse[2],
+                                                                   hist_bias=zero_bias),
+        }
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            for call in calls.values():
+                call()
+            torch.cuda.synchronize()
+        ms = {k: [] for k in calls}
+        for _ in range(3):
+            for k, call in calls.items():
+                ms[k].append(_time_calls(call, steps, warmup, torch))
+        ms = {k: float(np.median(v)) for k, v in ms.items()}
+        row = H * dh * 2
+        merge_bytes = 2 * n_hist * row + 2 * G * row + 4 * (G + 1) + 4 * n_hist + 4 * G
+        keys_orig = n_sink + n_cur + n_hist
+        keys_merged = n_sink + n_cur + G
+        reports.append({
+            "static_frac": frac, "hist_keys": n_hist, "merged_hist_keys": G,
+            "merge": {"ms": round(ms["merge"], 4), "bytes": merge_bytes,
+                      "gbps": round(merge_bytes / ms["merge"] / 1e6, 1),
+                      "frac_hbm": round(merge_bytes / ms["merge"] / 1e6 / PEAK_HBM_GBS, 4)},
+            "attn_original_ms": round(ms["original"], 4), "attn_merged_ms": round(ms["merged"], 4),
+            "attn_speedup": round(ms["original"] / ms["merged"], 3),
+            "key_ratio": round(keys_orig / keys_merged, 3),
+            "merged_tflops": round(attn_flops(n_q, keys_merged, H, dh) / ms["merged"] / 1e9, 1),
+            "bias_overhead": round(ms["biased_same_keys"] / ms["original"] - 1.0, 4)})
+        del hist_k, static_keys, mk, mv, mb
+    print(json.dumps({"workload": "wan1.3b-long tempcache", "frames": frames, "frame_tokens": ft,
+                      "heads": H, "head_dim": dh, "queries": n_q, "tempcache": reports}), flush=True)
+
+
 def steady_report(steps, warmup, torch):
     """After the warmup (ISPA stage 3): time of one chunk of an L-Layer (local-only attention over sink
     + current chunk, projection with W + dW) against an F-Layer (full attention over the whole cache,
@@ -333,6 +422,9 @@ def main():
         return
     if args.steady:
         steady_report(max(args.steps, 20), max(args.warmup, 5), torch)
+        return
+    if args.tempcache:
+        tempcache_report(max(args.steps, 20), max(args.warmup, 5), torch)
         return
     if args.gram_only_cfg is not None:
         gram_report(args.gram_only_cfg, max(args.steps, 20), max(args.warmup, 5), torch)
