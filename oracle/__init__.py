@@ -17,6 +17,9 @@ the HIP path: it is plain NumPy in float64 (plus pure-Python loops and exact rat
   * `oracle.tempcache`  FAST-AR summary page ("Sintesi Tecnica: FAST-AR"), section 2 part A
     "TempCache", Lemma 5.1: merging duplicate keys (mean values, log group size added to the
     merged key's logit) and softmax attention with a per-key additive logit bias.
+  * `oracle.future`     Future Forcing summary page ("Riepilogo Tecnico: Future Forcing"), section
+    "Componenti Algorithmiche", module 1: importance of cached keys as their mean attention weight
+    under proxy queries of future frames, per-token and hybrid eviction scores.
   * `oracle.brute`      tiny-size brute force (loops, `fractions.Fraction`) used to pin the above.
 
 Every function is pinned by a `-m "not gpu"` test against closed forms, identities fixed by the
@@ -24,4 +27,4 @@ mathematics, textbook routines or brute force. Readings the pages leave open (Gr
 normalisation, the warmup protocol, the key distribution) are fixed by the workload definitions and
 carry no pin from the pages: parity unpinned for those readings only.
 """
-from . import attention, absorb, brute, steady, tempcache  # noqa: F401
+from . import attention, absorb, brute, future, steady, tempcache  # noqa: F401
