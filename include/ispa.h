@@ -152,6 +152,39 @@ ispa_status ispa_kv_merge(ispa_dtype dt, int32_t width, const void *k, const voi
                           float *bias_out, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Future-query importance of cached keys (Future Forcing summary page, "Componenti Algorithmiche",
+ * module 1: keys are scored by the attention weight that proxies of future queries are predicted to
+ * give them, mixed with a historical score by a weight lambda; implementation detail 3: computed
+ * without the full Q K^T matrix). For head h and key j of the cache (sink, then current, then history):
+ *   scores[h * scores_head_stride + j] = (1/n_p) sum_i softmax_j(softmax_scale * q~_i . k_j)
+ * the mean over the n_p proxy queries of the weight each gives key j (a head's scores sum to 1).
+ * Two passes, no score matrix stored: the log-sum-exp of every proxy over all keys, then per-key sums
+ * of exp(softmax_scale * q~_i . k_j - lse_i). Optionally, per token:
+ *   token_score[j] = lambda * mean_h scores[h][j] + (1 - lambda) * hist_token_score[j]
+ * Building the proxies (rotary positions of future frames applied to the mean of past pre-rotary
+ * queries) is the caller's.
+ *
+ *   dt             ISPA_BF16 only (else ISPA_E_UNSUPPORTED)
+ *   n_heads        H >= 1; head_dim d_h in {64, 128}; softmax_scale tau > 0
+ *   q_proxy        [n_p, H, d_h] row stride q_row_stride (>= H*d_h, multiple of 8); n_p >= 1
+ *   sink, cur, hist  key segments as for ispa_attn_dual (only .k, .n, .row_stride are read; .v may be
+ *                  NULL); together at least one key
+ *   scores         out fp32 [H, scores_head_stride], scores_head_stride >= total keys
+ *   lambda, hist_token_score, token_score   token_score (fp32 [total keys]) may be NULL: then no
+ *                  token scores; hist_token_score may be NULL (historical score 0)
+ *   ws             device scratch of at least ispa_future_scores_workspace(H, n_p) bytes
+ * Errors: ISPA_E_ARG (sizes, NULL or misaligned pointers, lambda not finite), ISPA_E_UNSUPPORTED,
+ * ISPA_E_WORKSPACE, ISPA_E_HIP.
+ * ------------------------------------------------------------------------------------------- */
+size_t ispa_future_scores_workspace(int32_t n_heads, int64_t n_p);
+ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                               const void *q_proxy, int64_t n_p, int64_t q_row_stride,
+                               ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                               float *scores, int64_t scores_head_stride,
+                               float lambda, const float *hist_token_score, float *token_score,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Warmup statistics (ISPA page, section 2 stage 2 "Layer Absorb": the closed form needs
  * A_loc^T A_loc and A_loc^T (A_full - A_loc) over the warmup rows; stage 1 says these rows are the
  * warmup chunks' attention outputs).

@@ -17,7 +17,8 @@ from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVBias, KVSegment, l
                    status_string)
 
 __all__ = [
-    "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_absorb_accumulate", "ispa_absorb_accumulate_workspace",
+    "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_future_scores",
+    "ispa_future_scores_workspace", "ispa_absorb_accumulate", "ispa_absorb_accumulate_workspace",
     "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_layer_error",
     "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_apply_delta", "ispa_project",
     "ispa_kv_plan", "ispa_status_string", "ispa_version",
@@ -160,6 +161,47 @@ def ispa_kv_merge(k, v, offsets, members, k_out, v_out, bias_out=None, stream=No
         _ptr(members), n_groups, _ptr(k_out), _ptr(v_out), int(k_out.stride(0)) if n_groups else width,
         _ptr(bias_out), _stream_handle(stream))
     _check(st, "ispa_kv_merge")
+
+
+def ispa_future_scores_workspace(n_heads: int, n_p: int) -> int:
+    return int(lib().ispa_future_scores_workspace(int(n_heads), int(n_p)))
+
+
+def _key_seg(k, n_heads: int, head_dim: int) -> KVSegment:
+    if k is None or k.shape[0] == 0:
+        return KVSegment(None, None, 0, n_heads * head_dim)
+    if k.dim() != 3 or k.shape[1] != n_heads or k.shape[2] != head_dim:
+        raise ValueError(f"keys must be [n, {n_heads}, {head_dim}], got {tuple(k.shape)}")
+    if k.stride(2) != 1 or k.stride(1) != head_dim:
+        raise ValueError("key rows must be contiguous over (H, d_h)")
+    return KVSegment(_ptr(k), None, int(k.shape[0]), int(k.stride(0)))
+
+
+def ispa_future_scores(q_proxy, sink_k, cur_k, hist_k, softmax_scale: float, scores, ws=None,
+                       lam: float = 1.0, hist_token_score=None, token_score=None, stream=None) -> None:
+    """Future-query importance of the cached keys (see ispa_future_scores in include/ispa.h).
+
+    q_proxy: bf16 [n_p, H, d_h]; *_k: bf16 [n, H, d_h] or None; scores: float32 [H, >= total keys]
+    (a view with unit stride over the keys); token_score / hist_token_score: float32 [total] or None.
+    ws: device scratch of ispa_future_scores_workspace(H, n_p) bytes (allocated for the call if None).
+    """
+    n_p, H, dh = (int(x) for x in q_proxy.shape)
+    if q_proxy.stride(2) != 1 or q_proxy.stride(1) != dh:
+        raise ValueError("proxy rows must be contiguous over (H, d_h)")
+    torch = _torch()
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[0] != H or scores.stride(1) != 1:
+        raise ValueError("scores must be float32 [H, n] with unit stride over the keys")
+    for t in (hist_token_score, token_score):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("token scores must be contiguous float32")
+    if ws is None:
+        ws = torch.empty(max(1, ispa_future_scores_workspace(H, n_p)), dtype=torch.uint8, device=q_proxy.device)
+    st = lib().ispa_future_scores(
+        _dtype_code(q_proxy), H, dh, ctypes.c_float(softmax_scale), _ptr(q_proxy), n_p, int(q_proxy.stride(0)),
+        _key_seg(sink_k, H, dh), _key_seg(cur_k, H, dh), _key_seg(hist_k, H, dh), _ptr(scores),
+        int(scores.stride(0)), ctypes.c_float(lam), _ptr(hist_token_score), _ptr(token_score), _ptr(ws),
+        int(ws.numel() * ws.element_size()), _stream_handle(stream))
+    _check(st, "ispa_future_scores")
 
 
 def ispa_absorb_accumulate_workspace(n_rows: int, d: int) -> int:

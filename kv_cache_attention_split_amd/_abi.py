@@ -52,6 +52,9 @@ SIGNATURES = {
                                       KVSegment, ctypes.POINTER(KVBias), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "ispa_kv_merge": (c_int, [c_int, c_i32, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64,
                               c_vp, c_vp]),
+    "ispa_future_scores_workspace": (c_sz, [c_i32, c_i64]),
+    "ispa_future_scores": (c_int, [c_int, c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, KVSegment, KVSegment,
+                                   KVSegment, c_vp, c_i64, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ispa_absorb_accumulate_workspace": (c_sz, [c_i64, c_i32]),
     "ispa_absorb_accumulate": (c_int, [c_int, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ispa_absorb_solve_workspace": (c_sz, [c_i32, c_i32]),

@@ -199,6 +199,76 @@ ispa_status ispa_attn_dual_biased(ispa_dtype dt, int32_t n_heads, int32_t head_d
 }
 
 // ------------------------------------------------------------------------------------------------
+size_t ispa_future_scores_workspace(int32_t n_heads, int64_t n_p) {
+  if (n_heads <= 0 || n_p <= 0) return 0;
+  return (((size_t)n_heads * (size_t)n_p * sizeof(float)) + 255) / 256 * 256;
+}
+
+ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                               const void *q_proxy, int64_t n_p, int64_t q_row_stride,
+                               ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                               float *scores, int64_t scores_head_stride, float lambda,
+                               const float *hist_token_score, float *token_score, void *ws,
+                               size_t ws_bytes, void *stream) {
+  if (dt != ISPA_BF16) return ISPA_E_UNSUPPORTED;
+  if (n_heads <= 0 || n_p <= 0 || n_p > INT32_MAX / 2) return ISPA_E_ARG;
+  if (head_dim != 64 && head_dim != 128) return ISPA_E_UNSUPPORTED;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale) || !std::isfinite(lambda)) return ISPA_E_ARG;
+  const int64_t width = (int64_t)n_heads * head_dim;
+  ispa_kv_segment segs[3] = {sink, cur, hist};
+  int64_t total = 0;
+  for (ispa_kv_segment &sg : segs) {
+    if (sg.n < 0) return ISPA_E_ARG;
+    if (sg.n == 0) continue;
+    if (sg.k == nullptr || !aligned16(sg.k)) return ISPA_E_ARG;
+    if (sg.row_stride < width || sg.row_stride % 8 != 0) return ISPA_E_ARG;
+    if (sg.row_stride >= ((int64_t)1 << 23)) return ISPA_E_UNSUPPORTED;
+    total += sg.n;
+  }
+  if (total < 1 || total > INT32_MAX) return ISPA_E_ARG;
+  if (q_proxy == nullptr || !aligned16(q_proxy) || q_row_stride < width || q_row_stride % 8 != 0)
+    return ISPA_E_ARG;
+  if (scores == nullptr || !aligned4(scores) || scores_head_stride < total) return ISPA_E_ARG;
+  if (token_score != nullptr && !aligned4(token_score)) return ISPA_E_ARG;
+  if (hist_token_score != nullptr && !aligned4(hist_token_score)) return ISPA_E_ARG;
+  if (ws == nullptr || ws_bytes < ispa_future_scores_workspace(n_heads, n_p)) return ISPA_E_WORKSPACE;
+  if (!aligned16(ws)) return ISPA_E_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  float *lse = (float *)ws;
+
+  // pass 1: log-sum-exp of every proxy over all keys (values are not read; the key pointers stand in)
+  AttnArgs a{};
+  const bool local_empty = sink.n + cur.n == 0;
+  a.q = q_proxy;
+  a.q_stride = q_row_stride;
+  a.sink_k = a.sink_v = sink.k;
+  a.sink_n = sink.n;
+  a.sink_stride = sink.row_stride;
+  a.cur_k = a.cur_v = local_empty ? hist.k : cur.k;
+  a.cur_n = local_empty ? hist.n : cur.n;
+  a.cur_stride = local_empty ? hist.row_stride : cur.row_stride;
+  a.hist_k = a.hist_v = local_empty ? nullptr : hist.k;
+  a.hist_n = local_empty ? 0 : hist.n;
+  a.hist_stride = local_empty ? 0 : hist.row_stride;
+  a.lse_full = lse;
+  a.n_q = (int32_t)n_p;
+  a.n_heads = n_heads;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.bias_to_score = 1.0f / softmax_scale;
+  hipError_t e = launch_attn_lse_bf16(a, head_dim, s);
+  if (e != hipSuccess) return hip_status(e);
+  // pass 2: per-key sums of the proxies' weights
+  e = launch_future_colsum_bf16((const uint16_t *)q_proxy, q_row_stride, n_p, lse, (const uint16_t *)sink.k,
+                                sink.row_stride, sink.n, (const uint16_t *)cur.k, cur.row_stride, cur.n,
+                                (const uint16_t *)hist.k, hist.row_stride, hist.n, n_heads, head_dim,
+                                a.scale_log2, scores, scores_head_stride, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (token_score != nullptr)
+    e = launch_token_scores(scores, scores_head_stride, n_heads, total, lambda, hist_token_score, token_score, s);
+  return hip_status(e);
+}
+
+// ------------------------------------------------------------------------------------------------
 ispa_status ispa_kv_merge(ispa_dtype dt, int32_t width, const void *k, const void *v, int64_t n,
                           int64_t in_stride, const int32_t *offsets, const int32_t *members,
                           int64_t n_groups, void *k_out, void *v_out, int64_t out_stride,

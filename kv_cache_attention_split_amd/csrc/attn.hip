@@ -466,7 +466,8 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
 // a full wait while a global->LDS copy is in flight, which would serialise the operand reads. With
 // no copy in flight the reads run four operands ahead of the MFMAs (scheduling groups below).
 // ------------------------------------------------------------------------------------------------
-template <int D, bool BIAS>
+// LSE_ONLY: only the log-sum-exp outputs are wanted (no value copies, no value product, no A rows).
+template <int D, bool BIAS, bool LSE_ONLY = false>
 __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, int n_qt) {
   constexpr int BK = 64;
   constexpr int TB = BK * D * 2;
@@ -567,10 +568,10 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     const float tot = l + swap_halves(l);
     const float inv = 1.0f / tot;
     const float lse = (m + __log2f(tot)) * kLn2;
-    write_rows<D>(o, inv, a.a_loc, qi, n_q, out_stride, head_off, hf);
+    if constexpr (!LSE_ONLY) write_rows<D>(o, inv, a.a_loc, qi, n_q, out_stride, head_off, hf);
     write_lse(a.lse_loc, lse, head, qi, n_q, hf);
     if (nt_hist == 0) {
-      write_rows<D>(o, inv, a.a_full, qi, n_q, out_stride, head_off, hf);
+      if constexpr (!LSE_ONLY) write_rows<D>(o, inv, a.a_full, qi, n_q, out_stride, head_off, hf);
       write_lse(a.lse_full, lse, head, qi, n_q, hf);
       write_lse(a.lse_hist, -INFINITY, head, qi, n_q, hf);
     }
@@ -626,7 +627,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    if (i > 0) {
+    if (!LSE_ONLY && i > 0) {
       bf16x8 v0 = vread(i - 1, 0), v1 = vread(i - 1, 1);
 #pragma unroll
       for (int j = 0; j < NPV; ++j) {
@@ -651,7 +652,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
         dma_k(i + 1, (i + 1) & 1);
         if (BIAS && wl == 0) dma_b(i + 1, (i + 1) & 1);
       }
-      if (i < nt) dma_v(i, i & 1);
+      if (!LSE_ONLY && i < nt) dma_v(i, i & 1);
     }
     ISPA_LDS_BARRIER();   // copies in flight stay in flight across this barrier
     // ---- vector phase: softmax of tile i ----
@@ -717,7 +718,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     const float th = l + swap_halves(l);
     const float tl = l_loc + swap_halves(l_loc);
     const float tot = th + tl;
-    write_rows<D>(o, 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
+    if constexpr (!LSE_ONLY) write_rows<D>(o, 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
     write_lse(a.lse_full, (m + __log2f(tot)) * kLn2, head, qi, n_q, hf);
     write_lse(a.lse_hist, th > 0.f ? (m + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
   }
@@ -871,6 +872,18 @@ hipError_t launch_attn_f32_t(const AttnArgs &a, int head_dim, hipStream_t s) {
 bool has_bias(const AttnArgs &a) { return a.sink_b != nullptr || a.cur_b != nullptr || a.hist_b != nullptr; }
 
 }  // namespace
+
+hipError_t launch_attn_lse_bf16(const AttnArgs &a, int head_dim, hipStream_t s) {
+  if (has_bias(a) || a.a_loc != nullptr || a.a_full != nullptr) return hipErrorInvalidValue;
+  if (ISPA_ATTN_PP && head_dim == 128) {
+    const int n_qt = (a.n_q + 255) / 256;
+    const int grid = n_qt * a.n_heads;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, true>), dim3(grid), dim3(512), 0, s, a, n_qt);
+    return hipGetLastError();
+  }
+  return launch_attn_bf16_t<false>(a, head_dim, s);   // rows are not stored (NULL outputs)
+}
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s) {
   return has_bias(a) ? launch_attn_bf16_t<true>(a, head_dim, s) : launch_attn_bf16_t<false>(a, head_dim, s);

@@ -33,6 +33,17 @@ struct AttnArgs {
 };
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s);
+// Log-sum-exp rows only (a.a_loc and a.a_full must be NULL, no bias): no value copies or products.
+hipError_t launch_attn_lse_bf16(const AttnArgs &a, int head_dim, hipStream_t s);
+// Future-query importance: score[h][j] = (1/n_p) sum_i exp(tau q_i . k_j - lse[h][i]) over the keys
+// of three segments in cache order (bf16 keys and proxies, head_dim 64 or 128).
+hipError_t launch_future_colsum_bf16(const uint16_t *q, int64_t q_stride, int64_t n_p, const float *lse,
+                                     const uint16_t *k0, int64_t s0, int64_t n0, const uint16_t *k1,
+                                     int64_t s1, int64_t n1, const uint16_t *k2, int64_t s2, int64_t n2,
+                                     int n_heads, int head_dim, float scale_log2, float *scores,
+                                     int64_t scores_hs, hipStream_t s);
+hipError_t launch_token_scores(const float *scores, int64_t hs, int n_heads, int64_t n, float lambda,
+                               const float *hist, float *token, hipStream_t s);
 // TempCache merge: per group, mean key and value rows (fp32 sums in member order) and ln(count).
 hipError_t launch_kv_merge(bool bf16, int width, const void *k, const void *v, int64_t n, int64_t in_stride,
                            const int32_t *offsets, const int32_t *members, int64_t n_groups, void *k_out,

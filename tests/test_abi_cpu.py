@@ -143,6 +143,37 @@ def test_kv_merge_argument_errors(L):
     assert call(G=3, bias=FAKE + 1) == _abi.ISPA_E_ARG
 
 
+def test_future_scores_argument_errors(L):
+    f = L.ispa_future_scores
+    base = dict(dt=1, H=2, dh=128, scale=0.088, q=FAKE, n_p=10, q_stride=256, sink=seg(n=8), cur=seg(n=8),
+                hist=seg(n=16), scores=FAKE2, shs=32, lam=0.5, hist_tok=None, tok=None, ws=FAKE, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["dt"], a["H"], a["dh"], ctypes.c_float(a["scale"]), a["q"], a["n_p"], a["q_stride"], a["sink"],
+                 a["cur"], a["hist"], a["scores"], a["shs"], ctypes.c_float(a["lam"]), a["hist_tok"], a["tok"],
+                 a["ws"], a["ws_bytes"], None)
+    assert call(dt=0) == _abi.ISPA_E_UNSUPPORTED                  # bf16 only
+    assert call(dh=96) == _abi.ISPA_E_UNSUPPORTED
+    assert call(H=0) == _abi.ISPA_E_ARG
+    assert call(n_p=0) == _abi.ISPA_E_ARG                          # no proxies: no mean
+    assert call(scale=0.0) == _abi.ISPA_E_ARG
+    assert call(lam=float("inf")) == _abi.ISPA_E_ARG
+    assert call(sink=seg(n=0), cur=seg(n=0), hist=seg(n=0)) == _abi.ISPA_E_ARG   # no keys
+    assert call(hist=seg(k=MISALIGNED, n=16)) == _abi.ISPA_E_ARG
+    assert call(cur=seg(stride=260, n=8)) == _abi.ISPA_E_ARG
+    assert call(sink=seg(stride=1 << 23, n=8)) == _abi.ISPA_E_UNSUPPORTED
+    assert call(q=MISALIGNED) == _abi.ISPA_E_ARG
+    assert call(q_stride=128) == _abi.ISPA_E_ARG
+    assert call(scores=None) == _abi.ISPA_E_ARG
+    assert call(shs=31) == _abi.ISPA_E_ARG                         # head stride below the 32 keys
+    assert call(tok=FAKE + 2) == _abi.ISPA_E_ARG
+    assert call(ws=None) == _abi.ISPA_E_WORKSPACE
+    assert call(ws_bytes=L.ispa_future_scores_workspace(2, 10) - 1) == _abi.ISPA_E_WORKSPACE
+    assert L.ispa_future_scores_workspace(2, 10) == 256
+    assert L.ispa_future_scores_workspace(12, 4680) == (12 * 4680 * 4 + 255) // 256 * 256
+
+
 def test_accumulate_argument_errors(L):
     f = L.ispa_absorb_accumulate
     assert f(1, 100, 100, FAKE, FAKE2, FAKE, FAKE, FAKE, None, 0, None) == _abi.ISPA_E_UNSUPPORTED
