@@ -45,6 +45,8 @@ def parse():
                          "single-pass forms, warm and cold cache) and print one JSON line")
     ap.add_argument("--steady", action="store_true",
                     help="time the steady state after the warmup: L-Layer vs F-Layer chunk at 9/30/60 frames")
+    ap.add_argument("--future", action="store_true",
+                    help="time the future-query importance scores over workload 5's cache")
     ap.add_argument("--tempcache", action="store_true",
                     help="time the TempCache merge and attention over merged vs original history")
     ap.add_argument("--gram-only-cfg", type=int, default=None,
@@ -339,6 +341,45 @@ def tempcache_report(steps, warmup, torch):
                       "heads": H, "head_dim": dh, "queries": n_q, "tempcache": reports}), flush=True)
 
 
+def future_report(steps, warmup, torch):
+    """Future-query importance of every cached key (Future Forcing page, module 1) on workload 5's
+    cache: 12 heads x 128, 4680 sink + 4680 current + 93,600 history keys, proxies of one future
+    chunk (4680 queries, 3 frames) or one frame (1560). Two passes (proxy log-sum-exp, then per-key
+    sums); each does the 2 n_p n_k d_h FLOP of Q~ K^T per head and n_p n_k exponentials."""
+    import ispa_inputs as inputs
+    import kv_cache_attention_split_amd as ispa
+    wl = inputs.CONFIGS[5]
+    H, dh = wl.n_heads, wl.head_dim
+    n_sink = n_cur = inputs.CHUNK_TOKENS
+    n_hist = 60 * inputs.FRAME_TOKENS
+    n_keys = n_sink + n_cur + n_hist
+    g = torch.Generator(device="cuda").manual_seed(91)
+
+    def randn(*shape):
+        return torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16)
+
+    sink_k, cur_k, hist_k = randn(n_sink, H, dh), randn(n_cur, H, dh), randn(n_hist, H, dh)
+    scores = torch.empty((H, n_keys), dtype=torch.float32, device="cuda")
+    token = torch.empty(n_keys, dtype=torch.float32, device="cuda")
+    out = []
+    for n_p in (inputs.CHUNK_TOKENS, inputs.FRAME_TOKENS):
+        q = randn(n_p, H, dh)
+        ws = torch.empty(ispa.ispa_future_scores_workspace(H, n_p), dtype=torch.uint8, device="cuda")
+        call = lambda: ispa.ispa_future_scores(q, sink_k, cur_k, hist_k, wl.scale, scores, ws, lam=0.5,   # noqa: E731
+                                               token_score=token)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            call()
+            torch.cuda.synchronize()
+        ms = float(np.median([_time_calls(call, steps, warmup, torch) for _ in range(3)]))
+        fl = 2 * 2.0 * n_p * n_keys * dh * H          # Q~ K^T in both passes
+        out.append({"proxies": n_p, "keys": n_keys, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                    "frac_mfma": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                    "gexp_per_s": round(2.0 * n_p * n_keys * H / ms / 1e6, 1)})
+    print(json.dumps({"workload": "wan1.3b-long future scores", "heads": H, "head_dim": dh, "future": out}),
+          flush=True)
+
+
 def steady_report(steps, warmup, torch):
     """After the warmup (ISPA stage 3): time of one chunk of an L-Layer (local-only attention over sink
     + current chunk, projection with W + dW) against an F-Layer (full attention over the whole cache,
@@ -422,6 +463,9 @@ def main():
         return
     if args.steady:
         steady_report(max(args.steps, 20), max(args.warmup, 5), torch)
+        return
+    if args.future:
+        future_report(max(args.steps, 20), max(args.warmup, 5), torch)
         return
     if args.tempcache:
         tempcache_report(max(args.steps, 20), max(args.warmup, 5), torch)
