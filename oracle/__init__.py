@@ -20,6 +20,8 @@ the HIP path: it is plain NumPy in float64 (plus pure-Python loops and exact rat
   * `oracle.future`     Future Forcing summary page ("Riepilogo Tecnico: Future Forcing"), section
     "Componenti Algorithmiche", module 1: importance of cached keys as their mean attention weight
     under proxy queries of future frames, per-token and hybrid eviction scores.
+  * `oracle.fp8`        section 4 "Experimental Results" (ISPA combined with W8A8 quantisation): the
+    OCP E4M3 encoding, per-head scaling, and attention scores from dequantised e4m3 Q and K.
   * `oracle.brute`      tiny-size brute force (loops, `fractions.Fraction`) used to pin the above.
 
 Every function is pinned by a `-m "not gpu"` test against closed forms, identities fixed by the
@@ -27,4 +29,4 @@ mathematics, textbook routines or brute force. Readings the pages leave open (Gr
 normalisation, the warmup protocol, the key distribution) are fixed by the workload definitions and
 carry no pin from the pages: parity unpinned for those readings only.
 """
-from . import attention, absorb, brute, future, steady, tempcache  # noqa: F401
+from . import attention, absorb, brute, fp8, future, steady, tempcache  # noqa: F401

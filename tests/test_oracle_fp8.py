@@ -1,0 +1,101 @@
+"""Pins for the FP8 (e4m3) oracle (CPU only).
+
+The encoding is pinned to the OCP E4M3 definition by hand-decoded codes (zero, one, the largest
+finite, the smallest normal and subnormal, NaN), by round trips over all finite codes, by an
+exhaustive nearest-value search with ties to the even code, and by saturation cases; the per-head
+scaling recipe by its defining property (a head's largest magnitude maps to 448); the FP8 attention
+oracle by inputs that e4m3 holds exactly, where it must equal the plain attention oracle.
+"""
+import numpy as np
+import pytest
+
+import ispa_inputs as inputs
+from oracle import attention as oatt
+from oracle import fp8
+
+
+@pytest.mark.parametrize("code,value", [(0x00, 0.0), (0x38, 1.0), (0xB8, -1.0), (0x3C, 1.5), (0x40, 2.0),
+                                        (0x7E, 448.0), (0xFE, -448.0), (0x08, 2.0 ** -6), (0x01, 2.0 ** -9),
+                                        (0x07, 7 * 2.0 ** -9), (0x0F, 1.875 * 2.0 ** -6), (0x30, 0.5), (0x28, 0.25)])
+def test_decode_hand_cases(code, value):
+    assert fp8.e4m3_decode(np.array([code], dtype=np.uint8))[0] == value
+
+
+def test_decode_specials_and_order():
+    allc = np.arange(256, dtype=np.uint8)
+    v = fp8.e4m3_decode(allc)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.sum(np.isfinite(v)) == 254
+    assert np.signbit(v[0x80]) and v[0x80] == 0.0
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)                          # codes 0x00..0x7E ascend
+    np.testing.assert_array_equal(v[0x80:0xFF], -pos)        # the sign bit only flips the sign
+
+
+def test_round_trip_all_finite_codes():
+    allc = np.arange(256, dtype=np.uint8)
+    fin = np.isfinite(fp8.e4m3_decode(allc))
+    codes = allc[fin]
+    np.testing.assert_array_equal(fp8.e4m3_encode(fp8.e4m3_decode(codes)), codes)
+
+
+def test_nearest_value_brute_force():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(20000) * np.exp2(rng.uniform(-12, 9, 20000))
+    allc = np.arange(256, dtype=np.uint8)
+    vals = fp8.e4m3_decode(allc)
+    fin = np.isfinite(vals)
+    fc, fv = allc[fin], vals[fin]
+    got = fp8.e4m3_encode(x)
+    for xi, gi in zip(x[:4000], got[:4000]):
+        xs = np.clip(xi, -448.0, 448.0)
+        d = np.abs(fv - xs)
+        best = np.nonzero(d == d.min())[0]
+        cands = fc[best]
+        if len(cands) > 1:                       # a tie: the even code; +0 and -0 tie for 0
+            cands = cands[(cands & 1) == 0] if np.any((cands & 1) == 0) else cands
+            cands = cands[np.signbit(fp8.e4m3_decode(cands)) == np.signbit(xi)] if len(cands) > 1 else cands
+        assert gi in cands, (xi, gi, cands)
+
+
+def test_ties_and_saturation():
+    enc = lambda v: int(fp8.e4m3_encode(np.array([v]))[0])   # noqa: E731
+    assert enc(1.0625) == 0x38                   # between 1 (0x38) and 1.125 (0x39): even
+    assert enc(1.1875) == 0x3A                   # between 1.125 (0x39) and 1.25 (0x3A): even
+    assert enc(-1.0625) == 0xB8
+    assert enc(460.0) == 0x7E and enc(1e6) == 0x7E and enc(-1e6) == 0xFE and enc(np.inf) == 0x7E
+    assert enc(np.nan) == 0x7F
+    assert enc(-0.0) == 0x80 and enc(0.0) == 0x00
+    assert enc(2.0 ** -10) == 0x00               # half the smallest subnormal: tie to the even code 0
+    assert enc(1.5 * 2.0 ** -9) == 0x02          # between 0x01 and 0x02: even
+
+
+def test_head_scales_map_absmax_to_448():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal((50, 3, 16)) * np.array([0.1, 3.0, 40.0])[None, :, None]).astype(np.float32)
+    x[:, 2] = 0.0                                # an all-zero head keeps scale 1
+    s = fp8.head_scales(x)
+    assert s[2] == np.float32(1.0)
+    codes = fp8.quantize(x, s)
+    for h in range(2):
+        i = np.unravel_index(np.argmax(np.abs(x[:, h])), x[:, h].shape)
+        assert codes[i[0], h, i[1]] & 0x7F == 0x7E
+    assert np.all(codes[:, 2] & 0x7F == 0)
+    # dequantised values are within half an e4m3 step (2^-4 relative) of the originals
+    d = fp8.dequantize(codes, s)
+    assert np.all(np.abs(d - x) <= 2.0 ** -4 * np.abs(x) + 2.0 ** -9 * s[None, :, None])
+
+
+def test_fp8_attention_equals_plain_on_exact_inputs():
+    # small integers times powers of two are exact in e4m3: with scale 1 the FP8 scores are exact
+    rng = np.random.default_rng(3)
+    inp = inputs.attention_case(4, n_heads=2, head_dim=16, n_q=12, n_sink=4, n_cur=9, n_hist=11)
+    q = rng.integers(-3, 4, size=inp["q"].shape) * 0.5
+    ks = {n: rng.integers(-3, 4, size=inp[n + "_k"].shape) * 0.25 for n in ("sink", "cur", "hist")}
+    ones = np.ones(2, dtype=np.float32)
+    qc = fp8.quantize(q, ones)
+    kc = {n: fp8.quantize(v, ones) for n, v in ks.items()}
+    got = fp8.dual_stream_fp8(inp, qc, ones, kc, ones)
+    plain = oatt.dual_stream(dict(inp, q=q, sink_k=ks["sink"], cur_k=ks["cur"], hist_k=ks["hist"]))
+    for k in ("A_loc", "A_full", "lse_loc", "lse_hist", "lse_full"):
+        np.testing.assert_array_equal(got[k], plain[k])
