@@ -152,6 +152,41 @@ ispa_status ispa_kv_merge(ispa_dtype dt, int32_t width, const void *k, const voi
                           float *bias_out, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * FP8 attention scores (ISPA page, section 4 "Experimental Results": ISPA is paired with W8A8
+ * quantisation for its largest speed-up; the page gives no recipe). Queries and keys are stored as
+ * OCP FP8 E4M3 bytes with one fp32 scale per head (scale = absmax / 448, value = e4m3 * scale); the
+ * scores run on the FP8 matrix cores with fp32 accumulation, values, probabilities and outputs stay
+ * bf16. Otherwise exactly ispa_attn_dual: A_loc, A_full and the three LSE rows of the dequantised
+ * queries and keys.
+ *
+ * ispa_fp8_head_scales: scales[h] = max over rows and channels of |x[:, h, :]| / 448 (1 if all zero).
+ * ispa_fp8_quantize:   out[r][h*d_h + c] = e4m3(fp32(x[r][h][c] * fp32(1 / scales[h]))), round to
+ *                      nearest even, magnitudes beyond 448 saturate.
+ *   dt             ISPA_BF16 or ISPA_F32 (type of x); x [n, H, d_h] row stride row_stride (>= H*d_h,
+ *                  multiple of 8 elements), 16-byte aligned; n >= 0; d_h in {64, 128}
+ *   scales         device fp32 [H] (out for head_scales, in for quantize)
+ *   out            device uint8 [n, out_row_stride], out_row_stride >= H*d_h, multiple of 8
+ *
+ * ispa_attn_dual_fp8: as ispa_attn_dual with dt = ISPA_BF16 except
+ *   q              e4m3 bytes [n_q, H, d_h], row stride q_row_stride (bytes, multiple of 16)
+ *   q_scale, k_scale  device fp32 [H]: the scales of q and of every key of the cache
+ *   sink, cur, hist  .k e4m3 bytes, .v bf16, both with row stride .row_stride (in elements of each,
+ *                  multiple of 16, < 2^23)
+ *   head_dim       128 only (else ISPA_E_UNSUPPORTED)
+ * Errors as for ispa_attn_dual.
+ * ------------------------------------------------------------------------------------------- */
+ispa_status ispa_fp8_head_scales(ispa_dtype dt, const void *x, int64_t n, int32_t n_heads, int32_t head_dim,
+                                 int64_t row_stride, float *scales, void *stream);
+ispa_status ispa_fp8_quantize(ispa_dtype dt, const void *x, int64_t n, int32_t n_heads, int32_t head_dim,
+                              int64_t row_stride, const float *scales, uint8_t *out, int64_t out_row_stride,
+                              void *stream);
+ispa_status ispa_attn_dual_fp8(int32_t n_heads, int32_t head_dim, float softmax_scale,
+                               const uint8_t *q, int64_t n_q, int64_t q_row_stride, const float *q_scale,
+                               ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                               const float *k_scale, void *a_loc, void *a_full,
+                               float *lse_loc, float *lse_hist, float *lse_full, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Future-query importance of cached keys (Future Forcing summary page, "Componenti Algorithmiche",
  * module 1: keys are scored by the attention weight that proxies of future queries are predicted to
  * give them, mixed with a historical score by a weight lambda; implementation detail 3: computed

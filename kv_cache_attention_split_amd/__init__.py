@@ -18,7 +18,8 @@ from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVBias, KVSegment, l
 
 __all__ = [
     "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_future_scores",
-    "ispa_future_scores_workspace", "ispa_absorb_accumulate", "ispa_absorb_accumulate_workspace",
+    "ispa_future_scores_workspace", "ispa_fp8_head_scales", "ispa_fp8_quantize", "ispa_attn_dual_fp8",
+    "ispa_absorb_accumulate", "ispa_absorb_accumulate_workspace",
     "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_layer_error",
     "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_apply_delta", "ispa_project",
     "ispa_kv_plan", "ispa_status_string", "ispa_version",
@@ -161,6 +162,59 @@ def ispa_kv_merge(k, v, offsets, members, k_out, v_out, bias_out=None, stream=No
         _ptr(members), n_groups, _ptr(k_out), _ptr(v_out), int(k_out.stride(0)) if n_groups else width,
         _ptr(bias_out), _stream_handle(stream))
     _check(st, "ispa_kv_merge")
+
+
+def _rows3(x):
+    if x.dim() != 3 or x.stride(2) != 1 or x.stride(1) != x.shape[2]:
+        raise ValueError("rows must be [n, H, d_h], contiguous over (H, d_h)")
+    return int(x.shape[0]), int(x.shape[1]), int(x.shape[2]), int(x.stride(0))
+
+
+def ispa_fp8_head_scales(x, scales, stream=None) -> None:
+    """scales[h] = max |x[:, h, :]| / 448 (1 for an all-zero head); x bf16/fp32 [n, H, d_h]."""
+    n, H, dh, st = _rows3(x)
+    if tuple(scales.shape) != (H,) or scales.dtype != _torch().float32:
+        raise ValueError("scales must be float32 [H]")
+    s = lib().ispa_fp8_head_scales(_dtype_code(x), _ptr(x), n, H, dh, st, _ptr(scales), _stream_handle(stream))
+    _check(s, "ispa_fp8_head_scales")
+
+
+def ispa_fp8_quantize(x, scales, out, stream=None) -> None:
+    """out = e4m3 codes of x / scales (per head), uint8 [n, H, d_h] with contiguous rows."""
+    n, H, dh, st = _rows3(x)
+    torch = _torch()
+    if out.dtype != torch.uint8 or tuple(out.shape) != (n, H, dh) or out.stride(2) != 1 or out.stride(1) != dh:
+        raise ValueError("out must be uint8 [n, H, d_h] with contiguous rows")
+    s = lib().ispa_fp8_quantize(_dtype_code(x), _ptr(x), n, H, dh, st, _ptr(scales), _ptr(out),
+                                int(out.stride(0)) if n else H * dh, _stream_handle(stream))
+    _check(s, "ispa_fp8_quantize")
+
+
+def _seg_fp8(k, v, n_heads: int, head_dim: int) -> KVSegment:
+    if k is None or k.shape[0] == 0:
+        return KVSegment(None, None, 0, n_heads * head_dim)
+    for t in (k, v):
+        if t.dim() != 3 or t.shape[1] != n_heads or t.shape[2] != head_dim or t.stride(2) != 1 or \
+                t.stride(1) != head_dim:
+            raise ValueError("K/V segment must be [n, H, d_h] with contiguous rows")
+    if k.shape[0] != v.shape[0] or k.stride(0) != v.stride(0):
+        raise ValueError("K (e4m3) and V (bf16) of a segment must have the same rows and row stride")
+    return KVSegment(_ptr(k), _ptr(v), int(k.shape[0]), int(k.stride(0)))
+
+
+def ispa_attn_dual_fp8(q, q_scale, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v, k_scale, softmax_scale: float,
+                       a_loc, a_full=None, lse_loc=None, lse_hist=None, lse_full=None, stream=None) -> None:
+    """Dual-stream attention with e4m3 q and keys (uint8 codes, float32 per-head scales) and bf16 values
+    (see ispa_attn_dual_fp8 in include/ispa.h)."""
+    n_q, H, dh = (int(x) for x in q.shape)
+    if q.stride(2) != 1 or q.stride(1) != dh:
+        raise ValueError("q rows must be contiguous over (H, d_h)")
+    st = lib().ispa_attn_dual_fp8(
+        H, dh, ctypes.c_float(softmax_scale), _ptr(q), n_q, int(q.stride(0)), _ptr(q_scale),
+        _seg_fp8(sink_k, sink_v, H, dh), _seg_fp8(cur_k, cur_v, H, dh), _seg_fp8(hist_k, hist_v, H, dh),
+        _ptr(k_scale), _ptr(a_loc), _ptr(a_full), _ptr(lse_loc), _ptr(lse_hist), _ptr(lse_full),
+        _stream_handle(stream))
+    _check(st, "ispa_attn_dual_fp8")
 
 
 def ispa_future_scores_workspace(n_heads: int, n_p: int) -> int:

@@ -52,6 +52,10 @@ SIGNATURES = {
                                       KVSegment, ctypes.POINTER(KVBias), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "ispa_kv_merge": (c_int, [c_int, c_i32, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64,
                               c_vp, c_vp]),
+    "ispa_fp8_head_scales": (c_int, [c_int, c_vp, c_i64, c_i32, c_i32, c_i64, c_vp, c_vp]),
+    "ispa_fp8_quantize": (c_int, [c_int, c_vp, c_i64, c_i32, c_i32, c_i64, c_vp, c_vp, c_i64, c_vp]),
+    "ispa_attn_dual_fp8": (c_int, [c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, c_vp, KVSegment, KVSegment, KVSegment,
+                                   c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "ispa_future_scores_workspace": (c_sz, [c_i32, c_i64]),
     "ispa_future_scores": (c_int, [c_int, c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, KVSegment, KVSegment,
                                    KVSegment, c_vp, c_i64, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),

@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libispa.so")
 ARCH = os.environ.get("ISPA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["attn.hip", "gram.hip", "linalg.hip", "steady.hip", "tempcache.hip", "future.hip", "api.cpp"]
+SOURCES = ["attn.hip", "gram.hip", "linalg.hip", "steady.hip", "tempcache.hip", "future.hip", "fp8.hip", "api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -199,6 +199,98 @@ ispa_status ispa_attn_dual_biased(ispa_dtype dt, int32_t n_heads, int32_t head_d
 }
 
 // ------------------------------------------------------------------------------------------------
+namespace {
+ispa_status check_fp8_rows(ispa_dtype dt, const void *x, int64_t n, int32_t n_heads, int32_t head_dim,
+                           int64_t row_stride) {
+  if (dt != ISPA_BF16 && dt != ISPA_F32) return ISPA_E_UNSUPPORTED;
+  if (n < 0 || n_heads <= 0) return ISPA_E_ARG;
+  if (head_dim != 64 && head_dim != 128) return ISPA_E_UNSUPPORTED;
+  if (n > 0 && (x == nullptr || !aligned16(x) || row_stride < (int64_t)n_heads * head_dim || row_stride % 8 != 0))
+    return ISPA_E_ARG;
+  if (n > INT32_MAX) return ISPA_E_ARG;
+  return ISPA_OK;
+}
+}  // namespace
+
+ispa_status ispa_fp8_head_scales(ispa_dtype dt, const void *x, int64_t n, int32_t n_heads, int32_t head_dim,
+                                 int64_t row_stride, float *scales, void *stream) {
+  ispa_status st = check_fp8_rows(dt, x, n, n_heads, head_dim, row_stride);
+  if (st != ISPA_OK) return st;
+  if (scales == nullptr || !aligned4(scales)) return ISPA_E_ARG;
+  return hip_status(launch_fp8_head_scales(dt == ISPA_BF16, x, n, n_heads, head_dim, row_stride, scales,
+                                           (hipStream_t)stream));
+}
+
+ispa_status ispa_fp8_quantize(ispa_dtype dt, const void *x, int64_t n, int32_t n_heads, int32_t head_dim,
+                              int64_t row_stride, const float *scales, uint8_t *out, int64_t out_row_stride,
+                              void *stream) {
+  ispa_status st = check_fp8_rows(dt, x, n, n_heads, head_dim, row_stride);
+  if (st != ISPA_OK) return st;
+  if (n == 0) return ISPA_OK;
+  if (scales == nullptr || !aligned4(scales)) return ISPA_E_ARG;
+  if (out == nullptr || ((uintptr_t)out & 7) != 0 || out_row_stride < (int64_t)n_heads * head_dim ||
+      out_row_stride % 8 != 0)
+    return ISPA_E_ARG;
+  return hip_status(launch_fp8_quantize(dt == ISPA_BF16, x, n, n_heads, head_dim, row_stride, scales, out,
+                                        out_row_stride, (hipStream_t)stream));
+}
+
+ispa_status ispa_attn_dual_fp8(int32_t n_heads, int32_t head_dim, float softmax_scale, const uint8_t *q, int64_t n_q,
+                               int64_t q_row_stride, const float *q_scale, ispa_kv_segment sink, ispa_kv_segment cur,
+                               ispa_kv_segment hist, const float *k_scale, void *a_loc, void *a_full,
+                               float *lse_loc, float *lse_hist, float *lse_full, void *stream) {
+  if (n_heads <= 0 || n_q < 0) return ISPA_E_ARG;
+  if (head_dim != 128) return ISPA_E_UNSUPPORTED;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return ISPA_E_ARG;
+  if (n_q > INT32_MAX / 2) return ISPA_E_ARG;
+  const int64_t width = (int64_t)n_heads * head_dim;
+  if (sink.n < 0 || cur.n < 0 || hist.n < 0) return ISPA_E_ARG;
+  if (sink.n + cur.n < 1) return ISPA_E_ARG;
+  const bool want_full = a_full != nullptr;
+  ispa_kv_segment segs[3] = {sink, cur, hist};
+  for (int i = 0; i < 3; ++i) {
+    const ispa_kv_segment &sg = segs[i];
+    if (i == 2 && !want_full) break;
+    if (sg.n == 0) continue;
+    if (sg.k == nullptr || sg.v == nullptr || !aligned16(sg.k) || !aligned16(sg.v)) return ISPA_E_ARG;
+    if (sg.row_stride < width || sg.row_stride % 16 != 0) return ISPA_E_ARG;
+    if (sg.row_stride >= ((int64_t)1 << 23)) return ISPA_E_UNSUPPORTED;
+  }
+  if (n_q == 0) return ISPA_OK;
+  if (q == nullptr || !aligned16(q) || q_row_stride < width || q_row_stride % 16 != 0) return ISPA_E_ARG;
+  if (q_scale == nullptr || k_scale == nullptr || !aligned4(q_scale) || !aligned4(k_scale)) return ISPA_E_ARG;
+  if (a_loc == nullptr || !aligned16(a_loc)) return ISPA_E_ARG;
+  if (a_full != nullptr && !aligned16(a_full)) return ISPA_E_ARG;
+  AttnArgs a{};
+  a.q = q;
+  a.q_stride = q_row_stride;
+  a.sink_k = sink.k;
+  a.sink_v = sink.v;
+  a.sink_n = sink.n;
+  a.sink_stride = sink.row_stride;
+  a.cur_k = cur.k;
+  a.cur_v = cur.v;
+  a.cur_n = cur.n;
+  a.cur_stride = cur.row_stride;
+  a.hist_k = want_full ? hist.k : nullptr;
+  a.hist_v = want_full ? hist.v : nullptr;
+  a.hist_n = want_full ? hist.n : 0;
+  a.hist_stride = want_full ? hist.row_stride : 0;
+  a.a_loc = a_loc;
+  a.a_full = a_full;
+  a.lse_loc = lse_loc;
+  a.lse_hist = want_full ? lse_hist : nullptr;
+  a.lse_full = want_full ? lse_full : nullptr;
+  a.n_q = (int32_t)n_q;
+  a.n_heads = n_heads;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.bias_to_score = 1.0f / softmax_scale;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  return hip_status(launch_attn_fp8(a, head_dim, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------------------------------------
 size_t ispa_future_scores_workspace(int32_t n_heads, int64_t n_p) {
   if (n_heads <= 0 || n_p <= 0) return 0;
   return (((size_t)n_heads * (size_t)n_p * sizeof(float)) + 255) / 256 * 256;

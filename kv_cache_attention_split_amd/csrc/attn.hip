@@ -121,6 +121,33 @@ __device__ __forceinline__ void dma_tile(const SegRun &run, int64_t j0, int head
   }
 }
 
+// e4m3 key tile: row r holds D bytes; its 16-byte chunk c is stored at c ^ ((r / 2) mod 8), so the 16
+// rows of one operand read (same chunk) spread over the 16 bank groups. Each wave instruction fills
+// 1 KiB (1024 / D rows); `rr`, `cc` = the lane's row and source byte offset, fixed per instruction.
+template <int D>
+__device__ __forceinline__ int k8_off(int r, int byte) {
+  return r * D + ((((byte >> 4) ^ ((r >> 1) & 7))) << 4) + (byte & 15);
+}
+template <int D, int BK>
+__device__ __forceinline__ void dma_tile_k8(const AttnArgs &a, bool hist, int64_t j0, int head_off, uint8_t *lds_tile,
+                                            int w, const int (&rr)[BK * D / 4096], const int (&cc)[BK * D / 4096]) {
+  constexpr int NW = BK * D / 4096;
+  const uint8_t *k0 = (const uint8_t *)(hist ? a.hist_k : a.sink_k);
+  const uint8_t *k1 = (const uint8_t *)(hist ? a.hist_k : a.cur_k);
+  const int64_t s0 = hist ? a.hist_stride : a.sink_stride, s1 = hist ? a.hist_stride : a.cur_stride;
+  const int64_t n = hist ? a.hist_n : a.sink_n + a.cur_n, split = hist ? n : a.sink_n;
+#pragma unroll
+  for (int ii = 0; ii < NW; ++ii) {
+    int64_t j = j0 + rr[ii];
+    j = j < n ? j : n - 1;
+    const bool second = j >= split;
+    const uint8_t *src = (second ? k1 + (j - split) * s1 : k0 + j * s0) + head_off + cc[ii];
+    __builtin_amdgcn_global_load_lds((const void *)src,
+                                     (__attribute__((address_space(3))) void *)(lds_tile + 1024 * (w + 4 * ii)),
+                                     16, 0, 0);
+  }
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 #define ISPA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
 
@@ -467,16 +494,20 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
 // no copy in flight the reads run four operands ahead of the MFMAs (scheduling groups below).
 // ------------------------------------------------------------------------------------------------
 // LSE_ONLY: only the log-sum-exp outputs are wanted (no value copies, no value product, no A rows).
-template <int D, bool BIAS, bool LSE_ONLY = false>
+// FP8: q and the keys are e4m3 bytes (per-head scales): the scores run on v_mfma_f32_32x32x64_f8f6f4,
+// two k-steps of 64 per 32-key block, and a key tile is half the bytes; values stay bf16.
+template <int D, bool BIAS, bool LSE_ONLY = false, bool FP8 = false>
 __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, int n_qt) {
   constexpr int BK = 64;
   constexpr int TB = BK * D * 2;
+  constexpr int TBK = FP8 ? BK * D : TB;     // bytes of a key tile
   constexpr int NKK = D / 16;
+  constexpr int NK8 = D / 64;                // e4m3 k-steps
   constexpr int NDB = D / 32;
   constexpr int NB = BK / 32;
   constexpr int NPV = NDB * NB * 2;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][TBK];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][TB];
   __shared__ __attribute__((aligned(256))) float bbuf[2][BIAS ? BK : 1];   // bias of tiles, beside K
 
@@ -489,10 +520,21 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   const int qi = qt * 256 + w * 32 + l32;
   const int n_q = a.n_q;
   const int out_stride = a.n_heads * D;
-  const float sl2 = a.scale_log2;
+  float sl2 = a.scale_log2;
+  if constexpr (FP8) sl2 *= a.q_scale[head] * a.k_scale[head];   // scores of the dequantised values
 
-  bf16x8 qr[NKK];
-  {
+  bf16x8 qr[FP8 ? 1 : NKK];
+  i32x8 qf[FP8 ? NK8 : 1];   // e4m3 q: lane holds dims 64ks + 32hf .. +31
+  if constexpr (FP8) {
+    const bool ok = qi < n_q;
+    const uint8_t *src = (const uint8_t *)a.q + (int64_t)(ok ? qi : 0) * a.q_stride + head_off + hf * 32;
+#pragma unroll
+    for (int ks = 0; ks < NK8; ++ks) {
+      u32x4 x0 = *(const u32x4 *)(src + 64 * ks), x1 = *(const u32x4 *)(src + 64 * ks + 16);
+      if (!ok) x0 = x1 = u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    }
+  } else {
     const bool ok = qi < n_q;
     const uint16_t *src = (const uint16_t *)a.q + (int64_t)(ok ? qi : 0) * a.q_stride + head_off + hf * 8;
 #pragma unroll
@@ -517,9 +559,22 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     drow[ii] = r;
     dcol8[ii] = 8 * ((lane % CPR) ^ kv_swz<D>(r));
   }
+  constexpr int NW8 = FP8 ? BK * D / 4096 : 1;   // e4m3 key copies per group-A wave per tile
+  int k8row[NW8], k8col[NW8];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int ii = 0; ii < NW8; ++ii) {
+      const int r = (wl + 4 * ii) * (1024 / D) + lane / (D / 16);
+      k8row[ii] = r;
+      k8col[ii] = 16 * ((lane % (D / 16)) ^ ((r >> 1) & 7));
+    }
+  }
   auto tile_j0 = [&](int t) -> int64_t { return (int64_t)(t >= nt_loc ? t - nt_loc : t) * BK; };
   auto dma_k = [&](int t, int buf) {
-    dma_tile<D, BK, false>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, kbuf[buf], wl, drow, dcol8);
+    if constexpr (FP8)
+      dma_tile_k8<D, BK>(a, t >= nt_loc, tile_j0(t), head_off, kbuf[buf], wl, k8row, k8col);
+    else
+      dma_tile<D, BK, false>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, kbuf[buf], wl, drow, dcol8);
   };
   auto dma_v = [&](int t, int buf) {
     dma_tile<D, BK, true>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, vbuf[buf], wl, drow, dcol8);
@@ -608,24 +663,47 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
 #pragma unroll
           for (int v = 0; v < 16; ++v) sc[b][v] = 0.f;
       }
-      // operands two ahead of the MFMAs
-      bf16x8 k0 = kread(i & 1, 0), k1 = kread(i & 1, 1);
+      if constexpr (FP8) {
+        // e4m3 key operand of block b, k-step ks: row 32b + l32, bytes 64ks + 32hf .. +31 (two chunks)
+        i32x8 ka[NB * NK8];
 #pragma unroll
-      for (int j = 0; j < NKK * NB; ++j) {
-        const bf16x8 k2 = kread(i & 1, j + 2 < NKK * NB ? j + 2 : NKK * NB - 1);
-        sc[j % NB] = mfma_bf16_32x32x16(k0, qr[j / NB], sc[j % NB]);
-        k0 = k1;
-        k1 = k2;
-      }
-      // keep four operand reads in flight ahead of the MFMAs (the bias reads, if any, go first)
-      if constexpr (BIAS) __builtin_amdgcn_sched_group_barrier(0x100, NB * 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int j = 0; j < NB * NK8; ++j) {
+          const int b = j / NK8, ks = j % NK8;
+          const uint8_t *kt = kbuf[i & 1];
+          const int r = 32 * b + l32;
+          const u32x4 x0 = *(const u32x4 *)(kt + k8_off<D>(r, 64 * ks + 32 * hf));
+          const u32x4 x1 = *(const u32x4 *)(kt + k8_off<D>(r, 64 * ks + 32 * hf + 16));
+          ka[j] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        }
 #pragma unroll
-      for (int g = 0; g < NKK * NB / 2 - 2; ++g) {
+        for (int j = 0; j < NB * NK8; ++j) sc[j / NK8] = mfma_e4m3_32x32x64(ka[j], qf[j % NK8], sc[j / NK8]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int g = 0; g < NB * NK8 - 2; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      } else {
+        // operands two ahead of the MFMAs
+        bf16x8 k0 = kread(i & 1, 0), k1 = kread(i & 1, 1);
+#pragma unroll
+        for (int j = 0; j < NKK * NB; ++j) {
+          const bf16x8 k2 = kread(i & 1, j + 2 < NKK * NB ? j + 2 : NKK * NB - 1);
+          sc[j % NB] = mfma_bf16_32x32x16(k0, qr[j / NB], sc[j % NB]);
+          k0 = k1;
+          k1 = k2;
+        }
+        // keep four operand reads in flight ahead of the MFMAs (the bias reads, if any, go first)
+        if constexpr (BIAS) __builtin_amdgcn_sched_group_barrier(0x100, NB * 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int g = 0; g < NKK * NB / 2 - 2; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     if (!LSE_ONLY && i > 0) {
       bf16x8 v0 = vread(i - 1, 0), v1 = vread(i - 1, 1);
@@ -872,6 +950,15 @@ hipError_t launch_attn_f32_t(const AttnArgs &a, int head_dim, hipStream_t s) {
 bool has_bias(const AttnArgs &a) { return a.sink_b != nullptr || a.cur_b != nullptr || a.hist_b != nullptr; }
 
 }  // namespace
+
+hipError_t launch_attn_fp8(const AttnArgs &a, int head_dim, hipStream_t s) {
+  if (head_dim != 128 || has_bias(a) || a.q_scale == nullptr || a.k_scale == nullptr) return hipErrorInvalidValue;
+  const int n_qt = (a.n_q + 255) / 256;
+  const int grid = n_qt * a.n_heads;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, false, true>), dim3(grid), dim3(512), 0, s, a, n_qt);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_lse_bf16(const AttnArgs &a, int head_dim, hipStream_t s) {
   if (has_bias(a) || a.a_loc != nullptr || a.a_full != nullptr) return hipErrorInvalidValue;

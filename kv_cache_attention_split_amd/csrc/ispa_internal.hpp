@@ -30,6 +30,8 @@ struct AttnArgs {
   const float *sink_b, *cur_b, *hist_b;
   int64_t sink_bhs, cur_bhs, hist_bhs;
   float bias_to_score;
+  // FP8 scores: q and the keys as OCP e4m3 bytes with one scale per head each (device [H])
+  const float *q_scale, *k_scale;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s);
@@ -49,6 +51,13 @@ hipError_t launch_kv_merge(bool bf16, int width, const void *k, const void *v, i
                            const int32_t *offsets, const int32_t *members, int64_t n_groups, void *k_out,
                            void *v_out, int64_t out_stride, float *bias_out, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, int head_dim, hipStream_t s);
+// e4m3 q and keys (scores on the FP8 matrix cores), bf16 values and outputs; head_dim 128.
+hipError_t launch_attn_fp8(const AttnArgs &a, int head_dim, hipStream_t s);
+// Per-head absmax / 448 of [n, H, d] rows (bf16 or fp32); quantisation to e4m3 with per-head scales.
+hipError_t launch_fp8_head_scales(bool bf16, const void *x, int64_t n, int n_heads, int head_dim, int64_t stride,
+                                  float *scales, hipStream_t s);
+hipError_t launch_fp8_quantize(bool bf16, const void *x, int64_t n, int n_heads, int head_dim, int64_t stride,
+                               const float *scales, uint8_t *out, int64_t out_stride, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------------
 // Gram accumulation (bf16 rows, fp32 sums)

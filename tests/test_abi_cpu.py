@@ -27,7 +27,7 @@ MISALIGNED = 0x10008
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ispa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ispa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -141,6 +141,35 @@ def test_kv_merge_argument_errors(L):
     assert call(G=3, vo=MISALIGNED) == _abi.ISPA_E_ARG
     assert call(G=3, out_stride=128) == _abi.ISPA_E_ARG
     assert call(G=3, bias=FAKE + 1) == _abi.ISPA_E_ARG
+
+
+def test_fp8_argument_errors(L):
+    hs, qz = L.ispa_fp8_head_scales, L.ispa_fp8_quantize
+    assert hs(2, FAKE, 10, 2, 128, 256, FAKE2, None) == _abi.ISPA_E_UNSUPPORTED      # dtype
+    assert hs(1, FAKE, 10, 2, 96, 256, FAKE2, None) == _abi.ISPA_E_UNSUPPORTED       # head_dim
+    assert hs(1, FAKE, -1, 2, 128, 256, FAKE2, None) == _abi.ISPA_E_ARG
+    assert hs(1, MISALIGNED, 10, 2, 128, 256, FAKE2, None) == _abi.ISPA_E_ARG
+    assert hs(1, FAKE, 10, 2, 128, 255, FAKE2, None) == _abi.ISPA_E_ARG
+    assert hs(1, FAKE, 10, 2, 128, 256, None, None) == _abi.ISPA_E_ARG
+    assert qz(1, FAKE, 0, 2, 128, 256, None, None, 0, None) == _abi.ISPA_OK          # no rows: no-op
+    assert qz(1, FAKE, 10, 2, 128, 256, FAKE2, FAKE + 4, 256, None) == _abi.ISPA_E_ARG   # out misaligned
+    assert qz(1, FAKE, 10, 2, 128, 256, FAKE2, FAKE, 200, None) == _abi.ISPA_E_ARG   # out stride short
+    at = L.ispa_attn_dual_fp8
+
+    def call(dh=128, q=FAKE, n_q=32, qs=256, sink=None, cur=None, hist=None, a_loc=FAKE, sq=FAKE2, sk=FAKE2):
+        sink = sink if sink is not None else seg()
+        cur = cur if cur is not None else seg()
+        hist = hist if hist is not None else seg()
+        return at(2, dh, ctypes.c_float(0.088), q, n_q, qs, sq, sink, cur, hist, sk, a_loc, FAKE2, None, None,
+                  None, None)
+    assert call(dh=64) == _abi.ISPA_E_UNSUPPORTED
+    assert call(sink=seg(n=0), cur=seg(n=0)) == _abi.ISPA_E_ARG
+    assert call(hist=seg(stride=264)) == _abi.ISPA_E_ARG        # K rows need a multiple of 16
+    assert call(qs=264) == _abi.ISPA_E_ARG
+    assert call(sq=None) == _abi.ISPA_E_ARG
+    assert call(sk=FAKE + 2) == _abi.ISPA_E_ARG
+    assert call(a_loc=None) == _abi.ISPA_E_ARG
+    assert call(n_q=0) == _abi.ISPA_OK
 
 
 def test_future_scores_argument_errors(L):

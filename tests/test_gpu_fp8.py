@@ -1,0 +1,112 @@
+"""GPU parity of the FP8 (e4m3) path against the oracle (`oracle.fp8`).
+
+Gates: per-head scales and e4m3 codes bit-exact (the same fp32 steps and the same round-to-nearest-even
+decision on both sides); the FP8 attention within the attention tolerances of the oracle evaluated on
+the same codes (scores from exact products of the dequantised values).
+"""
+import numpy as np
+import pytest
+
+import ispa_inputs as inputs
+from oracle import fp8 as ofp
+
+from gpu_helpers import check_attention, empty_outputs, to_dev, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _scales_and_codes(x, dt, scales=None):
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    n, H, dh = x.shape
+    xd = to_dev(x.reshape(n, H * dh), dt).reshape(n, H, dh)
+    if scales is None:
+        sd = torch.full((H,), float("nan"), dtype=torch.float32, device="cuda")
+        ispa.ispa_fp8_head_scales(xd, sd)
+    else:
+        sd = torch.from_numpy(np.asarray(scales, dtype=np.float32)).cuda()
+    cd = torch.empty((n, H, dh), dtype=torch.uint8, device="cuda")
+    ispa.ispa_fp8_quantize(xd, sd, cd)
+    torch.cuda.synchronize()
+    return sd, cd
+
+
+@pytest.mark.parametrize("dt,n,H,dh", [("bf16", 1000, 3, 128), ("f32", 77, 2, 64), ("bf16", 1, 1, 64),
+                                       ("f32", 300, 12, 128)])
+def test_scales_and_codes_bit_exact(dt, n, H, dh):
+    _log(f"case: fp8 quantize {dt} rows={n} H={H} d_h={dh}")
+    rng = np.random.default_rng(n + H)
+    x = (rng.standard_normal((n, H, dh)) * np.exp2(rng.uniform(-14, 3, (n, H, dh)))).astype(np.float32)
+    x *= np.array([0.01, 3.0, 50.0] * 4)[:H][None, :, None].astype(np.float32)
+    if dt == "bf16":
+        x = inputs.round_bf16(x)
+    sd, cd = _scales_and_codes(x, dt)
+    s = ofp.head_scales(x)
+    np.testing.assert_array_equal(sd.cpu().numpy(), s)
+    np.testing.assert_array_equal(cd.cpu().numpy(), ofp.quantize(x, s))
+
+
+def test_codes_saturate_and_zero_head():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((64, 2, 64)) * 10).astype(np.float32)
+    x[:, 1] = 0.0
+    small = np.array([0.001, 1.0], dtype=np.float32)          # head 0 overflows 448 by far: saturates
+    _, cd = _scales_and_codes(x, "f32", scales=small)
+    np.testing.assert_array_equal(cd.cpu().numpy(), ofp.quantize(x, small))
+    assert np.all(cd.cpu().numpy()[:, 1] & 0x7F == 0)
+    sd, _ = _scales_and_codes(x, "f32")
+    assert float(sd.cpu().numpy()[1]) == 1.0
+
+
+def _run_fp8(inp, want_full=True):
+    """Codes and scales from the oracle (host), uploaded: the oracle never reads a device result."""
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    q_s = ofp.head_scales(inp["q"])
+    q_c = ofp.quantize(inp["q"], q_s)
+    keys = np.concatenate([inp["sink_k"], inp["cur_k"], inp["hist_k"]], axis=0)
+    k_s = ofp.head_scales(keys)                          # one key scale per head for the whole cache
+    codes = {n: ofp.quantize(inp[n + "_k"], k_s) for n in ("sink", "cur", "hist")}
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()   # noqa: E731
+    dev = {n + "_v": to_dev(inp[n + "_v"], "bf16") for n in ("sink", "cur", "hist")}
+    n_q, H, dh = inp["q"].shape
+    out = empty_outputs(n_q, H, dh, "bf16", want_full)
+    ispa.ispa_attn_dual_fp8(up(q_c), up(q_s), up(codes["sink"]), dev["sink_v"], up(codes["cur"]), dev["cur_v"],
+                            up(codes["hist"]), dev["hist_v"], up(k_s), float(inp["scale"]), out["a_loc"],
+                            out["a_full"], out["lse_loc"], out["lse_hist"], out["lse_full"])
+    torch.cuda.synchronize()
+    return out, q_c, q_s, codes, k_s
+
+
+@pytest.mark.parametrize("case", [dict(n_q=300, n_sink=40, n_cur=100, n_hist=333),
+                                  dict(n_q=257, n_sink=0, n_cur=64, n_hist=0),
+                                  dict(n_q=130, n_sink=17, n_cur=75, n_hist=129)])
+def test_fp8_attention_vs_oracle(case):
+    _log(f"case: fp8 attention 2 x 128 {case}")
+    inp = inputs.attention_case(60 + case["n_q"], n_heads=2, head_dim=128, **case)
+    out, qc, qs, kc, ks = _run_fp8(inp)
+    ref = ofp.dual_stream_fp8(inp, qc, qs, kc, ks)
+    rep = check_attention(out, ref, "bf16")
+    _log(f"   {rep}")
+
+
+def test_fp8_local_only():
+    inp = inputs.attention_case(71, n_heads=2, head_dim=128, n_q=200, n_sink=32, n_cur=160, n_hist=96)
+    out, qc, qs, kc, ks = _run_fp8(inp, want_full=False)
+    ref = ofp.dual_stream_fp8(inp, qc, qs, kc, ks)
+    check_attention(out, ref, "bf16")
+
+
+def test_fp8_wan_shape_sampled_rows():
+    inp = inputs.attention_inputs(2, 0, 0)               # 12 x 128, 4680 queries, 18,720 keys
+    _log("case: fp8 attention on workload 2 (12 x 128, 4680 queries, 18720 keys), sampled rows")
+    out, qc, qs, kc, ks = _run_fp8(inp)
+    rows = np.random.default_rng(2).choice(inp["q"].shape[0], size=48, replace=False)
+    rows.sort()
+    ref = ofp.dual_stream_fp8(dict(inp, q=inp["q"]), qc, qs, kc, ks, rows=rows)
+    rep = check_attention(out, ref, "bf16", rows=rows)
+    _log(f"   {rep}")
