@@ -45,6 +45,8 @@ def parse():
                          "single-pass forms, warm and cold cache) and print one JSON line")
     ap.add_argument("--steady", action="store_true",
                     help="time the steady state after the warmup: L-Layer vs F-Layer chunk at 9/30/60 frames")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8-score attention against the bf16 kernel on workloads 2 and 5")
     ap.add_argument("--future", action="store_true",
                     help="time the future-query importance scores over workload 5's cache")
     ap.add_argument("--tempcache", action="store_true",
@@ -380,6 +382,58 @@ def future_report(steps, warmup, torch):
           flush=True)
 
 
+def fp8_report(steps, warmup, torch):
+    """FP8 attention scores (e4m3 q and keys, per-head scales; bf16 values) against the bf16 kernel on
+    workloads 2 and 5 (dual stream), plus the quantiser's rate on workload 5's keys. Attention FLOP are
+    counted as for bf16 (4 n_q n_k d_h per head)."""
+    import ispa_inputs as inputs
+    import kv_cache_attention_split_amd as ispa
+    rows = []
+    for cfg in (2, 5):
+        wl = inputs.CONFIGS[cfg]
+        inp = inputs.attention_inputs(cfg, 0, 0)
+        dev = {k: bf16_dev(inp[k], torch) for k in ("q", "sink_k", "sink_v", "cur_k", "cur_v", "hist_k", "hist_v")}
+        H, dh = wl.n_heads, wl.head_dim
+        n_q = inp["q"].shape[0]
+        keys = torch.cat([dev["sink_k"], dev["cur_k"], dev["hist_k"]], dim=0)
+        q_s = torch.empty(H, dtype=torch.float32, device="cuda")
+        k_s = torch.empty(H, dtype=torch.float32, device="cuda")
+        ispa.ispa_fp8_head_scales(dev["q"], q_s)
+        ispa.ispa_fp8_head_scales(keys, k_s)
+        q8 = torch.empty(dev["q"].shape, dtype=torch.uint8, device="cuda")
+        ispa.ispa_fp8_quantize(dev["q"], q_s, q8)
+        k8 = {}
+        for n in ("sink", "cur", "hist"):
+            k8[n] = torch.empty(dev[n + "_k"].shape, dtype=torch.uint8, device="cuda")
+            ispa.ispa_fp8_quantize(dev[n + "_k"], k_s, k8[n])
+        a_loc = torch.empty((n_q, H * dh), dtype=torch.bfloat16, device="cuda")
+        a_full = torch.empty_like(a_loc)
+        lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
+        calls = {
+            "bf16": lambda: ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"],
+                                                dev["hist_k"], dev["hist_v"], wl.scale, a_loc, a_full, *lse),
+            "fp8": lambda: ispa.ispa_attn_dual_fp8(q8, q_s, k8["sink"], dev["sink_v"], k8["cur"], dev["cur_v"],
+                                                   k8["hist"], dev["hist_v"], k_s, wl.scale, a_loc, a_full, *lse),
+            "quantize_keys": lambda: ispa.ispa_fp8_quantize(keys, k_s, torch.empty(keys.shape, dtype=torch.uint8,
+                                                                                   device="cuda")),
+        }
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            for c in calls.values():
+                c()
+            torch.cuda.synchronize()
+        ms = {k: float(np.median([_time_calls(c, steps, warmup, torch) for _ in range(3)])) for k, c in calls.items()}
+        n_keys = keys.shape[0]
+        fl = attn_flops(n_q, n_keys, H, dh)
+        qbytes = n_keys * H * dh * 3          # bf16 read + e4m3 write
+        rows.append({"workload": wl.name, "keys": n_keys, "bf16_ms": round(ms["bf16"], 4),
+                     "fp8_ms": round(ms["fp8"], 4), "speedup": round(ms["bf16"] / ms["fp8"], 3),
+                     "fp8_tflops_bf16_count": round(fl / ms["fp8"] / 1e9, 1),
+                     "quantize_keys_ms": round(ms["quantize_keys"], 4),
+                     "quantize_gbps": round(qbytes / ms["quantize_keys"] / 1e6, 1)})
+    print(json.dumps({"fp8_attention": rows}), flush=True)
+
+
 def steady_report(steps, warmup, torch):
     """After the warmup (ISPA stage 3): time of one chunk of an L-Layer (local-only attention over sink
     + current chunk, projection with W + dW) against an F-Layer (full attention over the whole cache,
@@ -463,6 +517,9 @@ def main():
         return
     if args.steady:
         steady_report(max(args.steps, 20), max(args.warmup, 5), torch)
+        return
+    if args.fp8:
+        fp8_report(max(args.steps, 20), max(args.warmup, 5), torch)
         return
     if args.future:
         future_report(max(args.steps, 20), max(args.warmup, 5), torch)
