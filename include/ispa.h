@@ -243,6 +243,21 @@ ispa_status ispa_absorb_accumulate(ispa_dtype dt, int64_t n_rows, int32_t d,
                                    float *G, float *X, float *F,
                                    void *ws, size_t ws_bytes, void *stream);
 
+/* FP8 statistics (ISPA page, section 4: ISPA with W8A8): the same sums over rows stored as OCP e4m3
+ * bytes with one scale per head (rows quantised by ispa_fp8_quantize with scales from
+ * ispa_fp8_head_scales): G += A_loc^T A_loc etc. of the dequantised rows e4m3 * scale, exact products
+ * on the FP8 matrix cores, fp32 sums.
+ *   a_loc, a_full  device uint8 [n_rows, d] (row stride d), 16-byte aligned
+ *   s_loc, s_full  device fp32 [d / head_dim] per-head scales; head_dim in {64, 128}, d % 64 == 0,
+ *                  d % head_dim == 0
+ *   G, X, F, ws    as for ispa_absorb_accumulate (ws unused)
+ */
+ispa_status ispa_absorb_accumulate_fp8(int64_t n_rows, int32_t d, int32_t head_dim,
+                                       const uint8_t *a_loc, const float *s_loc,
+                                       const uint8_t *a_full, const float *s_full,
+                                       float *G, float *X, float *F,
+                                       void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Closed-form absorb update (ISPA page, section 2 stage 2 "Layer Absorb", second display equation):
  *   dW = (A_loc^T A_loc + lambda I)^-1 A_loc^T (A_full - A_loc) W = (G + lambda I)^-1 (X - G) W

@@ -19,7 +19,7 @@ from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVBias, KVSegment, l
 __all__ = [
     "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_future_scores",
     "ispa_future_scores_workspace", "ispa_fp8_head_scales", "ispa_fp8_quantize", "ispa_attn_dual_fp8",
-    "ispa_absorb_accumulate", "ispa_absorb_accumulate_workspace",
+    "ispa_absorb_accumulate", "ispa_absorb_accumulate_fp8", "ispa_absorb_accumulate_workspace",
     "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_layer_error",
     "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_apply_delta", "ispa_project",
     "ispa_kv_plan", "ispa_status_string", "ispa_version",
@@ -274,6 +274,20 @@ def ispa_absorb_accumulate(a_loc, a_full, G, X, F=None, ws=None, stream=None) ->
         _dtype_code(a_loc), n, d, _ptr(a_loc), _ptr(a_full), _ptr(G), _ptr(X), _ptr(F),
         _ptr(ws), 0 if ws is None else int(ws.numel() * ws.element_size()), _stream_handle(stream))
     _check(st, "ispa_absorb_accumulate")
+
+
+def ispa_absorb_accumulate_fp8(a_loc, s_loc, a_full, s_full, head_dim: int, G, X, F=None, stream=None) -> None:
+    """FP8 statistics: a_loc, a_full uint8 e4m3 codes [n, d] (contiguous), s_loc, s_full float32 per-head
+    scales [d / head_dim]; G, X, F as for ispa_absorb_accumulate."""
+    n, d = (int(x) for x in a_loc.shape)
+    if tuple(a_full.shape) != (n, d):
+        raise ValueError("a_loc and a_full must match")
+    for t in (a_loc, a_full, G, X) + ((F,) if F is not None else ()):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    st = lib().ispa_absorb_accumulate_fp8(n, d, int(head_dim), _ptr(a_loc), _ptr(s_loc), _ptr(a_full), _ptr(s_full),
+                                          _ptr(G), _ptr(X), _ptr(F), None, 0, _stream_handle(stream))
+    _check(st, "ispa_absorb_accumulate_fp8")
 
 
 def _ptr_array(ts: Sequence) -> ctypes.Array:

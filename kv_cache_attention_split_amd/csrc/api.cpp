@@ -427,6 +427,24 @@ ispa_status ispa_absorb_accumulate(ispa_dtype dt, int64_t n_rows, int32_t d, con
 }
 
 // ------------------------------------------------------------------------------------------------
+ispa_status ispa_absorb_accumulate_fp8(int64_t n_rows, int32_t d, int32_t head_dim, const uint8_t *a_loc,
+                                       const float *s_loc, const uint8_t *a_full, const float *s_full, float *G,
+                                       float *X, float *F, void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (n_rows < 0 || d <= 0) return ISPA_E_ARG;
+  if (head_dim != 64 && head_dim != 128) return ISPA_E_UNSUPPORTED;
+  if (d % 64 != 0 || d % head_dim != 0) return ISPA_E_UNSUPPORTED;
+  if (G == nullptr || X == nullptr || !aligned16(G) || !aligned16(X)) return ISPA_E_ARG;
+  if (F != nullptr && !aligned16(F)) return ISPA_E_ARG;
+  if (n_rows == 0) return ISPA_OK;
+  if (a_loc == nullptr || a_full == nullptr || !aligned16(a_loc) || !aligned16(a_full)) return ISPA_E_ARG;
+  if (s_loc == nullptr || s_full == nullptr || !aligned4(s_loc) || !aligned4(s_full)) return ISPA_E_ARG;
+  if (n_rows > INT32_MAX) return ISPA_E_ARG;
+  return hip_status(launch_gram_fp8(n_rows, d, head_dim, a_loc, s_loc, a_full, s_full, G, X, F,
+                                    (hipStream_t)stream));
+}
+
 size_t ispa_absorb_solve_workspace(int32_t d, int32_t batch) {
   if (d <= 0 || batch <= 0) return 0;
   return solve_layout(d).total(batch);

@@ -267,7 +267,249 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// e4m3 rows (OCP FP8 E4M3 with one scale per head): the same 128x128 tiles and ring, 64 rows per stage
+// (one v_mfma_f32_32x32x64_f8f6f4 k-step), 128-byte stage rows whose 16-byte chunk c is stored at
+// c ^ ((r / 2) mod 8). ds_read_b64_tr_b8 builds the operands: in each 16-lane group, lane s addresses
+// row k0 + s/2, bytes n0 + 8 (s mod 2) .. +7, and result lane i receives column n0 + i of rows k0 ..
+// k0+7; four reads give a lane its 32 rows. The per-head scales multiply each tile in the epilogue.
+// ---------------------------------------------------------------------------------------------
+constexpr int BR8 = 64;                       // rows per stage
+constexpr int RB8 = BT;                       // bytes of one stage row (128 e4m3 columns)
+constexpr int kPart8 = BR8 * RB8;             // 8 KB
+constexpr int kStage8 = 2 * kPart8;           // 16 KB
+constexpr int kCopies8 = kStage8 / 1024 / 4;  // 4
+
+struct GramArgs8 {
+  const uint8_t *a_loc, *a_full;
+  const float *s_loc, *s_full;                // per-head scales
+  float *G, *X, *F;
+  int64_t n_rows;
+  int d, T, n_upper, with_f, head_dim;
+};
+
+__device__ __forceinline__ int swz8_off(int r, int col) {   // byte offset of (r, col) in a stage part
+  return r * RB8 + ((((col >> 4) ^ ((r >> 1) & 7))) << 4) + (col & 15);
+}
+
+typedef int s32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ i32x8 read_operand8(const uint8_t *part, int cb, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int n0 = cb + 16 * (g & 1) + 8 * (s & 1);
+  const int k0 = 32 * (g >> 1) + (s >> 1);
+  s32x2 r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) s32x2 *)(part + swz8_off(k0 + 8 * j, n0)));
+  return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+}
+
+struct StageOps8 {
+  i32x8 a[2], b[2];   // [32-column block]
+};
+
+__global__ void __launch_bounds__(kThreads, 2) gram_fp8_kernel(GramArgs8 g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStage8];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStage8];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStage8];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[kStage8];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wm = w >> 1, wn = w & 1;
+
+  const int n_tiles = g.n_upper * (g.with_f ? 2 : 1) + g.T * g.T;
+  int idx = xcd_remap(blockIdx.x, n_tiles);
+  int mat, ti, tj;   // mat: 0 = G, 1 = F, 2 = X
+  if (idx < g.n_upper) {
+    mat = 0;
+    tri_decode(idx, g.T, ti, tj);
+  } else if (g.with_f && idx < 2 * g.n_upper) {
+    mat = 1;
+    tri_decode(idx - g.n_upper, g.T, ti, tj);
+  } else {
+    mat = 2;
+    idx -= g.n_upper * (g.with_f ? 2 : 1);
+    ti = idx / g.T;
+    tj = idx % g.T;
+  }
+  const uint8_t *P = (mat == 1) ? g.a_full : g.a_loc;
+  const uint8_t *Q = (mat == 0) ? g.a_loc : g.a_full;
+  const float *sP = (mat == 1) ? g.s_full : g.s_loc;
+  const float *sQ = (mat == 0) ? g.s_loc : g.s_full;
+  float *out = (mat == 0) ? g.G : (mat == 1) ? g.F : g.X;
+  const int i0 = ti * BT, j0 = tj * BT;
+  const int d = g.d;
+  const int64_t n_rows = g.n_rows;
+  const int nst = (int)((n_rows + BR8 - 1) / BR8);
+
+  // copy instruction ii of wave w fills 1 KB block blk = w + 4 ii: blocks 0-7 the left operand, 8-15
+  // the right one, 8 rows each; lane l lands at row 8 (blk mod 8) + l / 8, stored chunk l mod 8, which
+  // holds source chunk (l mod 8) ^ ((row / 2) mod 8). Columns past d are clamped (not stored).
+  const uint8_t *src[kCopies8];
+  int crow[kCopies8];
+#pragma unroll
+  for (int ii = 0; ii < kCopies8; ++ii) {
+    const int blk = w + 4 * ii;
+    const int op = blk >> 3;
+    const int r = 8 * (blk & 7) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    int col = (op ? j0 : i0) + 16 * c;
+    col = col < d ? col : d - 16;
+    crow[ii] = r;
+    src[ii] = (op ? Q : P) + (int64_t)r * d + col;
+  }
+  const int64_t stage_bytes = (int64_t)BR8 * d;
+  uint64_t zero_row = (uint64_t)(uintptr_t)g_zero_row;
+  asm volatile("" : "+s"(zero_row));
+
+  auto copy_stage = [&](int s, uint8_t *slot) {
+#pragma unroll
+    for (int ii = 0; ii < kCopies8; ++ii) {
+      const int64_t n = (int64_t)s * BR8 + crow[ii];
+      const uint8_t *p = src[ii] + (int64_t)s * stage_bytes;
+      p = n < n_rows ? p : (const uint8_t *)(uintptr_t)zero_row;
+      __builtin_amdgcn_global_load_lds((const void *)p,
+                                       (__attribute__((address_space(3))) void *)(slot + 1024 * (w + 4 * ii)),
+                                       16, 0, 0);
+    }
+  };
+  auto read_stage = [&](const uint8_t *slot, StageOps8 &o) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) o.a[bi] = read_operand8(slot, wm * 64 + bi * 32, lane);
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) o.b[bj] = read_operand8(slot + kPart8, wn * 64 + bj * 32, lane);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
+
+  auto stage = [&](int s, uint8_t *cur, const uint8_t *nxt, const StageOps8 &ocur, StageOps8 &onx) {
+    ISPA_GRAM_WAIT_VMCNT(kCopies8 * (NS - 2));
+    ISPA_GRAM_LDS_BARRIER();
+    copy_stage(s + NS, cur);
+    read_stage(nxt, onx);
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma_e4m3_32x32x64(ocur.a[bi], ocur.b[bj], acc[bi][bj]);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, kCopies8, 0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  };
+
+  StageOps8 oa, ob;
+  copy_stage(0, ring0);
+  copy_stage(1, ring1);
+  copy_stage(2, ring2);
+  copy_stage(3, ring3);
+  ISPA_GRAM_WAIT_VMCNT(kCopies8 * (NS - 1));
+  ISPA_GRAM_LDS_BARRIER();
+  read_stage(ring0, oa);
+  for (int s = 0; s < nst; s += NS) {
+    stage(s, ring0, ring1, oa, ob);
+    stage(s + 1, ring1, ring2, ob, oa);
+    stage(s + 2, ring2, ring3, oa, ob);
+    stage(s + 3, ring3, ring0, ob, oa);
+  }
+  ISPA_GRAM_WAIT_VMCNT(0);   // no copy may land in LDS after the workgroup has ended
+
+  // per-head scales: element (row i, column j) of the tile times sP[i / head_dim] * sQ[j / head_dim]
+  const int hd = g.head_dim;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      int cl = j0 + wn * 64 + bj * 32 + l32;
+      cl = cl < d ? cl : d - 1;
+      const float sq = sQ[cl / hd];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        int rw = i0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        rw = rw < d ? rw : d - 1;
+        acc[bi][bj][v] *= sP[rw / hd] * sq;
+      }
+    }
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int cl = j0 + wn * 64 + bj * 32 + l32;
+      const int clc = cl < d ? cl : d - 1;
+      float cur[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rw = i0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        const int rwc = rw < d ? rw : d - 1;
+        cur[v] = out[(int64_t)rwc * d + clc];
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rw = i0 + wm * 64 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        if (rw < d && cl < d) out[(int64_t)rw * d + cl] = cur[v] + acc[bi][bj][v];
+      }
+    }
+  if (mat != 2 && ti != tj) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj) {
+        const int mr = j0 + wn * 64 + bj * 32 + l32;
+        const int mrc = mr < d ? mr : d - 1;
+        f32x4 cur[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int mc = i0 + wm * 64 + bi * 32 + 8 * q + 4 * hf;
+          const int mcc = mc < d ? mc : d - 4;
+          cur[q] = *(const f32x4 *)&out[(int64_t)mrc * d + mcc];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int mc = i0 + wm * 64 + bi * 32 + 8 * q + 4 * hf;
+          f32x4 add;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) add[e] = acc[bi][bj][4 * q + e];
+          if (mr < d && mc < d) *(f32x4 *)&out[(int64_t)mr * d + mc] = cur[q] + add;
+        }
+      }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gram_fp8(int64_t n_rows, int d, int head_dim, const uint8_t *a_loc, const float *s_loc,
+                           const uint8_t *a_full, const float *s_full, float *G, float *X, float *F, hipStream_t s) {
+  GramArgs8 g;
+  g.a_loc = a_loc;
+  g.a_full = a_full;
+  g.s_loc = s_loc;
+  g.s_full = s_full;
+  g.G = G;
+  g.X = X;
+  g.F = F;
+  g.n_rows = n_rows;
+  g.d = d;
+  g.T = (d + BT - 1) / BT;
+  g.n_upper = g.T * (g.T + 1) / 2;
+  g.with_f = F != nullptr;
+  g.head_dim = head_dim;
+  const int n_tiles = g.n_upper * (g.with_f ? 2 : 1) + g.T * g.T;
+  if (n_rows == 0 || n_tiles == 0 || d < 16) return hipSuccess;
+  hipLaunchKernelGGL(gram_fp8_kernel, dim3(n_tiles), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_gram_bf16(int64_t n_rows, int d, const uint16_t *a_loc, const uint16_t *a_full,
                             float *G, float *X, float *F, hipStream_t s) {

@@ -64,6 +64,9 @@ hipError_t launch_fp8_quantize(bool bf16, const void *x, int64_t n, int n_heads,
 // ------------------------------------------------------------------------------------------------
 hipError_t launch_gram_bf16(int64_t n_rows, int d, const uint16_t *a_loc, const uint16_t *a_full,
                             float *G, float *X, float *F, hipStream_t s);
+// e4m3 rows [n, d] with per-head scales (d / head_dim of each); same sums of the dequantised rows.
+hipError_t launch_gram_fp8(int64_t n_rows, int d, int head_dim, const uint8_t *a_loc, const float *s_loc,
+                           const uint8_t *a_full, const float *s_full, float *G, float *X, float *F, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------------
 // fp32 batched GEMM on MFMA:  C[i][j] = alpha * sum_k opA[i][k] opB[k][j] + beta * C[i][j]

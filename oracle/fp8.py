@@ -14,7 +14,10 @@ the arithmetic of each step is pinned):
     scale = absmax / 448 (1 where the head is all zero); codes = e4m3(fp32(x * fp32(1 / scale)));
   * attention: the scores use the dequantised values q = e4m3_value * scale_q, k = e4m3_value *
     scale_k with exact products; values and probabilities stay at bf16 (only the score product is in
-    FP8), so the FP8 attention oracle is the plain attention oracle on dequantised Q and K.
+    FP8), so the FP8 attention oracle is the plain attention oracle on dequantised Q and K;
+  * statistics: the attention outputs A_loc and A_full (rows [n, d], d = H * d_h) are quantised per
+    head like the keys; G, X, F are the Gram sums of the dequantised rows (exact products), so the
+    FP8 statistics oracle is the plain one on dequantised rows.
 """
 from __future__ import annotations
 
@@ -91,3 +94,13 @@ def dual_stream_fp8(inp: Dict[str, np.ndarray], q_codes, q_scale, k_codes: Dict[
     for name in ("sink", "cur", "hist"):
         deq[name + "_k"] = dequantize(k_codes[name], k_scale)
     return oatt.dual_stream(deq, scale=scale if scale is not None else float(inp["scale"]), rows=rows)
+
+
+def grams_fp8(loc_codes, loc_scale, full_codes, full_scale, head_dim: int) -> Dict[str, np.ndarray]:
+    """G, X, F of dequantised e4m3 rows [n, d] with per-head scales ([d / head_dim] each)."""
+    from . import absorb as oab
+    n, d = np.shape(loc_codes)
+    H = d // head_dim
+    a = dequantize(np.reshape(loc_codes, (n, H, head_dim)), loc_scale).reshape(n, d)
+    b = dequantize(np.reshape(full_codes, (n, H, head_dim)), full_scale).reshape(n, d)
+    return oab.grams(a, b)

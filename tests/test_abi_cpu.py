@@ -172,6 +172,21 @@ def test_fp8_argument_errors(L):
     assert call(n_q=0) == _abi.ISPA_OK
 
 
+def test_accumulate_fp8_argument_errors(L):
+    f = L.ispa_absorb_accumulate_fp8
+
+    def call(n=10, d=256, hd=128, al=FAKE, sl=FAKE2, af=FAKE, sf=FAKE2, G=FAKE, X=FAKE, F=FAKE):
+        return f(n, d, hd, al, sl, af, sf, G, X, F, None, 0, None)
+    assert call(hd=96) == _abi.ISPA_E_UNSUPPORTED
+    assert call(d=192) == _abi.ISPA_E_UNSUPPORTED          # not a multiple of head_dim 128
+    assert call(d=100, hd=64) == _abi.ISPA_E_UNSUPPORTED
+    assert call(n=-1) == _abi.ISPA_E_ARG
+    assert call(G=None) == _abi.ISPA_E_ARG
+    assert call(al=MISALIGNED) == _abi.ISPA_E_ARG
+    assert call(sf=None) == _abi.ISPA_E_ARG
+    assert call(n=0, al=None, af=None, sl=None, sf=None) == _abi.ISPA_OK
+
+
 def test_future_scores_argument_errors(L):
     f = L.ispa_future_scores
     base = dict(dt=1, H=2, dh=128, scale=0.088, q=FAKE, n_p=10, q_stride=256, sink=seg(n=8), cur=seg(n=8),

@@ -2,7 +2,11 @@
 
 Gates: per-head scales and e4m3 codes bit-exact (the same fp32 steps and the same round-to-nearest-even
 decision on both sides); the FP8 attention within the attention tolerances of the oracle evaluated on
-the same codes (scores from exact products of the dequantised values).
+the same codes (scores from exact products of the dequantised values); FP8 statistics rel-Frobenius
+<= 5e-5. The FP8 matrix instruction adds its 64 products per step in an order the ISA does not state,
+so the sqrt(N) * 2^-24 estimate of the bf16 path does not apply; the worst case of an N-term fp32 sum,
+(N - 1) * 2^-24, is 2.8e-4 at 4680 rows. 5e-5 sits between the measured 1.0e-5 and that bound and still
+fails when a single row of 4680 is lost (2e-4).
 """
 import numpy as np
 import pytest
@@ -13,6 +17,8 @@ from oracle import fp8 as ofp
 from gpu_helpers import check_attention, empty_outputs, to_dev, torch_mod
 
 pytestmark = pytest.mark.gpu
+
+FP8_STATS_TOL = 5e-5
 
 
 def _log(msg):
@@ -110,3 +116,53 @@ def test_fp8_wan_shape_sampled_rows():
     ref = ofp.dual_stream_fp8(dict(inp, q=inp["q"]), qc, qs, kc, ks, rows=rows)
     rep = check_attention(out, ref, "bf16", rows=rows)
     _log(f"   {rep}")
+
+
+def _grams_fp8_gpu(loc_codes, s_loc, full_codes, s_full, head_dim, with_f=True, chunks=1):
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    n, d = loc_codes.shape
+    G, X, F = (torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3))
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()   # noqa: E731
+    bounds = np.linspace(0, n, chunks + 1).astype(int)
+    for c in range(chunks):
+        r0, r1 = bounds[c], bounds[c + 1]
+        ispa.ispa_absorb_accumulate_fp8(up(loc_codes[r0:r1]), up(s_loc), up(full_codes[r0:r1]), up(s_full),
+                                        head_dim, G, X, F if with_f else None)
+    torch.cuda.synchronize()
+    return G, X, F
+
+
+def _fp8_rows(cfg_rows, head_dim):
+    n, d = cfg_rows["a_loc"].shape
+    H = d // head_dim
+    a = cfg_rows["a_loc"].reshape(n, H, head_dim)
+    b = cfg_rows["a_full"].reshape(n, H, head_dim)
+    sa, sb = ofp.head_scales(a), ofp.head_scales(b)
+    return ofp.quantize(a, sa).reshape(n, d), sa, ofp.quantize(b, sb).reshape(n, d), sb
+
+
+@pytest.mark.parametrize("d,n,hd,chunks", [(1536, 4680, 128, 1), (192, 333, 64, 1), (1024, 40, 128, 1),
+                                           (1088, 517, 64, 3)])
+def test_fp8_statistics_vs_oracle(d, n, hd, chunks):
+    _log(f"case: fp8 statistics d={d} rows={n} head_dim={hd} chunks={chunks}")
+    rows = inputs.absorb_rows(3, 0, 3, d=d, n_rows=n, dtype="bf16")
+    lc, ls, fc, fs = _fp8_rows(rows, hd)
+    G, X, F = _grams_fp8_gpu(lc, ls, fc, fs, hd, chunks=chunks)
+    ref = ofp.grams_fp8(lc, ls, fc, fs, hd)
+    from gpu_helpers import rel_fro, to_host64
+    for name, t in (("G", G), ("X", X), ("F", F)):
+        err = rel_fro(to_host64(t), ref[name])
+        _log(f"  {name}: rel_fro {err:.2e}")
+        assert err <= FP8_STATS_TOL, (name, err)
+    torch = torch_mod()
+    assert torch.equal(G, G.T) and torch.equal(F, F.T)
+
+
+def test_fp8_statistics_zero_gap_bitwise():
+    # A_full = A_loc (same codes and scales): X equals G bitwise, as in the bf16 path
+    rows = inputs.absorb_rows(3, 1, 0)                  # a chunk without history
+    lc, ls, _, _ = _fp8_rows(rows, 128)
+    G, X, F = _grams_fp8_gpu(lc, ls, lc, ls, 128)
+    torch = torch_mod()
+    assert torch.equal(X, G) and torch.equal(F, G)

@@ -99,3 +99,18 @@ def test_fp8_attention_equals_plain_on_exact_inputs():
     plain = oatt.dual_stream(dict(inp, q=q, sink_k=ks["sink"], cur_k=ks["cur"], hist_k=ks["hist"]))
     for k in ("A_loc", "A_full", "lse_loc", "lse_hist", "lse_full"):
         np.testing.assert_array_equal(got[k], plain[k])
+
+
+def test_fp8_grams_equal_plain_on_exact_rows():
+    from oracle import absorb as oab
+    rng = np.random.default_rng(5)
+    n, H, hd = 40, 3, 8
+    a = rng.integers(-4, 5, size=(n, H, hd)) * 0.5
+    b = rng.integers(-4, 5, size=(n, H, hd)) * 0.25
+    s = np.array([1.0, 2.0, 0.5], dtype=np.float32)           # powers of two: still exact
+    ac = fp8.quantize(a, s)
+    bc = fp8.quantize(b, s)
+    got = fp8.grams_fp8(ac.reshape(n, H * hd), s, bc.reshape(n, H * hd), s, hd)
+    want = oab.grams(a.reshape(n, H * hd), b.reshape(n, H * hd))
+    for k in ("G", "X", "F", "C"):
+        np.testing.assert_array_equal(got[k], want[k])
