@@ -384,8 +384,9 @@ def future_report(steps, warmup, torch):
 
 def fp8_report(steps, warmup, torch):
     """FP8 attention scores (e4m3 q and keys, per-head scales; bf16 values) against the bf16 kernel on
-    workloads 2 and 5 (dual stream), plus the quantiser's rate on workload 5's keys. Attention FLOP are
-    counted as for bf16 (4 n_q n_k d_h per head)."""
+    workloads 2 and 5 (dual stream), the quantiser's rate on the keys, and the FP8 statistics of one
+    4680-row chunk against the bf16 ones at workload 3's and 4's width. Attention FLOP are counted as
+    for bf16 (4 n_q n_k d_h per head); statistics FLOP 4 N d^2."""
     import ispa_inputs as inputs
     import kv_cache_attention_split_amd as ispa
     rows = []
@@ -431,7 +432,37 @@ def fp8_report(steps, warmup, torch):
                      "fp8_tflops_bf16_count": round(fl / ms["fp8"] / 1e9, 1),
                      "quantize_keys_ms": round(ms["quantize_keys"], 4),
                      "quantize_gbps": round(qbytes / ms["quantize_keys"] / 1e6, 1)})
-    print(json.dumps({"fp8_attention": rows}), flush=True)
+    stats = []
+    for cfg in (3, 4):
+        wl = inputs.CONFIGS[cfg]
+        d, n, hd = wl.d, inputs.CHUNK_TOKENS, wl.head_dim
+        g = torch.Generator(device="cuda").manual_seed(4321 + cfg)
+        a_loc = (0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16)
+        a_full = (0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16)
+        H = d // hd
+        s_loc = torch.empty(H, dtype=torch.float32, device="cuda")
+        s_full = torch.empty_like(s_loc)
+        ispa.ispa_fp8_head_scales(a_loc.view(n, H, hd), s_loc)
+        ispa.ispa_fp8_head_scales(a_full.view(n, H, hd), s_full)
+        c_loc = torch.empty((n, H, hd), dtype=torch.uint8, device="cuda")
+        c_full = torch.empty_like(c_loc)
+        ispa.ispa_fp8_quantize(a_loc.view(n, H, hd), s_loc, c_loc)
+        ispa.ispa_fp8_quantize(a_full.view(n, H, hd), s_full, c_full)
+        st = [torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)]
+        calls = {"bf16": lambda: ispa.ispa_absorb_accumulate(a_loc, a_full, st[0], st[1], st[2]),
+                 "fp8": lambda: ispa.ispa_absorb_accumulate_fp8(c_loc.view(n, d), s_loc, c_full.view(n, d), s_full,
+                                                                hd, st[0], st[1], st[2])}
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            for c in calls.values():
+                c()
+            torch.cuda.synchronize()
+        ms = {k: float(np.median([_time_calls(c, steps, warmup, torch) for _ in range(3)])) for k, c in calls.items()}
+        fl = 4.0 * n * d * d
+        stats.append({"workload": wl.name, "rows": n, "d": d, "bf16_ms": round(ms["bf16"], 4),
+                      "fp8_ms": round(ms["fp8"], 4), "speedup": round(ms["bf16"] / ms["fp8"], 3),
+                      "fp8_tflops": round(fl / ms["fp8"] / 1e9, 1)})
+    print(json.dumps({"fp8_attention": rows, "fp8_statistics": stats}), flush=True)
 
 
 def steady_report(steps, warmup, torch):
