@@ -485,7 +485,6 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
     ISPA_TRY(launch_zero_i32(info + p0, cnt, s));
     CPtrBatch g{};
     for (int i = 0; i < cnt; ++i) g.p[i] = G[p0 + i];
-    ISPA_TRY(launch_shift_copy(g, Lp(0), per_f, d, lambda, cnt, s));
 
     // W in the standard orientation (y = A W)
     const float *Wuse[kMaxBatch];
@@ -502,22 +501,30 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
       for (int i = 0; i < cnt; ++i) Wuse[i] = W[p0 + i];
     }
 
-    // B = (X - G) W
+    // B = (X - G) W: C = X - G goes to the factor's region first (a plain GEMM then reads one operand
+    // instead of subtracting two in its inner loop), and G + lambda I overwrites it afterwards
     {
+      CPtrBatch x{};
+      PtrBatch c{};
+      for (int i = 0; i < cnt; ++i) {
+        x.p[i] = X[p0 + i];
+        c.p[i] = Lp(i);
+      }
+      ISPA_TRY(launch_sub(x, g, c, d, cnt, s));
       GemmBatch b{};
       GemmShape sh{};
       sh.M = d; sh.N = d; sh.K = d;
       sh.lda = d; sh.ldb = d; sh.ldc = d;
-      sh.ta = 0; sh.tb = 0; sh.sub = 1;
+      sh.ta = 0; sh.tb = 0;
       sh.alpha = 1.f; sh.beta = 0.f;
       for (int i = 0; i < cnt; ++i) {
-        b.A[i] = X[p0 + i];
-        b.A2[i] = G[p0 + i];
+        b.A[i] = Lp(i);
         b.B[i] = Wuse[i];
         b.C[i] = Bp(i);
       }
       ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
     }
+    ISPA_TRY(launch_shift_copy(g, Lp(0), per_f, d, lambda, cnt, s));
 
     // blocked right-looking Cholesky: L L^T = G + lambda I
     for (int k = 0; k < nt; ++k) {

@@ -128,8 +128,10 @@ hipError_t launch_potrf_diag(float *L, int64_t L_stride, int d, int k0, int nb, 
                              int64_t Linv_stride, int32_t *info, int count, hipStream_t s);
 // out = in^T for d x d matrices (batch, per-layer pointers)
 hipError_t launch_transpose(const CPtrBatch &in, const PtrBatch &out, int d, int count, hipStream_t s);
-// out = a + b (elementwise, d x d)
+// out = a + b, out = a - b (elementwise, d x d)
 hipError_t launch_add(const CPtrBatch &a, const CPtrBatch &b, const PtrBatch &out, int d, int count,
+                      hipStream_t s);
+hipError_t launch_sub(const CPtrBatch &a, const CPtrBatch &b, const PtrBatch &out, int d, int count,
                       hipStream_t s);
 hipError_t launch_copy(const CPtrBatch &in, const PtrBatch &out, int d, int count, hipStream_t s);
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t s);

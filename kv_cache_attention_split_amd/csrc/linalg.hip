@@ -398,6 +398,7 @@ __global__ void transpose_kernel(CPtrBatch in, PtrBatch out, int d) {
   }
 }
 
+template <bool SUB>
 __global__ void add_kernel(CPtrBatch a, CPtrBatch b, PtrBatch out, int d) {
   const int layer = blockIdx.y;
   const int64_t n4 = (int64_t)d * d / 4;
@@ -405,7 +406,7 @@ __global__ void add_kernel(CPtrBatch a, CPtrBatch b, PtrBatch out, int d) {
        e += (int64_t)gridDim.x * blockDim.x) {
     const f32x4 x = ((const f32x4 *)a.p[layer])[e];
     const f32x4 y = ((const f32x4 *)b.p[layer])[e];
-    ((f32x4 *)out.p[layer])[e] = x + y;
+    ((f32x4 *)out.p[layer])[e] = SUB ? x - y : x + y;
   }
 }
 
@@ -513,7 +514,14 @@ hipError_t launch_transpose(const CPtrBatch &in, const PtrBatch &out, int d, int
 
 hipError_t launch_add(const CPtrBatch &a, const CPtrBatch &b, const PtrBatch &out, int d, int count,
                       hipStream_t s) {
-  hipLaunchKernelGGL(add_kernel, dim3(grid_for((int64_t)d * d / 4), count), dim3(kThreads), 0, s, a, b,
+  hipLaunchKernelGGL(add_kernel<false>, dim3(grid_for((int64_t)d * d / 4), count), dim3(kThreads), 0, s, a, b,
+                     out, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_sub(const CPtrBatch &a, const CPtrBatch &b, const PtrBatch &out, int d, int count,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(add_kernel<true>, dim3(grid_for((int64_t)d * d / 4), count), dim3(kThreads), 0, s, a, b,
                      out, d);
   return hipGetLastError();
 }
