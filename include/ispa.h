@@ -193,8 +193,10 @@ ispa_status ispa_attn_dual_fp8(int32_t n_heads, int32_t head_dim, float softmax_
  * without the full Q K^T matrix). For head h and key j of the cache (sink, then current, then history):
  *   scores[h * scores_head_stride + j] = (1/n_p) sum_i softmax_j(softmax_scale * q~_i . k_j)
  * the mean over the n_p proxy queries of the weight each gives key j (a head's scores sum to 1).
- * Two passes, no score matrix stored: the log-sum-exp of every proxy over all keys, then per-key sums
- * of exp(softmax_scale * q~_i . k_j - lse_i). Optionally, per token:
+ * Two passes, no score matrix stored: the log-sum-exp of every proxy over all keys (for d_h = 128 the
+ * keys are split over up to 16 workgroups per query tile when the proxy tiles alone would leave compute
+ * units idle; their partial (max, sum) states are merged in split order, so the result does not depend
+ * on scheduling), then per-key sums of exp(softmax_scale * q~_i . k_j - lse_i). Optionally, per token:
  *   token_score[j] = lambda * mean_h scores[h][j] + (1 - lambda) * hist_token_score[j]
  * Building the proxies (rotary positions of future frames applied to the mean of past pre-rotary
  * queries) is the caller's.
@@ -207,7 +209,8 @@ ispa_status ispa_attn_dual_fp8(int32_t n_heads, int32_t head_dim, float softmax_
  *   scores         out fp32 [H, scores_head_stride], scores_head_stride >= total keys
  *   lambda, hist_token_score, token_score   token_score (fp32 [total keys]) may be NULL: then no
  *                  token scores; hist_token_score may be NULL (historical score 0)
- *   ws             device scratch of at least ispa_future_scores_workspace(H, n_p) bytes
+ *   ws             device scratch of at least ispa_future_scores_workspace(H, n_p) bytes: the
+ *                  proxies' log-sum-exp rows, then the partial states of the split key ranges
  * Errors: ISPA_E_ARG (sizes, NULL or misaligned pointers, lambda not finite), ISPA_E_UNSUPPORTED,
  * ISPA_E_WORKSPACE, ISPA_E_HIP.
  * ------------------------------------------------------------------------------------------- */

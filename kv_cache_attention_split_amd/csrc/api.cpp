@@ -291,9 +291,12 @@ ispa_status ispa_attn_dual_fp8(int32_t n_heads, int32_t head_dim, float softmax_
 }
 
 // ------------------------------------------------------------------------------------------------
+// [lse: H x n_p fp32 | partial (max, sum) states of the key ranges: splits x H x n_p float pairs]
 size_t ispa_future_scores_workspace(int32_t n_heads, int64_t n_p) {
   if (n_heads <= 0 || n_p <= 0) return 0;
-  return (((size_t)n_heads * (size_t)n_p * sizeof(float)) + 255) / 256 * 256;
+  const size_t lse = round_up((size_t)n_heads * (size_t)n_p * sizeof(float), 256);
+  const size_t part = (size_t)lse_splits_for(n_p, n_heads) * (size_t)n_heads * (size_t)n_p * 2 * sizeof(float);
+  return lse + round_up(part, 256);
 }
 
 ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
@@ -343,6 +346,8 @@ ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim,
   a.hist_n = local_empty ? 0 : hist.n;
   a.hist_stride = local_empty ? 0 : hist.row_stride;
   a.lse_full = lse;
+  a.lse_part = (float *)((uint8_t *)ws + round_up((size_t)n_heads * (size_t)n_p * sizeof(float), 256));
+  a.lse_splits = lse_splits_for(n_p, n_heads);
   a.n_q = (int32_t)n_p;
   a.n_heads = n_heads;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;

@@ -514,7 +514,9 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int grp = w >> 2, wl = w & 3;
-  const int vid = xcd_remap(blockIdx.x, n_qt * a.n_heads);
+  const int nsplit = LSE_ONLY ? a.lse_splits : 1;   // key ranges per (head, query tile)
+  const int lin = xcd_remap(blockIdx.x, n_qt * a.n_heads * nsplit);
+  const int vid = lin / nsplit, split = lin % nsplit;
   const int head = vid / n_qt, qt = vid % n_qt;
   const int head_off = head * D;
   const int qi = qt * 256 + w * 32 + l32;
@@ -549,6 +551,9 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   const int nt_loc = (int)((n_loc + BK - 1) / BK);
   const int nt_hist = (int)((a.hist_n + BK - 1) / BK);
   const int nt = nt_loc + nt_hist;
+  // tiles of this workgroup: all of them, or one contiguous range per split in the LSE-only form
+  const int t0 = LSE_ONLY ? (int)((int64_t)split * nt / nsplit) : 0;
+  const int t1 = LSE_ONLY ? (int)((int64_t)(split + 1) * nt / nsplit) : nt;
 
   constexpr int NW = BK * D * 2 / 4096;   // copy instructions per group-A wave per tile
   int drow[NW], dcol8[NW];
@@ -634,18 +639,18 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     l = 0.f;
   };
 
-  // prologue: K(0) for everyone; group B then falls one barrier behind
+  // prologue: K(t0) for everyone; group B then falls one barrier behind
   if (grp == 0) {
-    dma_k(0, 0);
+    if (!LSE_ONLY || t0 < t1) dma_k(t0, t0 & 1);
     if (BIAS && wl == 0) dma_b(0, 0);
     ISPA_WAIT_VMCNT(0);
   }
   ISPA_LDS_BARRIER();
   if (grp == 1) ISPA_LDS_BARRIER();
 
-  for (int i = 0; i <= nt; ++i) {
+  for (int i = t0; i <= t1; ++i) {
     // ---- matrix phase: scores of tile i, value product of tile i-1 ----
-    if (i < nt) {
+    if (i < t1) {
       if constexpr (BIAS) {
         // the score accumulators start at b / tau instead of 0, so the softmax below sees
         // tau q.k + b (lane element v of block b is key 32b + 8(v/4) + 4hf + v%4)
@@ -726,16 +731,16 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     }
     // copies issued after this phase's LDS reads (see the kernel comment)
     if (grp == 0) {
-      if (i + 1 < nt) {
+      if (i + 1 < t1) {
         dma_k(i + 1, (i + 1) & 1);
         if (BIAS && wl == 0) dma_b(i + 1, (i + 1) & 1);
       }
-      if (!LSE_ONLY && i < nt) dma_v(i, i & 1);
+      if (!LSE_ONLY && i < t1) dma_v(i, i & 1);
     }
     ISPA_LDS_BARRIER();   // copies in flight stay in flight across this barrier
     // ---- vector phase: softmax of tile i ----
-    if (i - 1 == nt_loc - 1) snapshot_local();   // accumulator holds tiles 0 .. nt_loc-1
-    if (i < nt) {
+    if (!LSE_ONLY && i - 1 == nt_loc - 1) snapshot_local();   // accumulator holds tiles 0 .. nt_loc-1
+    if (i < t1) {
       const int n_valid = n_valid_of(i);
       if (n_valid < BK) {
 #pragma unroll
@@ -792,14 +797,35 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   }
   if (grp == 0) ISPA_LDS_BARRIER();     // matches group B's extra prologue barrier
 
-  if (nt_hist > 0) {
+  if constexpr (LSE_ONLY) {
+    // partial state of this key range: running max (log2 units) and exp-sum, merged by lse_merge_kernel
+    const float tot = l + swap_halves(l);
+    if (hf == 0 && qi < n_q) {
+      float *dst = a.lse_part + 2 * (((int64_t)split * a.n_heads + head) * n_q + qi);
+      *(f32x2 *)dst = f32x2{m, tot};
+    }
+  } else if (nt_hist > 0) {
     const float th = l + swap_halves(l);
     const float tl = l_loc + swap_halves(l_loc);
     const float tot = th + tl;
-    if constexpr (!LSE_ONLY) write_rows<D>(o, 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
+    write_rows<D>(o, 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
     write_lse(a.lse_full, (m + __log2f(tot)) * kLn2, head, qi, n_q, hf);
     write_lse(a.lse_hist, th > 0.f ? (m + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
   }
+}
+
+// lse = log sum_s l_s 2^(m_s) over the key ranges, in split order
+__global__ void __launch_bounds__(256) lse_merge_kernel(const float *part, int splits, int64_t n, float *lse) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part[2 * (s * n + i)]);
+  float sum = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float ms = part[2 * (s * n + i)], ls = part[2 * (s * n + i) + 1];
+    if (ls > 0.f) sum += ls * __builtin_amdgcn_exp2f(ms - mx);
+  }
+  lse[i] = sum > 0.f ? (mx + __log2f(sum)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -960,13 +986,27 @@ hipError_t launch_attn_fp8(const AttnArgs &a, int head_dim, hipStream_t s) {
   return hipGetLastError();
 }
 
+int lse_splits_for(int64_t n_q, int n_heads) {
+  // about one workgroup per CU: split the keys when the query tiles alone leave CUs idle
+  const int64_t tiles = ((n_q + 255) / 256) * (int64_t)n_heads;
+  if (tiles <= 0) return 1;
+  const int64_t sp = (256 + tiles / 2) / tiles;
+  return (int)(sp < 1 ? 1 : sp > 16 ? 16 : sp);
+}
+
 hipError_t launch_attn_lse_bf16(const AttnArgs &a, int head_dim, hipStream_t s) {
   if (has_bias(a) || a.a_loc != nullptr || a.a_full != nullptr) return hipErrorInvalidValue;
   if (ISPA_ATTN_PP && head_dim == 128) {
     const int n_qt = (a.n_q + 255) / 256;
     const int grid = n_qt * a.n_heads;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, true>), dim3(grid), dim3(512), 0, s, a, n_qt);
+    if (a.lse_part == nullptr || a.lse_full == nullptr || a.lse_splits != lse_splits_for(a.n_q, a.n_heads))
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, true>), dim3(grid * a.lse_splits), dim3(512), 0, s,
+                       a, n_qt);
+    const int64_t n = (int64_t)a.n_heads * a.n_q;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.lse_part,
+                       a.lse_splits, n, a.lse_full);
     return hipGetLastError();
   }
   return launch_attn_bf16_t<false>(a, head_dim, s);   // rows are not stored (NULL outputs)

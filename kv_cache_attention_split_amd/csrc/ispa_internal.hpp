@@ -32,10 +32,17 @@ struct AttnArgs {
   float bias_to_score;
   // FP8 scores: q and the keys as OCP e4m3 bytes with one scale per head each (device [H])
   const float *q_scale, *k_scale;
+  // log-sum-exp-only form: the keys are split into lse_splits ranges per (head, query tile); each writes
+  // its (running max in log2 units, exp-sum) to lse_part[(split * n_heads + head) * n_q + query]
+  float *lse_part;
+  int lse_splits;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s);
 // Log-sum-exp rows only (a.a_loc and a.a_full must be NULL, no bias): no value copies or products.
+// For head_dim 128 the keys are split over lse_splits_for(n_q, n_heads) workgroups per query tile and
+// a.lse_part must hold that many [n_heads, n_q] float2 partial states; a.lse_full receives the merge.
+int lse_splits_for(int64_t n_q, int n_heads);
 hipError_t launch_attn_lse_bf16(const AttnArgs &a, int head_dim, hipStream_t s);
 // Future-query importance: score[h][j] = (1/n_p) sum_i exp(tau q_i . k_j - lse[h][i]) over the keys
 // of three segments in cache order (bf16 keys and proxies, head_dim 64 or 128).

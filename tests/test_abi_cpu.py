@@ -214,8 +214,12 @@ def test_future_scores_argument_errors(L):
     assert call(tok=FAKE + 2) == _abi.ISPA_E_ARG
     assert call(ws=None) == _abi.ISPA_E_WORKSPACE
     assert call(ws_bytes=L.ispa_future_scores_workspace(2, 10) - 1) == _abi.ISPA_E_WORKSPACE
-    assert L.ispa_future_scores_workspace(2, 10) == 256
-    assert L.ispa_future_scores_workspace(12, 4680) == (12 * 4680 * 4 + 255) // 256 * 256
+    # lse rows (fp32 [H, n_p], 256-byte rounded) + split partial states (splits x [H, n_p] float2):
+    # 2 heads x 1 tile of 256 proxies -> 16 splits (capped); 12 heads x 19 tiles -> 1 split;
+    # 12 heads x 7 tiles (1560 proxies) -> 3 splits
+    assert L.ispa_future_scores_workspace(2, 10) == 256 + 16 * 2 * 10 * 8
+    assert L.ispa_future_scores_workspace(12, 4680) == 878 * 256 + 12 * 4680 * 8
+    assert L.ispa_future_scores_workspace(12, 1560) == 75008 + (3 * 12 * 1560 * 8 + 255) // 256 * 256
 
 
 def test_accumulate_argument_errors(L):
