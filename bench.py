@@ -96,8 +96,8 @@ class Layer:
 # rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
 # attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only
 # while the source is unchanged.
-ATTN_TRAFFIC = {"sha256": "6884d8344dd03cabe85622cee041f3cdf9140b186a812f0a96dbb7841aacb814",
-                "bytes_per_launch": 158820095}
+ATTN_TRAFFIC = {"sha256": "12e459fde9f5702687ca7c0c093c07fc5178e132af1e5e2bf8efe2824f951124",
+                "bytes_per_launch": 158831604}
 
 
 def attn_traffic():
