@@ -545,6 +545,7 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
         sh.lda = d; sh.ldb = nb; sh.ldc = d;
         sh.ta = 0; sh.tb = 1;
         sh.alpha = 1.f; sh.beta = 0.f;
+        sh.inplace = 1;                        // C = A: each row's nb columns in one workgroup
         for (int i = 0; i < cnt; ++i) {
           float *panel = Lp(i) + (int64_t)(k0 + nb) * d + k0;
           b.A[i] = panel;
@@ -597,6 +598,7 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
         sh.lda = nb; sh.ldb = d; sh.ldc = d;
         sh.ta = 0; sh.tb = 0;
         sh.alpha = 1.f; sh.beta = 0.f;
+        sh.inplace = 1;                        // C = B: each column's nb rows in one workgroup
         for (int i = 0; i < cnt; ++i) {
           b.A[i] = Vp(i) + k * linv_blk;
           b.B[i] = Bp(i) + (int64_t)k0 * d;
@@ -631,6 +633,7 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
         sh.lda = nb; sh.ldb = d; sh.ldc = d;
         sh.ta = 1; sh.tb = 0;
         sh.alpha = 1.f; sh.beta = 0.f;
+        sh.inplace = 1;                        // C = B, as in the forward sweep
         for (int i = 0; i < cnt; ++i) {
           b.A[i] = Vp(i) + k * linv_blk;
           b.B[i] = Bp(i) + (int64_t)k0 * d;

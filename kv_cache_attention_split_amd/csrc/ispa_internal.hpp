@@ -85,6 +85,11 @@ hipError_t launch_gram_fp8(int64_t n_rows, int d, int head_dim, const uint8_t *a
 //     sum_{tile} E[i*lde + j] * (alpha * (AB)[i][j]) in fp64 to part[p * tiles + tile]
 //   sym (dot mode, AB and E both symmetric): tiles above the diagonal are skipped (their partial
 //     is 0) and strictly-lower tiles count twice, so the partials still sum to <E, AB>
+//   inplace: C is also the A or B operand, and the product only mixes elements within 128 rows (C = A)
+//     or 128 columns (C = B) of it. Such a launch keeps 128 x 128 tiles whatever its size: a workgroup
+//     then reads everything its own tile depends on before it writes, and no other workgroup reads
+//     what it writes. (With 64 x 64 tiles two workgroups would share those 128 rows or columns, and
+//     one could read what the other has already overwritten.)
 // ------------------------------------------------------------------------------------------------
 constexpr int kMaxGemmBatch = 48;
 
@@ -101,6 +106,7 @@ struct GemmShape {
   int lda, ldb, ldc, lde;
   int ta, tb, lower, sub, dot;
   int sym;        // dot mode with a symmetric product and E: lower tiles only, off-diagonal ones x2
+  int inplace;    // C aliases an operand within one 128-row or 128-column extent: 128 tiles only
   float alpha, beta;
 };
 

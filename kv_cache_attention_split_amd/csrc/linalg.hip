@@ -458,9 +458,9 @@ hipError_t launch_gemm_f32(const GemmBatch &b, int count, const GemmShape &sh, d
     for (int p = 0; p < count; ++p) bb.C[p] = (float *)(part + (int64_t)p * part_stride);
   }
   // fewer than two 128-tiles per CU: 64-tiles (dot launches keep 128-tiles: their partial
-  // count is gemm_tiles)
+  // count is gemm_tiles; in-place launches too, so that one workgroup owns each 128 extent)
   const int t128 = gemm_tiles(sh.M, sh.N);
-  if (!sh.dot && (int64_t)t128 * count < 512) {
+  if (!sh.dot && !sh.inplace && (int64_t)t128 * count < 512) {
     dim3 grid(((sh.M + 63) / 64) * ((sh.N + 63) / 64), count);
     hipLaunchKernelGGL((gemm_f32_kernel<64, 32>), grid, dim3(kThreads), 0, s, bb, sh);
   } else {

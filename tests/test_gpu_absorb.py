@@ -164,6 +164,40 @@ def test_solve_against_oracle(d, n_rows, batch):
         assert rel_fro(to_host64(dWT[i]).T, refs[i]) <= 1e-3
 
 
+@pytest.mark.parametrize("batch", [30, 50])
+def test_solve_full_batch_uniform_and_repeatable(batch):
+    """Every layer of a full batch (30 = the 1.3B model's layers; 50 = launches of 48 and 2 layers) gets
+    the same statistics and weight, so within one launch every layer's dW must be the same bits, on two
+    calls in a row, and every launch must match the oracle. A launch whose workgroups do not all run at
+    once (more tiles than the CUs hold) exposes any workgroup that reads what another one has already
+    overwritten: the last layers' tiles start last. (Launches of different sizes may pick different
+    GEMM tiles, whose sums round differently, so layers of different launches are compared through the
+    oracle only.)"""
+    torch = torch_mod()
+    d, lam = 1536, 1e-2
+    _log(f"case: solve d={d} batch={batch} (identical layers)")
+    st = _stats64(d, 4680, 7, n_chunks=2)
+    G32 = st["G"].astype(np.float32)
+    X32 = st["X"].astype(np.float32)
+    W = inputs.weight(3, 7, d=d)
+    G, X, Wd = to_dev(G32, "f32"), to_dev(X32, "f32"), to_dev(W, "f32")
+    dW1, info = _solve_gpu([G] * batch, [X] * batch, [Wd] * batch, lam)
+    assert info.cpu().tolist() == [0] * batch
+    dW2, _ = _solve_gpu([G] * batch, [X] * batch, [Wd] * batch, lam)
+    per_launch = 48
+    G64 = G32.astype(np.float64)
+    ref = oab.ridge_delta_w(G64, X32.astype(np.float64) - G64, W, lam)
+    for p0 in range(0, batch, per_launch):
+        last = min(batch, p0 + per_launch) - 1
+        bad = [i for i in range(p0, last + 1) if not torch.equal(dW1[i], dW1[p0])]
+        assert not bad, f"layers {bad} differ from layer {p0}"
+        for i in (p0, last):
+            err = rel_fro(to_host64(dW1[i]), ref)
+            _log(f"  layer {i}: dW rel_fro {err:.2e}")
+            assert err <= 1e-3
+    assert all(torch.equal(a, b) for a, b in zip(dW1, dW2)), "two calls differ"
+
+
 def test_solve_14b_shape():
     d = 5120
     _log("case: solve d=5120")
