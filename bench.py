@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 
 
 def parse():
@@ -53,6 +54,9 @@ def parse():
                     help="time the TempCache merge and attention over merged vs original history")
     ap.add_argument("--gram-only-cfg", type=int, default=None,
                     help="time only the statistics update of one chunk at workload 3's or 4's width")
+    ap.add_argument("--absorb-cfg", type=int, default=None,
+                    help="time the whole Layer Absorb of workload 3 or 4 (all layers: statistics of the "
+                         "warmup chunks, one batched solve, one batched error, ranking) per layer")
     return ap.parse_args()
 
 
@@ -254,6 +258,73 @@ def gram_report(cfg, steps, warmup, torch):
                                                           "tflops": round(fl / ms / 1e9, 1),
                                                           "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}}),
           flush=True)
+
+
+def absorb_report(cfg, steps, warmup, torch):
+    """Layer Absorb of a whole model: the statistics of its warmup chunks for every layer, one batched
+    ridge solve, one batched error and the ranking (the step of workload 3 without its attention, and
+    the same at the 14B shape of workload 4). Rows are drawn on the device (bf16 N(0, 0.02^2); chunks
+    without history have A_full = A_loc, the others a perturbed copy), W ~ N(0, 1/d) per layer. Reports
+    ms per layer for each part, its rate (statistics 4 N d^2 per chunk on bf16 matrix cores; solve
+    13/3 d^3 and error 4 d^3 on fp32 matrix cores) and the selected layers."""
+    import ispa_inputs as inputs
+    import kv_cache_attention_split_amd as ispa
+    wl = inputs.CONFIGS[cfg]
+    d, n, L = wl.d, inputs.CHUNK_TOKENS, wl.n_layers
+    g = torch.Generator(device="cuda").manual_seed(4321 + cfg)
+    rows = []
+    for ch in wl.chunks:
+        a_loc = (0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16)
+        if ch.hist[1] > ch.hist[0]:
+            a_full = (a_loc.float() + 0.005 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16)
+        else:
+            a_full = a_loc
+        rows.append((a_loc, a_full))
+    Ws = [torch.randn((d, d), device="cuda", generator=g) / float(np.sqrt(d)) for _ in range(L)]
+    stats = [[torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)] for _ in range(L)]
+    Gs, Xs, Fs = [s_[0] for s_ in stats], [s_[1] for s_ in stats], [s_[2] for s_ in stats]
+    dW = [torch.empty((d, d), dtype=torch.float32, device="cuda") for _ in range(L)]
+    info = torch.zeros((L,), dtype=torch.int32, device="cuda")
+    eps = torch.zeros((L,), dtype=torch.float64, device="cuda")
+    ref = torch.zeros_like(eps)
+    ws_solve = torch.empty(ispa.ispa_absorb_solve_workspace(d, L), dtype=torch.uint8, device="cuda")
+    ws_err = torch.empty(ispa.ispa_layer_error_workspace(d, L), dtype=torch.uint8, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+
+    def run():
+        for s_ in stats:
+            for t in s_:
+                t.zero_()
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        for li in range(L):
+            for a_loc, a_full in rows:
+                ispa.ispa_absorb_accumulate(a_loc, a_full, Gs[li], Xs[li], Fs[li])
+        e[1].record()
+        ispa.ispa_absorb_solve(Gs, Xs, Ws, dW, wl.lam, info, ws_solve)
+        e[2].record()
+        ispa.ispa_layer_error(Gs, Xs, Fs, Ws, dW, eps, ref, ws_err)
+        e[3].record()
+        sel = ispa.ispa_rank_layers(eps.cpu().numpy().tolist(), wl.k_select)
+        return [e[i].elapsed_time(e[i + 1]) for i in range(3)], sel
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:
+        run()
+    for _ in range(warmup):
+        run()
+    res = [run() for _ in range(steps)]
+    ms = np.median(np.array([r[0] for r in res]), axis=0) / L
+    fl = (4.0 * n * d * d * len(rows), 13.0 / 3.0 * d ** 3, 4.0 * d ** 3)
+    peaks = (PEAK_BF16_TFLOPS, PEAK_F32_TFLOPS, PEAK_F32_TFLOPS)
+    out = {}
+    for name, t, f, p in zip(("statistics", "solve", "error"), ms, fl, peaks):
+        out[name] = {"ms_per_layer": round(float(t), 4), "tflops": round(f / t / 1e9, 1),
+                     "frac": round(f / t / 1e9 / p, 4)}
+    print(json.dumps({"workload": wl.name, "layers": L, "d": d, "chunks": len(rows), "rows_per_chunk": n,
+                      "absorb_ms_per_layer": round(float(ms.sum()), 4), **out,
+                      "info_nonzero": int((info != 0).sum().item()),
+                      "selected_l_layers": list(res[-1][1][0])}), flush=True)
 
 
 def tempcache_report(steps, warmup, torch):
@@ -560,6 +631,9 @@ def main():
         return
     if args.gram_only_cfg is not None:
         gram_report(args.gram_only_cfg, max(args.steps, 20), max(args.warmup, 5), torch)
+        return
+    if args.absorb_cfg is not None:
+        absorb_report(args.absorb_cfg, min(args.steps, 5), min(args.warmup, 1), torch)
         return
 
     if args.calibrate_copy:
