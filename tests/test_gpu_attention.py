@@ -95,6 +95,72 @@ def test_zero_queries_uniform_weights():
     check_attention(out, ref, "bf16")
 
 
+def _scores_against(inp, kstar):
+    """tau q . k* for every (head, query) in float64 on the exact input values: [H, n_q]."""
+    q = inp["q"].astype(np.float64)
+    return float(inp["scale"]) * np.einsum("qhd,hd->hq", q, kstar.astype(np.float64))
+
+
+@pytest.mark.parametrize("dh", [64, 128])
+def test_equal_keys_closed_form(dh):
+    """P-3 on the device: when every key equals one k*, all weights are equal, so lse_X = tau q.k* +
+    log n_X and A_X is the mean of segment X's values (closed forms, no oracle code)."""
+    n_q, n_s, n_c, n_h = 160, 70, 90, 300
+    inp = inputs.attention_case(21, 2, dh, n_q, n_s, n_c, n_h, dtype="bf16")
+    kstar = inp["cur_k"][0].copy()
+    for name in ("sink_k", "cur_k", "hist_k"):
+        inp[name][:] = kstar[None]
+    _log(f"case: all keys equal, d_h={dh}")
+    _, out = run_attn(inp)
+    s = _scores_against(inp, kstar)
+    for name, n in (("lse_loc", n_s + n_c), ("lse_hist", n_h), ("lse_full", n_s + n_c + n_h)):
+        want = s + math.log(n)
+        got = to_host64(out[name])
+        err = float(np.max(np.abs(got - want) / np.maximum(np.abs(want), 1.0)))
+        assert err <= 1e-6, (name, err)
+    v_loc = np.concatenate([inp["sink_v"], inp["cur_v"]]).astype(np.float64).mean(axis=0)
+    v_all = np.concatenate([inp["sink_v"], inp["cur_v"], inp["hist_v"]]).astype(np.float64).mean(axis=0)
+    for name, m in (("a_loc", v_loc), ("a_full", v_all)):
+        got = to_host64(out[name]).reshape(n_q, 2, dh)
+        err = float(np.max(np.abs(got - m[None])))
+        assert err <= 2.0 ** -8 * float(np.max(np.abs(m))) + 1e-6, (name, err)
+
+
+def test_single_key_gives_its_value():
+    """P-3 on the device: one local key and no history give A_loc = A_full = v of that key exactly and
+    lse_loc = lse_full = tau q.k, lse_hist = -inf."""
+    torch = torch_mod()
+    inp = inputs.attention_case(22, 2, 128, 100, 0, 1, 0, dtype="bf16")
+    _, out = run_attn(inp)
+    v = inp["cur_v"][0].astype(np.float64)
+    got = to_host64(out["a_loc"]).reshape(100, 2, 128)
+    assert np.array_equal(got, np.broadcast_to(v, got.shape))
+    assert torch.equal(out["a_full"], out["a_loc"])
+    want = _scores_against(inp, inp["cur_k"][0])
+    for name in ("lse_loc", "lse_full"):
+        got = to_host64(out[name])
+        assert float(np.max(np.abs(got - want) / np.maximum(np.abs(want), 1.0))) <= 1e-6, name
+    assert np.all(np.isneginf(to_host64(out["lse_hist"])))
+
+
+def test_constant_values_give_constant_output():
+    """P-3 on the device: when every value row equals one c, A_loc = A_full = c whatever the weights
+    (up to the bf16 rounding of the probabilities and of the output)."""
+    n_q, n_s, n_c, n_h = 130, 40, 90, 200
+    inp = inputs.attention_case(23, 2, 128, n_q, n_s, n_c, n_h, dtype="bf16")
+    c = inp["cur_v"][0].copy()
+    for name in ("sink_v", "cur_v", "hist_v"):
+        inp[name][:] = c[None]
+    _, out = run_attn(inp)
+    c64 = c.astype(np.float64)
+    for name in ("a_loc", "a_full"):
+        got = to_host64(out[name]).reshape(n_q, 2, 128)
+        err = float(np.max(np.abs(got - c64[None]) / np.maximum(np.abs(c64[None]), 1e-3)))
+        assert err <= 2.0 ** -7, (name, err)
+    ref = oatt.dual_stream(inp)
+    check_attention(out, ref, "bf16")
+
+
 def test_deterministic_repeat():
     inp = inputs.attention_case(11, 2, 128, 200, 64, 100, 250, dtype="bf16")
     dev, out1 = run_attn(inp)
