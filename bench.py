@@ -155,7 +155,47 @@ def cpu_baseline(wl):
                    f"{t_abs:.2f} s; rate = the GPU's algorithmic FLOP count for that work / time"),
         "attn_tflops": round(f_att / t_att / 1e12, 6),
         "absorb_ms_per_layer": round(t_abs * 1e3 / n_abs_layers, 1),
+        "cpu_model": _cpu_model(),
+        "blas": _blas_name(),
+        "brute_force": _brute_force_leg(),
     }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_name():
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')}"
+    except Exception:   # noqa: BLE001 - the build description is optional
+        return None
+
+
+def _brute_force_leg():
+    """The pure-Python loop form of the oracle (one core) on 16 query rows of workload 1 (2 heads x 64,
+    all 704 keys), timed on its own."""
+    import ispa_inputs as inputs
+    from oracle import brute
+    inp = inputs.attention_inputs(1, 0, 0)
+    rows = 16
+    q = inp["q"][:rows].tolist()
+    k = np.concatenate([inp["sink_k"], inp["cur_k"], inp["hist_k"]]).tolist()
+    v = np.concatenate([inp["sink_v"], inp["cur_v"], inp["hist_v"]]).tolist()
+    t0 = time.perf_counter()
+    brute.attention_loops(q, k, v, float(inp["scale"]))
+    t = time.perf_counter() - t0
+    H, dh = inp["q"].shape[1], inp["q"].shape[2]
+    return {"rows": rows, "keys": len(k), "heads": H, "head_dim": dh, "seconds": round(t, 3),
+            "gflops": round(attn_flops(rows, len(k), H, dh) / t / 1e9, 4), "cores": 1}
 
 
 def _time_calls(call, n, warmup, torch, cold_scratch=None):
