@@ -198,6 +198,30 @@ def test_solve_full_batch_uniform_and_repeatable(batch):
     assert all(torch.equal(a, b) for a, b in zip(dW1, dW2)), "two calls differ"
 
 
+def test_solve_14b_full_batch_uniform_and_repeatable():
+    """The 14B model's batch (40 layers at d = 5120, one launch of every GEMM) on identical layers: the
+    same bits in every layer and on two calls, and the oracle's dW."""
+    torch = torch_mod()
+    d, batch, lam = 5120, 40, 1e-2
+    _log(f"case: solve d={d} batch={batch} (identical layers)")
+    st = _stats64(d, 5600, 1, cfg=4)
+    G32 = st["G"].astype(np.float32)
+    X32 = st["X"].astype(np.float32)
+    W = inputs.weight(4, 1)
+    G, X, Wd = to_dev(G32, "f32"), to_dev(X32, "f32"), to_dev(W, "f32")
+    dW1, info = _solve_gpu([G] * batch, [X] * batch, [Wd] * batch, lam)
+    assert info.cpu().tolist() == [0] * batch
+    dW2, _ = _solve_gpu([G] * batch, [X] * batch, [Wd] * batch, lam)
+    bad = [i for i in range(batch) if not torch.equal(dW1[i], dW1[0])]
+    assert not bad, f"layers {bad} differ from layer 0"
+    assert all(torch.equal(a, b) for a, b in zip(dW1, dW2)), "two calls differ"
+    G64 = G32.astype(np.float64)
+    ref = oab.ridge_delta_w(G64, X32.astype(np.float64) - G64, W, lam)
+    err = rel_fro(to_host64(dW1[batch - 1]), ref)
+    _log(f"  dW rel_fro {err:.2e}")
+    assert err <= 1e-3
+
+
 def test_solve_14b_shape():
     d = 5120
     _log("case: solve d=5120")
