@@ -6,7 +6,8 @@ One step = one full ISPA warmup of a Wan-1.3B-shaped model (workload "wan1.3b-wa
 0 -> 9 frames) each followed by the warmup-statistics update, then the batched ridge solve of all
 30 layers (d = 1536, lambda = 1e-2), their reconstruction errors, and the selection of K = 15
 L-Layers (errors copied to the host and ranked there). Inputs are seeded synthetic tensors already
-resident in HBM when the timed region starts.
+resident in HBM when the timed region starts. `--workload-cfg 4` runs the same step at the 14B shape
+(40 layers x 40 heads, d = 5120, K = 20).
 
 Prints one JSON line. `value` is the step's algorithmic TFLOP/s (attention 4 n_q n_keys H d_h per
 call, statistics 4 N d^2 per chunk, solve 13/3 d^3, error 4 d^3 per layer) over the measured step
@@ -38,6 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (tuning only)")
+    ap.add_argument("--workload-cfg", type=int, default=3, choices=(3, 4),
+                    help="workload of the timed step: 3 = the Wan-1.3B warmup (default), 4 = the 14B warmup "
+                         "(40 layers x 40 heads, d = 5120)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (HBM counter calibration)")
@@ -122,16 +126,17 @@ def cpu_baseline(wl):
     from oracle import attention as oatt
     cores = len(os.sched_getaffinity(0))
     H, dh, d = wl.n_heads, wl.head_dim, wl.d
-    # (a) attention of all 4680 query rows of chunk 4 (all heads, 18720 keys)
+    # (a) attention of all 4680 query rows of chunk 4 (all heads, 18720 keys); at 40 heads the first
+    # frame's 1560 rows, so that the sample stays within about half a minute
     inp = inputs.attention_inputs(wl.cfg, 0, 3)
-    rows = np.arange(inp["q"].shape[0])
+    rows = np.arange(inp["q"].shape[0] if H <= 16 else inputs.FRAME_TOKENS)
     t0 = time.perf_counter()
     oatt.dual_stream(inp, rows=rows)
     t_att = time.perf_counter() - t0
     n_keys = sum(inp[k].shape[0] for k in ("sink_k", "cur_k", "hist_k"))
     f_att = attn_flops(len(rows), n_keys, H, dh)
     # (b) Layer Absorb of 8 layers: statistics over the 4 warmup chunks, solve, error
-    n_abs_layers = 8
+    n_abs_layers = 8 if d <= 2048 else 1
     t_abs = 0.0
     f_abs = 0.0
     for layer in range(n_abs_layers):
@@ -683,7 +688,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    wl = inputs.CONFIGS[3]
+    wl = inputs.CONFIGS[args.workload_cfg]
     n_layers = args.layers or wl.n_layers
     H, dh, d = wl.n_heads, wl.head_dim, wl.d
     n_q = inputs.CHUNK_TOKENS
@@ -709,7 +714,7 @@ def main():
     Fs = [s[2] for s in stats]
     Ws = [L.w for L in layers]
 
-    seg_keys = [sum(inputs.CONFIGS[3].segment_sizes(c)[k] for k in ("n_sink", "n_cur", "n_hist"))
+    seg_keys = [sum(wl.segment_sizes(c)[k] for k in ("n_sink", "n_cur", "n_hist"))
                 for c in range(len(wl.chunks))]
     flops_attn = sum(attn_flops(n_q, nk, H, dh) for nk in seg_keys) * n_layers
     flops_stats = 4.0 * n_q * len(wl.chunks) * d * d * n_layers
@@ -791,7 +796,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) queries/values, AR(1) rho=0.95 keys across latent frames, W ~ N(0,1/d))",
-        "config": {"workload": "wan1.3b-warmup", "layers": n_layers, "chunks": len(wl.chunks),
+        "config": {"workload": wl.name, "layers": n_layers, "chunks": len(wl.chunks),
                    "heads": H, "head_dim": dh, "queries_per_chunk": n_q,
                    "keys_per_chunk": seg_keys, "lambda": wl.lam, "k_select": min(wl.k_select, n_layers)},
         "attn_tflops": round(att_tflops, 1),
@@ -806,7 +811,8 @@ def main():
         "selected_l_layers": sel,
         "roofline": {"kernel": "attn_dual_bf16_pp_kernel", "bound": "mfma",
                      "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic(),
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": attn_traffic() if wl.cfg == 3 else None,
                      "avg_launch_ms": round(att_avg_ms, 5),
                      "flops_per_launch": att_flops_per_launch},
         "setup_s": round(t_setup, 1),
