@@ -74,7 +74,11 @@ __global__ void __launch_bounds__(64 * kWaves) kv_merge_kernel(MergeArgs a) {
   const int count = m1 > m0 ? m1 - m0 : 0;
   if (lane == 0 && a.bias_out != nullptr) a.bias_out[g] = count > 0 ? logf((float)count) : -INFINITY;
   const float fc = (float)count;
-  for (int c0 = 8 * lane; c0 < a.width; c0 += 8 * 64 * P) {
+  // The pass loop is wave-uniform: every lane runs every pass, also lanes whose columns lie past the
+  // row end (width < 512 P), because the member indices below are loaded one per lane and broadcast
+  // with readlane, which must read a lane that has executed the load.
+  for (int cb = 0; cb < a.width; cb += 8 * 64 * P) {
+    const int c0 = cb + 8 * lane;
     float sk[P][8], sv[P][8];
 #pragma unroll
     for (int p = 0; p < P; ++p)
@@ -89,7 +93,7 @@ __global__ void __launch_bounds__(64 * kWaves) kv_merge_kernel(MergeArgs a) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int c = c0 + 8 * 64 * p;
-        const int cc = c < a.width ? c : c0;   // lanes past the row end reload their first chunk
+        const int cc = c < a.width ? c : 0;    // lanes past the row end reload column 0 (not stored)
         load8<BF16>(a.k, base + cc, xk[p]);
         load8<BF16>(a.v, base + cc, xv[p]);
       }

@@ -165,6 +165,26 @@ def test_merge_vs_oracle(dt, H, dh, n, G, max_size, pad):
     _check_merge(k, v, off, mem_all, gk, gv, gb, dt)
 
 
+@pytest.mark.parametrize("dt,H,dh,n,G", [("bf16", 1, 128, 600, 12), ("f32", 1, 64, 400, 9),
+                                         ("bf16", 2, 64, 700, 10), ("bf16", 1, 8, 300, 7)])
+def test_merge_large_groups_narrow_rows(dt, H, dh, n, G):
+    """Groups of 40 to 100 members on rows narrower than one pass of the wave (H * d_h < 512): the member
+    indices of a group are read one per lane and broadcast, so every lane must take part in that read,
+    also lanes whose columns lie past the row end; groups over 64 members cross a batch of indices."""
+    _log(f"case: merge {dt} H={H} d_h={dh} rows={n} groups={G} of 40-100 members")
+    rng = np.random.default_rng(7 * n + G)
+    k = rng.standard_normal((n, H, dh)).astype(np.float32)
+    v = rng.standard_normal((n, H, dh)).astype(np.float32)
+    if dt == "bf16":
+        k, v = inputs.round_bf16(k), inputs.round_bf16(v)
+    sizes = rng.integers(40, 101, size=G)
+    mem_all = rng.choice(n, size=int(sizes.sum()), replace=True).astype(np.int32)
+    off = np.zeros(G + 1, dtype=np.int32)
+    off[1:] = np.cumsum(sizes)
+    gk, gv, gb = _merge_gpu(k, v, off, mem_all, dt)
+    _check_merge(k, v, off, mem_all, gk, gv, gb, dt)
+
+
 def test_merge_identical_keys_are_bitwise_and_bad_members_are_skipped():
     inp = inputs.static_history_case(5, n_heads=2, head_dim=64, n_q=8, n_sink=4, n_cur=8, n_frames=7,
                                      frame_tokens=40, static_frac=0.5)
