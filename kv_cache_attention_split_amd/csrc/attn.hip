@@ -96,16 +96,13 @@ __device__ __forceinline__ void dma_tile(const SegRun &run, int64_t j0, int head
   const uint16_t *base0 = VALUE ? run.v0 : run.k0;
   const uint16_t *base1 = VALUE ? run.v1 : run.k1;
   if (in_first || in_second) {
-    // whole tile inside one sub-run: uniform base + 32-bit per-lane offset
+    // whole tile inside one sub-run: no clamping; each lane's 64-bit address is the tile base plus
+    // its row and chunk offset (rows < BK, strides < 2^23 elements)
     const uint16_t *tb = (in_first ? base0 + j0 * run.s0 : base1 + (j0 - run.split) * run.s1) + head_off;
-    const uint32_t st = (uint32_t)(in_first ? run.s0 : run.s1);
+    const int64_t st = in_first ? run.s0 : run.s1;
 #pragma unroll
-    for (int ii = 0; ii < NW; ++ii) {
-      const uint32_t off = (uint32_t)rr[ii] * st + (uint32_t)cc8[ii];
-      __builtin_amdgcn_global_load_lds((const void *)(tb + off),
-                                       (__attribute__((address_space(3))) void *)(lds_tile + 1024 * (w + 4 * ii)),
-                                       16, 0, 0);
-    }
+    for (int ii = 0; ii < NW; ++ii)
+      copy_to_lds<16>(tb + (int64_t)rr[ii] * st + cc8[ii], lds_tile + 1024 * (w + 4 * ii));
     return;
   }
 #pragma unroll
@@ -115,9 +112,7 @@ __device__ __forceinline__ void dma_tile(const SegRun &run, int64_t j0, int head
     const bool second = j >= run.split;
     const int64_t jj = second ? j - run.split : j;
     const uint16_t *src = (second ? base1 : base0) + jj * (second ? run.s1 : run.s0) + head_off + cc8[ii];
-    __builtin_amdgcn_global_load_lds((const void *)src,
-                                     (__attribute__((address_space(3))) void *)(lds_tile + 1024 * (w + 4 * ii)),
-                                     16, 0, 0);
+    copy_to_lds<16>(src, lds_tile + 1024 * (w + 4 * ii));
   }
 }
 
@@ -142,9 +137,7 @@ __device__ __forceinline__ void dma_tile_k8(const AttnArgs &a, bool hist, int64_
     j = j < n ? j : n - 1;
     const bool second = j >= split;
     const uint8_t *src = (second ? k1 + (j - split) * s1 : k0 + j * s0) + head_off + cc[ii];
-    __builtin_amdgcn_global_load_lds((const void *)src,
-                                     (__attribute__((address_space(3))) void *)(lds_tile + 1024 * (w + 4 * ii)),
-                                     16, 0, 0);
+    copy_to_lds<16>(src, lds_tile + 1024 * (w + 4 * ii));
   }
 }
 
@@ -595,8 +588,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     const int64_t nseg = hist ? a.hist_n : n_loc;
     int64_t j = tile_j0(t) + lane;
     j = j < nseg ? j : nseg - 1;
-    __builtin_amdgcn_global_load_lds((const void *)bias_ptr(a, hist, j, head),
-                                     (__attribute__((address_space(3))) void *)bbuf[buf], 4, 0, 0);
+    copy_to_lds<4>(bias_ptr(a, hist, j, head), bbuf[buf]);
   };
   auto kread = [&](int buf, int i) -> bf16x8 {
     const int kk = i / NB, b = i % NB;

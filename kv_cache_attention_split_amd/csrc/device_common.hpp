@@ -58,6 +58,22 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
 
 __device__ __forceinline__ uint32_t u4_get(const u32x4 &v, int i) { return v[i]; }
 
+// Direct global -> LDS copy of `Bytes` (4 or 16) per lane into LDS at `lds` (the wave's block; lane l
+// lands at byte Bytes * l of it). The lane's source address goes to the instruction as a full 64-bit
+// value held in that lane's VGPRs: the empty asm hides how the address was formed, so the copy is
+// always issued in the per-lane 64-bit form (`global_load_lds_dword* v[a:a+1], off`), never as a
+// scalar base plus a 32-bit lane offset (the form two discarded experimental attention builds used
+// when they faulted the GPU).
+template <int Bytes>
+__device__ __forceinline__ void copy_to_lds(const void *src, void *lds) {
+  static_assert(Bytes == 4 || Bytes == 16, "4- or 16-byte copies");
+  asm("" : "+v"(src));
+  if constexpr (Bytes == 16)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+}
+
 // Lanes l and l^32 exchange a value (the two halves of a wave hold the same MFMA column).
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);

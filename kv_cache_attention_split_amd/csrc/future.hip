@@ -118,14 +118,12 @@ __global__ void __launch_bounds__(kThreads, 1) future_colsum_kernel(ScoreArgs a)
       int64_t i = row0 + crow[ii];
       i = i < a.n_p ? i : a.n_p - 1;
       const uint16_t *src = a.q + i * a.q_stride + head_off + ccol[ii];
-      __builtin_amdgcn_global_load_lds((const void *)src,
-                                       (__attribute__((address_space(3))) void *)(qs + 1024 * (w + kWaves * ii)),
-                                       16, 0, 0);
+      copy_to_lds<16>(src, qs + 1024 * (w + kWaves * ii));
     }
     if (w == 0) {
       const int64_t i = row0 + lane;
       const float *src = i < a.n_p ? lse_h + i : (const float *)(uintptr_t)zinf;
-      __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)ls, 4, 0, 0);
+      copy_to_lds<4>(src, ls);
     }
   };
 

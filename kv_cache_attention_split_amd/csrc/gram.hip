@@ -153,9 +153,7 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
       const int64_t n = (int64_t)s * BR + crow[ii];
       const uint8_t *p = src[ii] + (int64_t)s * stage_bytes;
       p = n < n_rows ? p : (const uint8_t *)(uintptr_t)zero_row;
-      __builtin_amdgcn_global_load_lds((const void *)p,
-                                       (__attribute__((address_space(3))) void *)(slot + 1024 * (w + 4 * ii)),
-                                       16, 0, 0);
+      copy_to_lds<16>(p, slot + 1024 * (w + 4 * ii));
     }
   };
   auto read_stage = [&](const uint8_t *slot, StageOps &o) {
@@ -371,9 +369,7 @@ __global__ void __launch_bounds__(kThreads, 2) gram_fp8_kernel(GramArgs8 g) {
       const int64_t n = (int64_t)s * BR8 + crow[ii];
       const uint8_t *p = src[ii] + (int64_t)s * stage_bytes;
       p = n < n_rows ? p : (const uint8_t *)(uintptr_t)zero_row;
-      __builtin_amdgcn_global_load_lds((const void *)p,
-                                       (__attribute__((address_space(3))) void *)(slot + 1024 * (w + 4 * ii)),
-                                       16, 0, 0);
+      copy_to_lds<16>(p, slot + 1024 * (w + 4 * ii));
     }
   };
   auto read_stage = [&](const uint8_t *slot, StageOps8 &o) {

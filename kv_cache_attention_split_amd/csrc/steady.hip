@@ -127,9 +127,7 @@ __global__ void __launch_bounds__(kThreads, 2) proj_bf16_kernel(ProjArgs g) {
     for (int ii = 0; ii < kCopies; ++ii) {
       const uint8_t *p = (src[ii] != nullptr && s < nst) ? src[ii] + (int64_t)s * RB
                                                           : (const uint8_t *)(uintptr_t)zero;
-      __builtin_amdgcn_global_load_lds((const void *)p,
-                                       (__attribute__((address_space(3))) void *)(slot + 1024 * (w + 4 * ii)),
-                                       16, 0, 0);
+      copy_to_lds<16>(p, slot + 1024 * (w + 4 * ii));
     }
   };
   // MFMA operand of 32 rows starting at rb, 16-k step t: lane (l32, hf) reads row rb + l32, k chunk
