@@ -267,12 +267,15 @@ def ispa_absorb_accumulate(a_loc, a_full, G, X, F=None, ws=None, stream=None) ->
     n, d = (int(x) for x in a_loc.shape)
     if tuple(a_full.shape) != (n, d) or a_full.dtype != a_loc.dtype:
         raise ValueError("a_loc and a_full must match")
-    for t in (a_loc, a_full, G, X) + ((F,) if F is not None else ()):
+    for t, what in ((a_loc, "a_loc"), (a_full, "a_full")):
+        _device_tensor(t, what)
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+    _square_list([G, X] + ([F] if F is not None else []), d, 3 if F is not None else 2, "statistic")
+    ws_ptr, ws_bytes = _workspace(ws)
     st = lib().ispa_absorb_accumulate(
         _dtype_code(a_loc), n, d, _ptr(a_loc), _ptr(a_full), _ptr(G), _ptr(X), _ptr(F),
-        _ptr(ws), 0 if ws is None else int(ws.numel() * ws.element_size()), _stream_handle(stream))
+        ws_ptr, ws_bytes, _stream_handle(stream))
     _check(st, "ispa_absorb_accumulate")
 
 
@@ -280,11 +283,18 @@ def ispa_absorb_accumulate_fp8(a_loc, s_loc, a_full, s_full, head_dim: int, G, X
     """FP8 statistics: a_loc, a_full uint8 e4m3 codes [n, d] (contiguous), s_loc, s_full float32 per-head
     scales [d / head_dim]; G, X, F as for ispa_absorb_accumulate."""
     n, d = (int(x) for x in a_loc.shape)
+    torch = _torch()
     if tuple(a_full.shape) != (n, d):
         raise ValueError("a_loc and a_full must match")
-    for t in (a_loc, a_full, G, X) + ((F,) if F is not None else ()):
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    for t, what in ((a_loc, "a_loc"), (a_full, "a_full")):
+        _device_tensor(t, what)
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("FP8 rows must be contiguous uint8 (e4m3 codes)")
+    if head_dim <= 0 or d % head_dim != 0:
+        raise ValueError("d must be a multiple of head_dim")
+    for t, what in ((s_loc, "s_loc"), (s_full, "s_full")):
+        _vector(t, d // head_dim, torch.float32, what)
+    _square_list([G, X] + ([F] if F is not None else []), d, 3 if F is not None else 2, "statistic")
     st = lib().ispa_absorb_accumulate_fp8(n, d, int(head_dim), _ptr(a_loc), _ptr(s_loc), _ptr(a_full), _ptr(s_full),
                                           _ptr(G), _ptr(X), _ptr(F), None, 0, _stream_handle(stream))
     _check(st, "ispa_absorb_accumulate_fp8")
@@ -299,6 +309,46 @@ def _ptr_array(ts: Sequence) -> ctypes.Array:
     return arr
 
 
+def _device_tensor(t, what: str) -> None:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+
+
+def _square_list(ts: Sequence, d: int, batch: int, what: str) -> ctypes.Array:
+    """Device pointers of `batch` contiguous float32 [d, d] GPU matrices."""
+    torch = _torch()
+    if len(ts) != batch:
+        raise ValueError(f"{what} must have one entry per layer ({batch}), got {len(ts)}")
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or tuple(t.shape) != (d, d) or \
+                not t.is_contiguous():
+            raise ValueError(f"every {what} entry must be a contiguous float32 [{d}, {d}] tensor")
+        _device_tensor(t, what)
+    return _ptr_array(ts)
+
+
+def _vector(t, n: int, dtype, what: str, optional: bool = False) -> None:
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{what} is required")
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.dim() != 1 or t.shape[0] < n or \
+            not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous {dtype} vector of at least {n} entries")
+    _device_tensor(t, what)
+
+
+def _workspace(ws):
+    if ws is None:
+        return None, 0
+    _device_tensor(ws, "ws")
+    if not ws.is_contiguous():
+        raise ValueError("ws must be contiguous")
+    return _ptr(ws), int(ws.numel() * ws.element_size())
+
+
 def ispa_absorb_solve_workspace(d: int, batch: int) -> int:
     return int(lib().ispa_absorb_solve_workspace(int(d), int(batch)))
 
@@ -308,12 +358,14 @@ def ispa_absorb_solve(G: Sequence, X: Sequence, W: Sequence, dW: Sequence, lam: 
     """dW_l = (G_l + lam I)^-1 (X_l - G_l) W_l for each layer l (lists of [d, d] fp32 tensors)."""
     batch = len(G)
     d = int(G[0].shape[0]) if batch else 0
-    if not (len(X) == len(W) == len(dW) == batch):
-        raise ValueError("G, X, W, dW must have one entry per layer")
+    torch = _torch()
+    ptrs = [_square_list(m, d, batch, name) for m, name in ((G, "G"), (X, "X"), (W, "W"), (dW, "dW"))]
+    if batch:
+        _vector(info, batch, torch.int32, "info")
+    ws_ptr, ws_bytes = _workspace(ws)
     st = lib().ispa_absorb_solve(
-        d, batch, ctypes.c_float(lam), _ptr_array(G), _ptr_array(X), _ptr_array(W),
-        1 if w_is_linear_weight else 0, _ptr_array(dW), _ptr(info), _ptr(ws),
-        0 if ws is None else int(ws.numel() * ws.element_size()), _stream_handle(stream))
+        d, batch, ctypes.c_float(lam), ptrs[0], ptrs[1], ptrs[2], 1 if w_is_linear_weight else 0, ptrs[3],
+        _ptr(info), ws_ptr, ws_bytes, _stream_handle(stream))
     _check(st, "ispa_absorb_solve")
 
 
@@ -326,10 +378,15 @@ def ispa_layer_error(G: Sequence, X: Sequence, F: Sequence, W: Sequence, dW: Seq
     """eps_l = ||A_loc (W + dW) - A_full W||_F^2 from the statistics; ref_l = ||A_full W||_F^2."""
     batch = len(G)
     d = int(G[0].shape[0]) if batch else 0
+    torch = _torch()
+    ptrs = [_square_list(m, d, batch, name) for m, name in ((G, "G"), (X, "X"), (F, "F"), (W, "W"), (dW, "dW"))]
+    if batch:
+        _vector(eps, batch, torch.float64, "eps")
+        _vector(ref, batch, torch.float64, "ref", optional=True)
+    ws_ptr, ws_bytes = _workspace(ws)
     st = lib().ispa_layer_error(
-        d, batch, _ptr_array(G), _ptr_array(X), _ptr_array(F), _ptr_array(W),
-        1 if w_is_linear_weight else 0, _ptr_array(dW), _ptr(eps), _ptr(ref), _ptr(ws),
-        0 if ws is None else int(ws.numel() * ws.element_size()), _stream_handle(stream))
+        d, batch, ptrs[0], ptrs[1], ptrs[2], ptrs[3], 1 if w_is_linear_weight else 0, ptrs[4],
+        _ptr(eps), _ptr(ref), ws_ptr, ws_bytes, _stream_handle(stream))
     _check(st, "ispa_layer_error")
 
 

@@ -327,3 +327,43 @@ def test_kv_plan_matches_oracle():
         ref = ost.layer_plan([bool(f) for f in flags], ns, nh, nc)
         assert kept == ref["hist_kept"]
         assert ev == ref["evicted_tokens"]
+
+
+def test_absorb_bindings_validate_every_entry():
+    """The Python binding checks every per-layer matrix and output vector before the library is called
+    (a wrong dtype or a short vector would otherwise let the kernels write out of bounds)."""
+    import torch
+    import kv_cache_attention_split_amd as ispa
+    d = 64
+    m = lambda dt=torch.float32, shape=(d, d): torch.zeros(shape, dtype=dt)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    info = torch.zeros(2, dtype=torch.int32)
+    eps = torch.zeros(2, dtype=torch.float64)
+    good = [m(), m()]
+    cases = [
+        lambda: ispa.ispa_absorb_solve([m(), m(torch.float64)], good, good, good, 1e-2, info, ws),
+        lambda: ispa.ispa_absorb_solve(good, [m(), m(shape=(d, d + 8))], good, good, 1e-2, info, ws),
+        lambda: ispa.ispa_absorb_solve(good, good, [m(), m().t()], good, 1e-2, info, ws),
+        lambda: ispa.ispa_absorb_solve(good, good, good, [m()], 1e-2, info, ws),
+        lambda: ispa.ispa_absorb_solve(good, good, good, good, 1e-2, info.to(torch.int64), ws),
+        lambda: ispa.ispa_absorb_solve(good, good, good, good, 1e-2, info[:1], ws),
+        lambda: ispa.ispa_absorb_solve(good, good, good, good, 1e-2, None, ws),
+        lambda: ispa.ispa_layer_error(good, good, good, good, good, eps.to(torch.float32), None, ws),
+        lambda: ispa.ispa_layer_error(good, good, good, good, good, eps[:1], None, ws),
+        lambda: ispa.ispa_layer_error(good, good, good, good, good, eps, eps[:1], ws),
+        lambda: ispa.ispa_layer_error(good, good, [m(), m(torch.bfloat16)], good, good, eps, None, ws),
+        lambda: ispa.ispa_absorb_accumulate(m(torch.bfloat16, (10, d)), m(torch.bfloat16, (10, d)), m(), m(torch.float64)),
+        lambda: ispa.ispa_absorb_accumulate(m(torch.bfloat16, (10, d)), m(torch.bfloat16, (10, d)), m(), m(), m(shape=(d, 8))),
+        lambda: ispa.ispa_absorb_accumulate_fp8(m(torch.uint8, (10, d)), m(shape=(1,)), m(torch.uint8, (10, d)),
+                                                m(shape=(1,)), 64, m(), m(torch.float64)),
+        lambda: ispa.ispa_absorb_accumulate_fp8(m(torch.uint8, (10, d)), m(shape=(1,)), m(torch.uint8, (10, d)),
+                                                m(torch.float64, (1,)), 64, m(), m()),
+    ]
+    for i, call in enumerate(cases):
+        with pytest.raises(ValueError):
+            call()
+    # well-formed arguments that live in host memory are refused too (the library takes device pointers)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ispa.ispa_absorb_solve(good, good, good, good, 1e-2, info, ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ispa.ispa_layer_error(good, good, good, good, good, eps, None, ws)
