@@ -299,20 +299,21 @@ size_t ispa_future_scores_workspace(int32_t n_heads, int64_t n_p) {
   return lse + round_up(part, 256);
 }
 
-ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
-                               const void *q_proxy, int64_t n_p, int64_t q_row_stride,
-                               ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
-                               float *scores, int64_t scores_head_stride, float lambda,
-                               const float *hist_token_score, float *token_score, void *ws,
-                               size_t ws_bytes, void *stream) {
+namespace {
+
+// Argument checks of ispa_future_scores (all but the workspace); `total` receives the number of keys.
+ispa_status future_scores_check(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                const void *q_proxy, int64_t n_p, int64_t q_row_stride, const ispa_kv_segment *segs,
+                                const float *scores, int64_t scores_head_stride, float lambda,
+                                const float *hist_token_score, const float *token_score, int64_t *total_out) {
   if (dt != ISPA_BF16) return ISPA_E_UNSUPPORTED;
   if (n_heads <= 0 || n_p <= 0 || n_p > INT32_MAX / 2) return ISPA_E_ARG;
   if (head_dim != 64 && head_dim != 128) return ISPA_E_UNSUPPORTED;
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale) || !std::isfinite(lambda)) return ISPA_E_ARG;
   const int64_t width = (int64_t)n_heads * head_dim;
-  ispa_kv_segment segs[3] = {sink, cur, hist};
   int64_t total = 0;
-  for (ispa_kv_segment &sg : segs) {
+  for (int i = 0; i < 3; ++i) {
+    const ispa_kv_segment &sg = segs[i];
     if (sg.n < 0) return ISPA_E_ARG;
     if (sg.n == 0) continue;
     if (sg.k == nullptr || !aligned16(sg.k)) return ISPA_E_ARG;
@@ -326,11 +327,18 @@ ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim,
   if (scores == nullptr || !aligned4(scores) || scores_head_stride < total) return ISPA_E_ARG;
   if (token_score != nullptr && !aligned4(token_score)) return ISPA_E_ARG;
   if (hist_token_score != nullptr && !aligned4(hist_token_score)) return ISPA_E_ARG;
-  if (ws == nullptr || ws_bytes < ispa_future_scores_workspace(n_heads, n_p)) return ISPA_E_WORKSPACE;
-  if (!aligned16(ws)) return ISPA_E_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  float *lse = (float *)ws;
+  *total_out = total;
+  return ISPA_OK;
+}
 
+// The two passes of ispa_future_scores on checked arguments, with scratch at ws (16-byte aligned, at
+// least ispa_future_scores_workspace(n_heads, n_p) bytes).
+ispa_status future_scores_run(int32_t n_heads, int32_t head_dim, float softmax_scale, const void *q_proxy,
+                              int64_t n_p, int64_t q_row_stride, ispa_kv_segment sink, ispa_kv_segment cur,
+                              ispa_kv_segment hist, int64_t total, float *scores, int64_t scores_head_stride,
+                              float lambda, const float *hist_token_score, float *token_score, void *ws,
+                              hipStream_t s) {
+  float *lse = (float *)ws;
   // pass 1: log-sum-exp of every proxy over all keys (values are not read; the key pointers stand in)
   AttnArgs a{};
   const bool local_empty = sink.n + cur.n == 0;
@@ -363,6 +371,26 @@ ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim,
   if (token_score != nullptr)
     e = launch_token_scores(scores, scores_head_stride, n_heads, total, lambda, hist_token_score, token_score, s);
   return hip_status(e);
+}
+
+}  // namespace
+
+ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                               const void *q_proxy, int64_t n_p, int64_t q_row_stride,
+                               ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                               float *scores, int64_t scores_head_stride, float lambda,
+                               const float *hist_token_score, float *token_score, void *ws,
+                               size_t ws_bytes, void *stream) {
+  const ispa_kv_segment segs[3] = {sink, cur, hist};
+  int64_t total = 0;
+  ispa_status st = future_scores_check(dt, n_heads, head_dim, softmax_scale, q_proxy, n_p, q_row_stride, segs,
+                                       scores, scores_head_stride, lambda, hist_token_score, token_score, &total);
+  if (st != ISPA_OK) return st;
+  if (ws == nullptr || ws_bytes < ispa_future_scores_workspace(n_heads, n_p)) return ISPA_E_WORKSPACE;
+  if (!aligned16(ws)) return ISPA_E_ARG;
+  return future_scores_run(n_heads, head_dim, softmax_scale, q_proxy, n_p, q_row_stride, sink, cur, hist, total,
+                           scores, scores_head_stride, lambda, hist_token_score, token_score, ws,
+                           (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------------------------------------
