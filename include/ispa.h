@@ -11,6 +11,8 @@
  *  - Tensors are caller-owned device memory (allocated by the caller, e.g. PyTorch). The library
  *    never allocates or frees device memory and keeps no state between calls. Scratch memory is
  *    passed in through (ws, ws_bytes); the matching *_workspace() function gives the size needed.
+ *    One exception: ispa_future_scores_noalloc takes no workspace and uses a fixed-size library array
+ *    on each GPU instead (see its declaration).
  *  - Every call validates its arguments on the host first, enqueues its kernels on `stream`
  *    (a hipStream_t; NULL is the default stream) and returns without waiting. An argument error
  *    returns before anything is enqueued. Nothing throws across the ABI.
@@ -221,6 +223,28 @@ ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim,
                                float *scores, int64_t scores_head_stride,
                                float lambda, const float *hist_token_score, float *token_score,
                                void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * ispa_future_scores without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Arguments,
+ * results and errors are those of ispa_future_scores (the same kernels run); the scratch lives in a
+ * library array of ISPA_NOALLOC_SCRATCH_BYTES on each GPU, held until the process ends, and the call
+ * allocates and frees nothing.
+ *  - Limit: a call needs ispa_future_scores_workspace(n_heads, n_p) bytes of it (0.7 MB for 12 heads x
+ *    4680 proxies); larger calls return ISPA_E_WORKSPACE before any GPU work.
+ *  - The array belongs to the device current on the calling thread, which must be the device of
+ *    `stream`. Its address is looked up on the first call on each device (ISPA_E_HIP if that fails).
+ *  - Every call on one GPU uses the same array: calls that overlap on one GPU (other streams, other
+ *    threads, a replayed graph beside an eager call) race and must be serialised by the caller.
+ *    Nothing in the array needs clearing: each call writes every word it reads.
+ * ------------------------------------------------------------------------------------------- */
+#define ISPA_NOALLOC_SCRATCH_BYTES (16u << 20)
+ispa_status ispa_future_scores_noalloc(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                       const void *q_proxy, int64_t n_p, int64_t q_row_stride,
+                                       ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                                       float *scores, int64_t scores_head_stride,
+                                       float lambda, const float *hist_token_score, float *token_score,
+                                       void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Warmup statistics (ISPA page, section 2 stage 2 "Layer Absorb": the closed form needs

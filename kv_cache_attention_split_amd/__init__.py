@@ -18,7 +18,7 @@ from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVBias, KVSegment, l
 
 __all__ = [
     "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_future_scores",
-    "ispa_future_scores_workspace", "ispa_fp8_head_scales", "ispa_fp8_quantize", "ispa_attn_dual_fp8",
+    "ispa_future_scores_workspace", "ispa_future_scores_noalloc", "ispa_fp8_head_scales", "ispa_fp8_quantize", "ispa_attn_dual_fp8",
     "ispa_absorb_accumulate", "ispa_absorb_accumulate_fp8", "ispa_absorb_accumulate_workspace",
     "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_layer_error",
     "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_apply_delta", "ispa_project",
@@ -256,6 +256,27 @@ def ispa_future_scores(q_proxy, sink_k, cur_k, hist_k, softmax_scale: float, sco
         int(scores.stride(0)), ctypes.c_float(lam), _ptr(hist_token_score), _ptr(token_score), _ptr(ws),
         int(ws.numel() * ws.element_size()), _stream_handle(stream))
     _check(st, "ispa_future_scores")
+
+
+def ispa_future_scores_noalloc(q_proxy, sink_k, cur_k, hist_k, softmax_scale: float, scores, lam: float = 1.0,
+                               hist_token_score=None, token_score=None, stream=None) -> None:
+    """ispa_future_scores with the library's own per-GPU scratch instead of a workspace (see
+    ispa_future_scores_noalloc in include/ispa.h): allocates nothing; calls that overlap on one GPU race."""
+    n_p, H, dh = (int(x) for x in q_proxy.shape)
+    if q_proxy.stride(2) != 1 or q_proxy.stride(1) != dh:
+        raise ValueError("proxy rows must be contiguous over (H, d_h)")
+    torch = _torch()
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[0] != H or scores.stride(1) != 1:
+        raise ValueError("scores must be float32 [H, n] with unit stride over the keys")
+    for t in (hist_token_score, token_score):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("token scores must be contiguous float32")
+    st = lib().ispa_future_scores_noalloc(
+        _dtype_code(q_proxy), H, dh, ctypes.c_float(softmax_scale), _ptr(q_proxy), n_p, int(q_proxy.stride(0)),
+        _key_seg(sink_k, H, dh), _key_seg(cur_k, H, dh), _key_seg(hist_k, H, dh), _ptr(scores),
+        int(scores.stride(0)), ctypes.c_float(lam), _ptr(hist_token_score), _ptr(token_score),
+        _stream_handle(stream))
+    _check(st, "ispa_future_scores_noalloc")
 
 
 def ispa_absorb_accumulate_workspace(n_rows: int, d: int) -> int:

@@ -12,6 +12,7 @@ ISPA_E_WORKSPACE = -3
 ISPA_E_HIP = -4
 ISPA_F32 = 0
 ISPA_BF16 = 1
+ISPA_NOALLOC_SCRATCH_BYTES = 16 << 20   # include/ispa.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _DEFAULT_LIB = os.path.join(_HERE, "libispa.so")
@@ -59,6 +60,8 @@ SIGNATURES = {
     "ispa_future_scores_workspace": (c_sz, [c_i32, c_i64]),
     "ispa_future_scores": (c_int, [c_int, c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, KVSegment, KVSegment,
                                    KVSegment, c_vp, c_i64, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "ispa_future_scores_noalloc": (c_int, [c_int, c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, KVSegment, KVSegment,
+                                           KVSegment, c_vp, c_i64, c_f32, c_vp, c_vp, c_vp]),
     "ispa_absorb_accumulate_workspace": (c_sz, [c_i64, c_i32]),
     "ispa_absorb_accumulate": (c_int, [c_int, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ispa_absorb_accumulate_fp8": (c_int, [c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -388,6 +389,55 @@ ispa_status ispa_future_scores(ispa_dtype dt, int32_t n_heads, int32_t head_dim,
   if (st != ISPA_OK) return st;
   if (ws == nullptr || ws_bytes < ispa_future_scores_workspace(n_heads, n_p)) return ISPA_E_WORKSPACE;
   if (!aligned16(ws)) return ISPA_E_ARG;
+  return future_scores_run(n_heads, head_dim, softmax_scale, q_proxy, n_p, q_row_stride, sink, cur, hist, total,
+                           scores, scores_head_stride, lambda, hist_token_score, token_score, ws,
+                           (hipStream_t)stream);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Scratch of ispa_future_scores_noalloc: one array per GPU, held until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+}  // extern "C"
+
+static __device__ __align__(256) uint8_t scratch[ISPA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+ispa_status scratch_for_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ISPA_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ISPA_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ISPA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+ispa_status ispa_future_scores_noalloc(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                       const void *q_proxy, int64_t n_p, int64_t q_row_stride,
+                                       ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                                       float *scores, int64_t scores_head_stride, float lambda,
+                                       const float *hist_token_score, float *token_score, void *stream) {
+  const ispa_kv_segment segs[3] = {sink, cur, hist};
+  int64_t total = 0;
+  ispa_status st = future_scores_check(dt, n_heads, head_dim, softmax_scale, q_proxy, n_p, q_row_stride, segs,
+                                       scores, scores_head_stride, lambda, hist_token_score, token_score, &total);
+  if (st != ISPA_OK) return st;
+  if (ispa_future_scores_workspace(n_heads, n_p) > (size_t)ISPA_NOALLOC_SCRATCH_BYTES) return ISPA_E_WORKSPACE;
+  void *ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != ISPA_OK) return st;
+  // every word of the scratch that a pass reads is written earlier in the same call (the per-split
+  // states by pass 1's workgroups, the merged log-sum-exp rows by its merge), so nothing is cleared
   return future_scores_run(n_heads, head_dim, softmax_scale, q_proxy, n_p, q_row_stride, sink, cur, hist, total,
                            scores, scores_head_stride, lambda, hist_token_score, token_score, ws,
                            (hipStream_t)stream);
