@@ -310,6 +310,30 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda,
                               void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Closed-form absorb update and the layer's reconstruction error at it, in one call (ISPA page, section
+ * 2 stage 2 "Layer Absorb", both display equations, and "Dynamic Layer Selection"). dW and info are
+ * exactly those of ispa_absorb_solve (the same kernels in the same order: identical bits). At the
+ * optimum (G + lambda I) dW = C W =: B, so the objective's data term reduces to
+ *   eps = <W, H W> - <dW, B> - lambda ||dW||_F^2,   H = (F + G) - (X + X^T) = D^T D,
+ * and with L L^T = G + lambda I and Y = L^-1 B (the forward sweep), <dW, B> = ||Y||_F^2. The only d^3
+ * term left is W W^T (lower tiles), reduced against H and F in fp64: about d^3 FLOP per layer instead of
+ * ispa_layer_error's 4 d^3. ref = <F, W W^T> = ||A_full W||_F^2.
+ *
+ *   G, X, F, W, dW, info, lambda, w_is_linear_weight   as for ispa_absorb_solve / ispa_layer_error
+ *   eps        device double [batch], out; NaN for a layer whose info is nonzero
+ *   ref        device double [batch], out (may be NULL)
+ *   ws         device scratch of at least ispa_absorb_solve_eps_workspace(d, batch) bytes, 256-byte
+ *              aligned
+ * For a dW that is not this call's optimum (e.g. rounded or edited weights) use ispa_layer_error.
+ * ------------------------------------------------------------------------------------------- */
+size_t ispa_absorb_solve_eps_workspace(int32_t d, int32_t batch);
+ispa_status ispa_absorb_solve_eps(int32_t d, int32_t batch, float lambda,
+                                  const float *const *G, const float *const *X, const float *const *F,
+                                  const float *const *W, int32_t w_is_linear_weight,
+                                  float *const *dW, int32_t *info, double *eps, double *ref,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Reconstruction error per layer (ISPA page, section 2 "Dynamic Layer Selection": layers are ranked
  * by their reconstruction error after the warmup). For the given dW (any dW, not only the optimum):
  *   eps = || A_loc (W + dW) - A_full W ||_F^2

@@ -20,7 +20,8 @@ __all__ = [
     "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_future_scores",
     "ispa_future_scores_workspace", "ispa_future_scores_noalloc", "ispa_fp8_head_scales", "ispa_fp8_quantize", "ispa_attn_dual_fp8",
     "ispa_absorb_accumulate", "ispa_absorb_accumulate_fp8", "ispa_absorb_accumulate_workspace",
-    "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_layer_error",
+    "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_absorb_solve_eps",
+    "ispa_absorb_solve_eps_workspace", "ispa_layer_error",
     "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_apply_delta", "ispa_project",
     "ispa_kv_plan", "ispa_status_string", "ispa_version",
     "IspaError", "lib_path",
@@ -388,6 +389,29 @@ def ispa_absorb_solve(G: Sequence, X: Sequence, W: Sequence, dW: Sequence, lam: 
         d, batch, ctypes.c_float(lam), ptrs[0], ptrs[1], ptrs[2], 1 if w_is_linear_weight else 0, ptrs[3],
         _ptr(info), ws_ptr, ws_bytes, _stream_handle(stream))
     _check(st, "ispa_absorb_solve")
+
+
+def ispa_absorb_solve_eps_workspace(d: int, batch: int) -> int:
+    return int(lib().ispa_absorb_solve_eps_workspace(int(d), int(batch)))
+
+
+def ispa_absorb_solve_eps(G: Sequence, X: Sequence, F: Sequence, W: Sequence, dW: Sequence, lam: float, info, eps,
+                          ref=None, ws=None, w_is_linear_weight: bool = False, stream=None) -> None:
+    """dW as ispa_absorb_solve, plus eps_l = ||A_loc (W + dW) - A_full W||_F^2 at that optimum and
+    ref_l = ||A_full W||_F^2 (float64 [batch]; eps is NaN where info is nonzero)."""
+    batch = len(G)
+    d = int(G[0].shape[0]) if batch else 0
+    torch = _torch()
+    ptrs = [_square_list(m, d, batch, name) for m, name in ((G, "G"), (X, "X"), (F, "F"), (W, "W"), (dW, "dW"))]
+    if batch:
+        _vector(info, batch, torch.int32, "info")
+        _vector(eps, batch, torch.float64, "eps")
+        _vector(ref, batch, torch.float64, "ref", optional=True)
+    ws_ptr, ws_bytes = _workspace(ws)
+    st = lib().ispa_absorb_solve_eps(
+        d, batch, ctypes.c_float(lam), ptrs[0], ptrs[1], ptrs[2], ptrs[3], 1 if w_is_linear_weight else 0, ptrs[4],
+        _ptr(info), _ptr(eps), _ptr(ref), ws_ptr, ws_bytes, _stream_handle(stream))
+    _check(st, "ispa_absorb_solve_eps")
 
 
 def ispa_layer_error_workspace(d: int, batch: int) -> int:

@@ -68,6 +68,9 @@ SIGNATURES = {
                                            c_sz, c_vp]),
     "ispa_absorb_solve_workspace": (c_sz, [c_i32, c_i32]),
     "ispa_absorb_solve": (c_int, [c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "ispa_absorb_solve_eps_workspace": (c_sz, [c_i32, c_i32]),
+    "ispa_absorb_solve_eps": (c_int, [c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                      c_vp, c_sz, c_vp]),
     "ispa_layer_error_workspace": (c_sz, [c_i32, c_i32]),
     "ispa_layer_error": (c_int, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ispa_rank_layers": (c_int, [c_vp, c_i32, c_i32, c_vp, c_vp]),

@@ -533,28 +533,29 @@ size_t ispa_absorb_solve_workspace(int32_t d, int32_t batch) {
   return solve_layout(d).total(batch);
 }
 
-ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const float *const *G,
-                              const float *const *X, const float *const *W, int32_t w_is_linear_weight,
-                              float *const *dW, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
-  ispa_status st = check_square_batch(d, batch);
-  if (st != ISPA_OK) return st;
-  if (!(lambda >= 0.f) || !std::isfinite(lambda)) return ISPA_E_ARG;
-  if (batch == 0) return ISPA_OK;
-  if ((st = check_ptr_array(G, batch)) != ISPA_OK) return st;
-  if ((st = check_ptr_array(X, batch)) != ISPA_OK) return st;
-  if ((st = check_ptr_array(W, batch)) != ISPA_OK) return st;
-  if ((st = check_ptr_array((const float *const *)dW, batch)) != ISPA_OK) return st;
-  if (info == nullptr) return ISPA_E_ARG;
-  const SolveLayout lay = solve_layout(d);
-  if (ws == nullptr || ws_bytes < lay.total(batch) || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
-    return ws == nullptr || ws_bytes < lay.total(batch) ? ISPA_E_WORKSPACE : ISPA_E_ARG;
+namespace {
 
-  hipStream_t s = (hipStream_t)stream;
+// The error at the optimum, requested from the solve: F per layer, outputs, and the partial sums'
+// region (4 terms x batch x stride doubles: <H, W W^T>, <F, W W^T>, ||Y||^2, ||dW||^2 per tile).
+struct EpsRequest {
+  const float *const *F;
+  double *eps, *ref;
+  double *part;
+  int64_t stride;
+};
+
+ispa_status solve_impl(int32_t d, int32_t batch, float lambda, const float *const *G, const float *const *X,
+                       const float *const *W, int32_t w_is_linear_weight, float *const *dW, int32_t *info,
+                       void *ws, const EpsRequest *er, hipStream_t s) {
+  const SolveLayout lay = solve_layout(d);
+
   const int nb = solve_nb(d);
   const int nt = (d + nb - 1) / nb;
   const int64_t mat_f = (int64_t)(lay.mat / sizeof(float));
   const int64_t per_f = (int64_t)(lay.per_layer / sizeof(float));
 
+  const int tiles = gemm_tiles(d, d);
+  auto term = [&](int g, int layer) { return er->part + ((int64_t)g * batch + layer) * er->stride; };
   for (int p0 = 0; p0 < batch; p0 += kMaxBatch) {
     const int cnt = std::min(batch - p0, kMaxBatch);
     float *base = (float *)ws + (int64_t)p0 * per_f;
@@ -685,6 +686,8 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
         ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
       }
     }
+    // ||Y||^2 = <dW, B> at the optimum (B^T (L L^T)^-1 B), before the back sweep overwrites Y
+    if (er != nullptr) ISPA_TRY(launch_sumsq_tiles(Bp(0), per_f, d, cnt, term(2, p0), er->stride, s));
     // back substitution L^T dW = Y, left-looking by block rows (bottom to top):
     //   X_k = Linv_k^T (Y_k - L[k+1:, k]^T X[k+1:])
     for (int k = nt - 1; k >= 0; --k) {
@@ -720,6 +723,31 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
         ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
       }
     }
+    if (er != nullptr) {
+      // eps = <W, H W> - <dW, B> - lambda ||dW||^2 with H = (F + G) - (X + X^T): H goes to the factor's
+      // region (L is no longer needed), then one product W W^T, lower tiles only, reduced against H and
+      // F in its epilogue (<F, W W^T> = ||A_full W||^2 is the reference)
+      ISPA_TRY(launch_sumsq_tiles(Bp(0), per_f, d, cnt, term(3, p0), er->stride, s));
+      CPtrBatch f{}, x{};
+      for (int i = 0; i < cnt; ++i) {
+        f.p[i] = er->F[p0 + i];
+        x.p[i] = X[p0 + i];
+      }
+      ISPA_TRY(launch_h_form(f, x, g, Lp(0), per_f, d, cnt, s));
+      GemmBatch b{};
+      GemmShape sh{};
+      sh.M = d; sh.N = d; sh.K = d;
+      sh.lda = d; sh.ldb = d; sh.ldc = d; sh.lde = d;
+      sh.ta = 0; sh.tb = 1; sh.dot = 2; sh.sym = 1;
+      sh.alpha = 1.f; sh.beta = 0.f;
+      for (int i = 0; i < cnt; ++i) {
+        b.A[i] = Wuse[i];
+        b.B[i] = Wuse[i];
+        b.E[i] = Lp(i);
+        b.E2[i] = er->F[p0 + i];
+      }
+      ISPA_TRY(launch_gemm_f32(b, cnt, sh, term(0, p0), er->stride, s, term(1, p0)));
+    }
     // dW in the caller's orientation
     CPtrBatch in{};
     PtrBatch out{};
@@ -732,8 +760,72 @@ ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const floa
     else
       ISPA_TRY(launch_copy(in, out, d, cnt, s));
   }
+  if (er != nullptr) {
+    const double coef_eps[4] = {1.0, 0.0, -1.0, -(double)lambda};
+    ISPA_TRY(launch_reduce_partials(er->part, batch, er->stride, tiles, 4, coef_eps, er->eps, s, info));
+    if (er->ref != nullptr) {
+      const double coef_ref[1] = {1.0};
+      ISPA_TRY(launch_reduce_partials(term(1, 0), batch, er->stride, tiles, 1, coef_ref, er->ref, s));
+    }
+  }
   return ISPA_OK;
 }
+
+ispa_status check_solve_args(int32_t d, int32_t batch, float lambda, const float *const *G, const float *const *X,
+                             const float *const *W, float *const *dW, const int32_t *info) {
+  ispa_status st = check_square_batch(d, batch);
+  if (st != ISPA_OK) return st;
+  if (!(lambda >= 0.f) || !std::isfinite(lambda)) return ISPA_E_ARG;
+  if (batch == 0) return ISPA_OK;
+  if ((st = check_ptr_array(G, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array(X, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array(W, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array((const float *const *)dW, batch)) != ISPA_OK) return st;
+  if (info == nullptr) return ISPA_E_ARG;
+  return ISPA_OK;
+}
+
+// doubles per (term, layer) of the error's partial sums: one per 128 x 128 tile, 256-byte rounded
+int64_t eps_part_stride(int d) { return (int64_t)round_up((size_t)gemm_tiles(d, d), 32); }
+
+}  // namespace
+
+ispa_status ispa_absorb_solve(int32_t d, int32_t batch, float lambda, const float *const *G,
+                              const float *const *X, const float *const *W, int32_t w_is_linear_weight,
+                              float *const *dW, int32_t *info, void *ws, size_t ws_bytes, void *stream) {
+  ispa_status st = check_solve_args(d, batch, lambda, G, X, W, dW, info);
+  if (st != ISPA_OK || batch == 0) return st;
+  const size_t need = solve_layout(d).total(batch);
+  if (ws == nullptr || ws_bytes < need) return ISPA_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ISPA_E_ARG;
+  return solve_impl(d, batch, lambda, G, X, W, w_is_linear_weight, dW, info, ws, nullptr, (hipStream_t)stream);
+}
+
+size_t ispa_absorb_solve_eps_workspace(int32_t d, int32_t batch) {
+  if (d <= 0 || batch <= 0) return 0;
+  return solve_layout(d).total(batch) + 4 * (size_t)batch * (size_t)eps_part_stride(d) * sizeof(double);
+}
+
+ispa_status ispa_absorb_solve_eps(int32_t d, int32_t batch, float lambda, const float *const *G,
+                                  const float *const *X, const float *const *F, const float *const *W,
+                                  int32_t w_is_linear_weight, float *const *dW, int32_t *info, double *eps,
+                                  double *ref, void *ws, size_t ws_bytes, void *stream) {
+  ispa_status st = check_solve_args(d, batch, lambda, G, X, W, dW, info);
+  if (st != ISPA_OK || batch == 0) return st;
+  if ((st = check_ptr_array(F, batch)) != ISPA_OK) return st;
+  if (eps == nullptr || ((uintptr_t)eps & 7) != 0 || ((uintptr_t)ref & 7) != 0) return ISPA_E_ARG;
+  const size_t need = ispa_absorb_solve_eps_workspace(d, batch);
+  if (ws == nullptr || ws_bytes < need) return ISPA_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ISPA_E_ARG;
+  EpsRequest er;
+  er.F = F;
+  er.eps = eps;
+  er.ref = ref;
+  er.part = (double *)((uint8_t *)ws + solve_layout(d).total(batch));
+  er.stride = eps_part_stride(d);
+  return solve_impl(d, batch, lambda, G, X, W, w_is_linear_weight, dW, info, ws, &er, (hipStream_t)stream);
+}
+
 
 // ------------------------------------------------------------------------------------------------
 size_t ispa_layer_error_workspace(int32_t d, int32_t batch) {

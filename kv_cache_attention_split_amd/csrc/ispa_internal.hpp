@@ -85,6 +85,8 @@ hipError_t launch_gram_fp8(int64_t n_rows, int d, int head_dim, const uint8_t *a
 //     sum_{tile} E[i*lde + j] * (alpha * (AB)[i][j]) in fp64 to part[p * tiles + tile]
 //   sym (dot mode, AB and E both symmetric): tiles above the diagonal are skipped (their partial
 //     is 0) and strictly-lower tiles count twice, so the partials still sum to <E, AB>
+//   dot = 2: a second matrix E2 (same lde) is reduced against the same product tile, its partials
+//     written to part2 (same layout); with sym, E2 must be symmetric too
 //   inplace: C is also the A or B operand, and the product only mixes elements within 128 rows (C = A)
 //     or 128 columns (C = B) of it. Such a launch keeps 128 x 128 tiles whatever its size: a workgroup
 //     then reads everything its own tile depends on before it writes, and no other workgroup reads
@@ -99,6 +101,8 @@ struct GemmBatch {
   const float *B[kMaxGemmBatch];
   float *C[kMaxGemmBatch];
   const float *E[kMaxGemmBatch];
+  const float *E2[kMaxGemmBatch];
+  double *P2[kMaxGemmBatch];     // set by launch_gemm_f32 from part2
 };
 
 struct GemmShape {
@@ -110,16 +114,22 @@ struct GemmShape {
   float alpha, beta;
 };
 
-// Launch one batched GEMM of `count` problems (count <= kMaxGemmBatch). `part` is required in dot mode.
+// Launch one batched GEMM of `count` problems (count <= kMaxGemmBatch). `part` is required in dot mode,
+// `part2` when dot = 2.
 hipError_t launch_gemm_f32(const GemmBatch &b, int count, const GemmShape &sh, double *part,
-                           int64_t part_stride, hipStream_t s);
+                           int64_t part_stride, hipStream_t s, double *part2 = nullptr);
 int gemm_tiles(int M, int N);     // number of output tiles (partials per problem in dot mode)
 
 // Sum the dot partials per problem in a fixed order (deterministic), over `terms` groups:
 //   out[p] = sum_g coef[g] * sum_{t < tiles} part[(g * count + p) * stride + t]
+// With `info` (device int32 [count]), problems whose info is nonzero get NaN instead.
 hipError_t launch_reduce_partials(const double *part, int count, int64_t stride, int tiles, int terms,
                                   const double *coef /* host, terms <= 4 */, double *out,
-                                  hipStream_t s);
+                                  hipStream_t s, const int32_t *info = nullptr);
+// Per 128 x 128 tile of a d x d matrix (the tiles of gemm_tiles(d, d), same order): the sum of
+// squares in fp64, a fixed order within the tile -> part[p * stride + tile]
+hipError_t launch_sumsq_tiles(const float *base, int64_t layer_stride, int d, int count, double *part,
+                              int64_t stride, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------------
 // Blocked Cholesky building blocks
@@ -147,6 +157,9 @@ hipError_t launch_add(const CPtrBatch &a, const CPtrBatch &b, const PtrBatch &ou
 hipError_t launch_sub(const CPtrBatch &a, const CPtrBatch &b, const PtrBatch &out, int d, int count,
                       hipStream_t s);
 hipError_t launch_copy(const CPtrBatch &in, const PtrBatch &out, int d, int count, hipStream_t s);
+// H = (F + G) - (X + X^T) elementwise (exactly symmetric when F and G are), d x d
+hipError_t launch_h_form(const CPtrBatch &F, const CPtrBatch &X, const CPtrBatch &G, float *H, int64_t H_stride,
+                         int d, int count, hipStream_t s);
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------------

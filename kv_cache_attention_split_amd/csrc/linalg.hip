@@ -35,7 +35,10 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
   const int ti = tile / tn, tj = tile % tn;
   const int m0 = ti * GTT, n0 = tj * GTT;
   if (sh.dot && sh.sym && tj > ti) {
-    if (threadIdx.x == 0) ((double *)bt.C[blockIdx.y])[tile] = 0.0;
+    if (threadIdx.x == 0) {
+      ((double *)bt.C[blockIdx.y])[tile] = 0.0;
+      if (sh.dot == 2) bt.P2[blockIdx.y][tile] = 0.0;
+    }
     return;
   }
   if (sh.lower && n0 > m0 + GTT - 1) return;
@@ -169,9 +172,11 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
         }
     return;
   }
-  // dot epilogue: sum E .* (alpha AB) over this tile in fp64
+  // dot epilogue: sum E .* (alpha AB) (and E2 .* (alpha AB)) over this tile in fp64
   const float *E = bt.E[p];
-  double s = 0.0;
+  const float *E2 = bt.E2[p];
+  const bool two = sh.dot == 2;
+  double s = 0.0, s2 = 0.0;
 #pragma unroll
   for (int bi = 0; bi < NBK; ++bi)
 #pragma unroll
@@ -180,18 +185,28 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wm * WT + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
         const int col = n0 + wn * WT + bj * 32 + l32;
-        if (row < sh.M && col < sh.N)
-          s += (double)E[(int64_t)row * sh.lde + col] * (double)(sh.alpha * acc[bi][bj][v]);
+        if (row < sh.M && col < sh.N) {
+          const double prod = (double)(sh.alpha * acc[bi][bj][v]);
+          s += (double)E[(int64_t)row * sh.lde + col] * prod;
+          if (two) s2 += (double)E2[(int64_t)row * sh.lde + col] * prod;
+        }
       }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  __shared__ double wsum[4];
-  if (lane == 0) wsum[w] = s;
+  for (int off = 32; off >= 1; off >>= 1) {
+    s += __shfl_xor(s, off, 64);
+    s2 += __shfl_xor(s2, off, 64);
+  }
+  __shared__ double wsum[2][4];
+  if (lane == 0) {
+    wsum[0][w] = s;
+    wsum[1][w] = s2;
+  }
   __syncthreads();
   if (tid == 0) {
     double *part = (double *)bt.C[p];   // dot mode: C holds this problem's partial array
     const double wgt = (sh.sym && ti != tj) ? 2.0 : 1.0;
-    part[tile] = wgt * (((wsum[0] + wsum[1]) + wsum[2]) + wsum[3]);
+    part[tile] = wgt * (((wsum[0][0] + wsum[0][1]) + wsum[0][2]) + wsum[0][3]);
+    if (two) bt.P2[p][tile] = wgt * (((wsum[1][0] + wsum[1][1]) + wsum[1][2]) + wsum[1][3]);
   }
 }
 
@@ -428,7 +443,7 @@ struct Coef {
 };
 
 __global__ void reduce_partials_kernel(const double *part, int count, int64_t stride, int tiles,
-                                       int terms, Coef coef, double *out) {
+                                       int terms, Coef coef, double *out, const int32_t *info) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= count) return;
   double tot = 0.0;
@@ -438,7 +453,56 @@ __global__ void reduce_partials_kernel(const double *part, int count, int64_t st
     for (int t = 0; t < tiles; ++t) s += pp[t];
     tot += coef.c[g] * s;
   }
-  out[p] = tot;
+  out[p] = (info != nullptr && info[p] != 0) ? __builtin_nan("") : tot;
+}
+
+// Sum of squares of one 128 x 128 tile of layer blockIdx.y's d x d matrix, in fp64: each thread sums
+// its column pairs of every row in row order, then a fixed tree over the threads.
+__global__ void __launch_bounds__(256) sumsq_tiles_kernel(const float *base, int64_t layer_stride, int d,
+                                                          double *part, int64_t stride) {
+  const int tile = blockIdx.x, layer = blockIdx.y;
+  const int tn = (d + GT - 1) / GT;
+  const int r0 = (tile / tn) * GT, c0 = (tile % tn) * GT;
+  const float *m = base + layer * layer_stride;
+  const int tid = threadIdx.x;
+  const int c = c0 + (tid & 63) * 2;   // two columns per thread
+  const int rq = tid >> 6;             // rows rq, rq + 4, ...
+  double s = 0.0;
+  for (int r = r0 + rq; r < r0 + GT && r < d; r += 4)
+    for (int e = 0; e < 2; ++e)
+      if (c + e < d) {
+        const double x = m[(int64_t)r * d + c + e];
+        s += x * x;
+      }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  __shared__ double ws[4];
+  if ((tid & 63) == 0) ws[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) part[layer * stride + tile] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+}
+
+// H = (F + G) - (X + X^T): X^T through a 32 x 33 LDS tile. Each element's two sums are commutative, so
+// H is exactly symmetric when F and G are.
+__global__ void h_form_kernel(CPtrBatch F, CPtrBatch X, CPtrBatch G, float *Hbase, int64_t H_stride, int d) {
+  __shared__ float t[32][33];
+  const int layer = blockIdx.z;
+  const float *x = X.p[layer];
+  const int bx = blockIdx.x * 32, by = blockIdx.y * 32;   // output columns bx.., rows by..
+  const int tx = threadIdx.x, ty = threadIdx.y;           // 32 x 8
+  for (int r = ty; r < 32; r += 8) {                      // t[c][r'] = X[bx + r][by + tx] = X^T[by + tx][bx + r]
+    const int gr = bx + r, gc = by + tx;
+    if (gr < d && gc < d) t[r][tx] = x[(int64_t)gr * d + gc];
+  }
+  __syncthreads();
+  float *H = Hbase + layer * H_stride;
+  for (int r = ty; r < 32; r += 8) {
+    const int gr = by + r, gc = bx + tx;
+    if (gr < d && gc < d) {
+      const int64_t e = (int64_t)gr * d + gc;
+      H[e] = (F.p[layer][e] + G.p[layer][e]) - (x[e] + t[tx][r]);
+    }
+  }
 }
 
 inline int grid_for(int64_t n4) {
@@ -451,11 +515,14 @@ inline int grid_for(int64_t n4) {
 int gemm_tiles(int M, int N) { return ((M + GT - 1) / GT) * ((N + GT - 1) / GT); }
 
 hipError_t launch_gemm_f32(const GemmBatch &b, int count, const GemmShape &sh, double *part,
-                           int64_t part_stride, hipStream_t s) {
+                           int64_t part_stride, hipStream_t s, double *part2) {
   if (count <= 0 || sh.M <= 0 || sh.N <= 0) return hipSuccess;
+  if (sh.dot == 2 && part2 == nullptr) return hipErrorInvalidValue;
   GemmBatch bb = b;
   if (sh.dot) {
     for (int p = 0; p < count; ++p) bb.C[p] = (float *)(part + (int64_t)p * part_stride);
+    if (sh.dot == 2)
+      for (int p = 0; p < count; ++p) bb.P2[p] = part2 + (int64_t)p * part_stride;
   }
   // fewer than two 128-tiles per CU: 64-tiles (dot launches keep 128-tiles: their partial
   // count is gemm_tiles; in-place launches too, so that one workgroup owns each 128 extent)
@@ -471,11 +538,27 @@ hipError_t launch_gemm_f32(const GemmBatch &b, int count, const GemmShape &sh, d
 }
 
 hipError_t launch_reduce_partials(const double *part, int count, int64_t stride, int tiles, int terms,
-                                  const double *coef, double *out, hipStream_t s) {
+                                  const double *coef, double *out, hipStream_t s, const int32_t *info) {
   Coef c = {{0, 0, 0, 0}};
   for (int g = 0; g < terms && g < 4; ++g) c.c[g] = coef[g];
   hipLaunchKernelGGL(reduce_partials_kernel, dim3((count + 63) / 64), dim3(64), 0, s, part, count,
-                     stride, tiles, terms, c, out);
+                     stride, tiles, terms, c, out, info);
+  return hipGetLastError();
+}
+
+hipError_t launch_sumsq_tiles(const float *base, int64_t layer_stride, int d, int count, double *part,
+                              int64_t stride, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sumsq_tiles_kernel, dim3(gemm_tiles(d, d), count), dim3(256), 0, s, base, layer_stride, d,
+                     part, stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_h_form(const CPtrBatch &F, const CPtrBatch &X, const CPtrBatch &G, float *H, int64_t H_stride,
+                         int d, int count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  dim3 grid((d + 31) / 32, (d + 31) / 32, count);
+  hipLaunchKernelGGL(h_form_kernel, grid, dim3(32, 8), 0, s, F, X, G, H, H_stride, d);
   return hipGetLastError();
 }
 

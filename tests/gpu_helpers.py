@@ -106,3 +106,21 @@ def check_attention(out, ref, dtype: str, rows=None, heads=None):
         report[mine] = err
         assert err <= tol["lse_abs"], (mine, err)
     return report
+
+
+def admissible_selection(sel, eps_ref, k: int, tol: float) -> None:
+    """Assert that `sel` is a selection the layer-ranking rule admits when errors are known to within
+    a relative `tol`: k distinct layers, and no selected layer's oracle error exceeds an unselected
+    layer's by more than the tolerance allows, max_{i in sel} eps_i <= (1 + tol)/(1 - tol) * min_{j not
+    in sel} eps_j. When the k-th and (k+1)-th errors are further apart than that, the only admissible
+    set is the oracle's own."""
+    eps_ref = np.asarray(eps_ref, dtype=np.float64)
+    sel = [int(i) for i in sel]
+    assert len(sel) == k and len(set(sel)) == k, sel
+    rest = [j for j in range(len(eps_ref)) if j not in set(sel)]
+    if not rest or not sel:
+        return
+    r = (1.0 + tol) / (1.0 - tol)
+    worst_in = float(eps_ref[sel].max())
+    best_out = float(eps_ref[rest].min())
+    assert worst_in <= r * best_out, (sel, worst_in, best_out)

@@ -257,6 +257,33 @@ def test_solve_argument_errors_and_workspace(L):
     assert s(d, 0, ctypes.c_float(1e-2), None, None, None, 0, None, None, None, 0, None) == _abi.ISPA_OK
 
 
+def test_solve_eps_argument_errors_and_workspace(L):
+    d, b = 256, 3
+    need = L.ispa_absorb_solve_eps_workspace(d, b)
+    # the solve's workspace plus 4 terms x 3 layers x 32 tile partials (4 tiles, rounded up to 32 doubles)
+    assert need == L.ispa_absorb_solve_workspace(d, b) + 4 * b * 32 * 8
+    s = L.ispa_absorb_solve_eps
+    P = ptrs(b)
+    ok = lambda **kw: dict(dict(d=d, lam=1e-2, F=P, info=FAKE, eps=FAKE2, ref=None, ws=FAKE, nbytes=need), **kw)
+    call = lambda a: s(a["d"], b, ctypes.c_float(a["lam"]), P, P, a["F"], P, 0, P, a["info"], a["eps"], a["ref"],
+                       a["ws"], a["nbytes"], None)
+    assert call(ok(d=100)) == _abi.ISPA_E_UNSUPPORTED
+    assert call(ok(lam=-1.0)) == _abi.ISPA_E_ARG
+    assert call(ok(nbytes=need - 1)) == _abi.ISPA_E_WORKSPACE
+    assert call(ok(ws=None)) == _abi.ISPA_E_WORKSPACE
+    assert call(ok(ws=FAKE + 16)) == _abi.ISPA_E_ARG          # 256-byte alignment
+    assert call(ok(info=None)) == _abi.ISPA_E_ARG
+    assert call(ok(eps=None)) == _abi.ISPA_E_ARG
+    assert call(ok(eps=FAKE2 + 4)) == _abi.ISPA_E_ARG
+    assert call(ok(ref=FAKE + 4)) == _abi.ISPA_E_ARG
+    assert call(ok(F=None)) == _abi.ISPA_E_ARG
+    bad = ptrs(b)
+    bad[2] = MISALIGNED
+    assert call(ok(F=bad)) == _abi.ISPA_E_ARG
+    assert s(d, 0, ctypes.c_float(1e-2), None, None, None, None, 0, None, None, None, None, None, 0, None) == \
+        _abi.ISPA_OK
+
+
 def test_error_argument_errors_and_workspace(L):
     d, b = 128, 2
     need = L.ispa_layer_error_workspace(d, b)

@@ -164,6 +164,30 @@ def test_error_identity(seed):
         assert abs(e_rows - e_stats) <= 1e-11 * max(1.0, e_rows)
 
 
+@pytest.mark.parametrize("seed", [16, 17])
+@pytest.mark.parametrize("lam", [1e-2, 3.0])
+def test_error_at_the_optimum(seed, lam):
+    """At the closed-form optimum (G + lam I) dW = C W =: B, so <dW, G dW> = <dW, B> - lam ||dW||^2 and
+    eps = <W, H W> - <dW, B> - lam ||dW||^2; with L L^T = G + lam I and Y = L^-1 B, <dW, B> = ||Y||_F^2
+    (B^T (L L^T)^-1 B = (L^-1 B)^T (L^-1 B)), and <W, H W> = <(F + G) - (X + X^T), W W^T>. The error on
+    the rows must come out of these three terms; a wrong sign or a missing lam term fails."""
+    a, b, w = _rows(seed)
+    st = oab.grams(a, b)
+    dw = oab.ridge_delta_w(st["G"], st["C"], w, lam)
+    B = st["C"] @ w
+    L = np.linalg.cholesky(st["G"] + lam * np.eye(st["G"].shape[0]))
+    Y = np.linalg.solve(L, B)
+    H = (st["F"] + st["G"]) - (st["X"] + st["X"].T)
+    np.testing.assert_allclose(H, st["H"], rtol=0, atol=1e-12 * np.abs(st["F"]).max())
+    wh = np.sum(H * (w @ w.T))
+    e_rows = oab.layer_error_rows(a, b, w, dw)
+    assert abs(np.sum(Y * Y) - np.sum(dw * B)) <= 1e-11 * np.sum(dw * B)
+    assert abs((wh - np.sum(Y * Y) - lam * np.sum(dw * dw)) - e_rows) <= 1e-10 * max(1.0, e_rows)
+    # away from the optimum the shortcut does not hold
+    off = dw * 1.1
+    assert abs(oab.layer_error_rows(a, b, w, off) - (wh - np.sum(off * B) - lam * np.sum(off * off))) > 1e-6
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_exact_rational_brute_force(seed):
     """P-13: d <= 4 with small-integer A_loc, D, W and lam = 1, solved in exact rationals."""
