@@ -1,13 +1,18 @@
-"""End to end on one layer of the 1.3B warmup: the oracle's own chain against the GPU chain.
+"""One layer of the 1.3B warmup on its real attention outputs: Layer Absorb at the workload's own
+conditioning, and the oracle's whole chain against the device's whole chain.
 
-The oracle runs its whole chain in float64 from the seeded bf16 inputs: attention of the 4 warmup chunks
-(scores built explicitly, no merge), the statistics of its own A_loc / A_full, the LU solve and eps on
-the rows. The GPU runs ispa_attn_dual -> ispa_absorb_accumulate (4 chunks) -> ispa_absorb_solve ->
-ispa_layer_error on the same inputs. The two differ by more than each stage's own error, because the
-GPU stores A in bf16 (the stated output precision) and the statistics then multiply those rounded rows;
-(G + lambda I)^-1 amplifies that by up to its condition number. So this comparison is reported (printed
-with kappa(G + lambda I)) and gated only loosely; the stage gates (attention max-abs 1e-2, dW 1e-3 on
-identical statistics) live in the other test files.
+The oracle computes A_loc / A_full of the 4 warmup chunks of workload 3's layer 0 in float64 from the
+seeded bf16 inputs (explicit scores, no merge). Two comparisons follow (ISPA summary page, section 2
+"Framework Core", stage 2 "Layer Absorb": closed form and objective; "Dynamic Layer Selection": eps):
+
+  * identical rows: the oracle's own A, rounded to bf16 (the stored precision of A), is given to both
+    sides. The device forms the statistics, solves and evaluates eps; the oracle does the same in float64
+    (LU solve) on the same rows. Gates: statistics rel-Frobenius <= 1e-5, dW <= 1e-3, eps <= 1e-3, with
+    kappa(G + lambda I) about 2e3 (these rows, unlike the synthetic absorb rows, carry the conditioning
+    the workload really has).
+  * whole chain: the device computes its own attention and runs the chain from there; the oracle runs
+    its chain on its unrounded A. The device's A is stored in bf16, and (G + lambda I)^-1 amplifies that
+    rounding by up to kappa, so dW is reported and gated loosely (2e-2); eps is gated at 1e-3.
 """
 import time
 
@@ -23,29 +28,33 @@ from gpu_helpers import rel_fro, to_dev, to_host64, torch_mod
 pytestmark = pytest.mark.gpu
 
 E2E_DW_GATE = 2e-2       # loose: a few times the spread bf16 storage of A alone causes
-E2E_EPS_GATE = 2e-2
+EPS_GATE = 1e-3
+DW_GATE = 1e-3
+STATS_GATE = 1e-5
+QKV = ("q", "sink_k", "sink_v", "cur_k", "cur_v", "hist_k", "hist_v")
 
 
-def test_layer0_chain_against_oracle_chain():
-    import kv_cache_attention_split_amd as ispa
-    torch = torch_mod()
+@pytest.fixture(scope="module")
+def layer0():
     wl = inputs.CONFIGS[3]
-    d, H, dh, lam = wl.d, wl.n_heads, wl.head_dim, wl.lam
-    print("case: workload 3 layer 0, 4 chunks, GPU chain vs oracle chain", flush=True)
+    print("case: workload 3 layer 0, oracle attention of the 4 warmup chunks", flush=True)
     cache = inputs.LayerCache(wl, 0)
     chunks = [inputs.attention_inputs(3, 0, c, cache=cache) for c in range(len(wl.chunks))]
-    W = inputs.weight(3, 0)
-
-    # GPU chain
-    G, X, F = (torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3))
+    t0 = time.perf_counter()
+    rows = []
     for inp in chunks:
-        dev = {k: to_dev(inp[k], "bf16") for k in ("q", "sink_k", "sink_v", "cur_k", "cur_v", "hist_k", "hist_v")}
-        n_q = inp["q"].shape[0]
-        a_loc = torch.empty((n_q, d), dtype=torch.bfloat16, device="cuda")
-        a_full = torch.empty_like(a_loc)
-        lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
-        ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"], dev["hist_k"],
-                            dev["hist_v"], float(inp["scale"]), a_loc, a_full, lse[0], lse[1], lse[2])
+        out = oatt.dual_stream(inp)
+        rows.append((out["A_loc"], out["A_full"]))
+    print(f"   oracle attention {time.perf_counter() - t0:.1f} s", flush=True)
+    return {"wl": wl, "chunks": chunks, "rows": rows, "W": inputs.weight(3, 0)}
+
+
+def _absorb_gpu(row_chunks, W, lam, d):
+    """Device statistics over the chunks (device tensors), solve and eps."""
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    G, X, F = (torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3))
+    for a_loc, a_full in row_chunks:
         ispa.ispa_absorb_accumulate(a_loc, a_full, G, X, F)
     Wd = to_dev(W, "f32")
     dW = torch.empty((d, d), dtype=torch.float32, device="cuda")
@@ -56,28 +65,72 @@ def test_layer0_chain_against_oracle_chain():
     ref = torch.zeros_like(eps)
     ws2 = torch.empty(ispa.ispa_layer_error_workspace(d, 1), dtype=torch.uint8, device="cuda")
     ispa.ispa_layer_error([G], [X], [F], [Wd], [dW], eps, ref, ws2)
+    # the same solve with the error at its optimum
+    dW2 = torch.empty_like(dW)
+    eps2 = torch.zeros_like(eps)
+    ws3 = torch.empty(ispa.ispa_absorb_solve_eps_workspace(d, 1), dtype=torch.uint8, device="cuda")
+    ispa.ispa_absorb_solve_eps([G], [X], [F], [Wd], [dW2], lam, info, eps2, None, ws3)
     torch.cuda.synchronize()
     assert info.cpu().tolist() == [0]
-    dW_gpu = to_host64(dW)
-    eps_gpu = float(eps.cpu()[0])
+    assert torch.equal(dW2, dW)
+    return {"G": G, "X": X, "F": F, "dW": to_host64(dW), "eps": float(eps.cpu()[0]), "ref": float(ref.cpu()[0]),
+            "eps_opt": float(eps2.cpu()[0])}
 
-    # oracle chain (float64 from the same inputs; its own A, never the GPU's)
-    t0 = time.perf_counter()
-    rows = []
-    for inp in chunks:
-        out = oatt.dual_stream(inp)
-        rows.append((out["A_loc"], out["A_full"]))
-    st = oab.accumulate(rows)
+
+def test_layer0_absorb_on_oracle_rows_real_conditioning(layer0):
+    wl, W = layer0["wl"], layer0["W"]
+    d, lam = wl.d, wl.lam
+    # the oracle's A rounded to the stored precision; both sides get exactly these values
+    rows = [(inputs.round_bf16(a.astype(np.float32)), inputs.round_bf16(b.astype(np.float32)))
+            for a, b in layer0["rows"]]
+    got = _absorb_gpu([(to_dev(a, "bf16"), to_dev(b, "bf16")) for a, b in rows], W, lam, d)
+    a_loc = np.concatenate([r[0] for r in rows]).astype(np.float64)
+    a_full = np.concatenate([r[1] for r in rows]).astype(np.float64)
+    st = oab.grams(a_loc, a_full)
+    kappa = float(np.linalg.cond(st["G"] + lam * np.eye(d)))
     dW_ref = oab.ridge_delta_w(st["G"], st["C"], W, lam)
-    a_loc = np.concatenate([r[0] for r in rows])
-    a_full = np.concatenate([r[1] for r in rows])
+    eps_ref = oab.layer_error_rows(a_loc, a_full, W, dW_ref)
+    errs = {k: rel_fro(to_host64(got[k]), st[k]) for k in ("G", "X", "F")}
+    e_dw = rel_fro(got["dW"], dW_ref)
+    e_eps = abs(got["eps"] - eps_ref) / eps_ref
+    e_opt = abs(got["eps_opt"] - eps_ref) / eps_ref
+    e_ref = abs(got["ref"] - oab.reference_energy(st["F"], W)) / got["ref"]
+    print(f"   statistics rel_fro {errs}; dW rel_fro {e_dw:.3e}; eps rel {e_eps:.3e} (at the optimum: "
+          f"{e_opt:.3e}); ref rel {e_ref:.3e}; kappa(G + lambda I) {kappa:.3e}", flush=True)
+    assert e_opt <= EPS_GATE
+    assert kappa > 1e3, "these rows are meant to carry the workload's own conditioning"
+    assert all(e <= STATS_GATE for e in errs.values()), errs
+    assert e_dw <= DW_GATE
+    assert e_eps <= EPS_GATE
+    assert e_ref <= EPS_GATE
+
+
+def test_layer0_chain_against_oracle_chain(layer0):
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    wl, W = layer0["wl"], layer0["W"]
+    d, H, lam = wl.d, wl.n_heads, wl.lam
+    dev_rows = []
+    for inp in layer0["chunks"]:
+        dev = {k: to_dev(inp[k], "bf16") for k in QKV}
+        n_q = inp["q"].shape[0]
+        a_loc = torch.empty((n_q, d), dtype=torch.bfloat16, device="cuda")
+        a_full = torch.empty_like(a_loc)
+        lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
+        ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"], dev["hist_k"],
+                            dev["hist_v"], float(inp["scale"]), a_loc, a_full, lse[0], lse[1], lse[2])
+        dev_rows.append((a_loc, a_full))
+    got = _absorb_gpu(dev_rows, W, lam, d)
+
+    st = oab.accumulate(layer0["rows"])
+    dW_ref = oab.ridge_delta_w(st["G"], st["C"], W, lam)
+    a_loc = np.concatenate([r[0] for r in layer0["rows"]])
+    a_full = np.concatenate([r[1] for r in layer0["rows"]])
     eps_ref = oab.layer_error_rows(a_loc, a_full, W, dW_ref)
     kappa = float(np.linalg.cond(st["G"] + lam * np.eye(d)))
-    t_oracle = time.perf_counter() - t0
-
-    e_dw = rel_fro(dW_gpu, dW_ref)
-    e_eps = abs(eps_gpu - eps_ref) / eps_ref
-    print(f"   dW rel_fro {e_dw:.3e}, eps rel {e_eps:.3e}, kappa(G + lambda I) {kappa:.3e}, "
-          f"eps/ref {eps_ref / oab.reference_energy(st['F'], W):.4f}, oracle chain {t_oracle:.1f} s", flush=True)
+    e_dw = rel_fro(got["dW"], dW_ref)
+    e_eps = abs(got["eps"] - eps_ref) / eps_ref
+    print(f"   whole chain: dW rel_fro {e_dw:.3e} (reported), eps rel {e_eps:.3e}, kappa {kappa:.3e}, "
+          f"eps/ref {eps_ref / oab.reference_energy(st['F'], W):.4f}", flush=True)
     assert e_dw <= E2E_DW_GATE
-    assert e_eps <= E2E_EPS_GATE
+    assert e_eps <= EPS_GATE
