@@ -270,6 +270,20 @@ ispa_status ispa_absorb_accumulate(ispa_dtype dt, int64_t n_rows, int32_t d,
                                    float *G, float *X, float *F,
                                    void *ws, size_t ws_bytes, void *stream);
 
+/* The statistics of several layers' chunks in one call (all with the same n_rows and d), for each
+ * layer l:  G[l] += A_loc[l]^T A_loc[l],  X[l] += A_loc[l]^T A_full[l],  F[l] += A_full[l]^T A_full[l].
+ * For a model whose layers' attention outputs of a warmup chunk are kept until the chunk ends. The
+ * sums are bitwise those of `batch` ispa_absorb_accumulate calls (every output element is a fixed-order
+ * sum of exact products); one launch holds the tiles of up to 48 layers, so the GPU stays full at any d.
+ *   a_loc, a_full   host arrays of `batch` device pointers to [n_rows, d] rows (row stride d, 16-byte
+ *                   aligned), type dt
+ *   G, X, F         host arrays of `batch` device pointers to [d, d] fp32 sums (F may be NULL: no F for
+ *                   any layer)
+ * Errors as for ispa_absorb_accumulate; batch >= 0 (0 is a no-op). */
+ispa_status ispa_absorb_accumulate_batched(ispa_dtype dt, int64_t n_rows, int32_t d, int32_t batch,
+                                           const void *const *a_loc, const void *const *a_full,
+                                           float *const *G, float *const *X, float *const *F, void *stream);
+
 /* FP8 statistics (ISPA page, section 4: ISPA with W8A8): the same sums over rows stored as OCP e4m3
  * bytes with one scale per head (rows quantised by ispa_fp8_quantize with scales from
  * ispa_fp8_head_scales): G += A_loc^T A_loc etc. of the dequantised rows e4m3 * scale, exact products

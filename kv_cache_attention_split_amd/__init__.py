@@ -19,7 +19,7 @@ from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVBias, KVSegment, l
 __all__ = [
     "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_future_scores",
     "ispa_future_scores_workspace", "ispa_future_scores_noalloc", "ispa_fp8_head_scales", "ispa_fp8_quantize", "ispa_attn_dual_fp8",
-    "ispa_absorb_accumulate", "ispa_absorb_accumulate_fp8", "ispa_absorb_accumulate_workspace",
+    "ispa_absorb_accumulate", "ispa_absorb_accumulate_batched", "ispa_absorb_accumulate_fp8", "ispa_absorb_accumulate_workspace",
     "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_absorb_solve_eps",
     "ispa_absorb_solve_eps_workspace", "ispa_layer_error",
     "ispa_layer_error_workspace", "ispa_rank_layers", "ispa_apply_delta", "ispa_project",
@@ -299,6 +299,28 @@ def ispa_absorb_accumulate(a_loc, a_full, G, X, F=None, ws=None, stream=None) ->
         _dtype_code(a_loc), n, d, _ptr(a_loc), _ptr(a_full), _ptr(G), _ptr(X), _ptr(F),
         ws_ptr, ws_bytes, _stream_handle(stream))
     _check(st, "ispa_absorb_accumulate")
+
+
+def ispa_absorb_accumulate_batched(a_loc: Sequence, a_full: Sequence, G: Sequence, X: Sequence,
+                                   F: Optional[Sequence] = None, stream=None) -> None:
+    """For each layer l: G[l] += A_loc[l]^T A_loc[l], X[l] += A_loc[l]^T A_full[l], F[l] += A_full[l]^T A_full[l]
+    (lists of [n, d] rows of one dtype and [d, d] fp32 sums; every layer the same n and d)."""
+    batch = len(a_loc)
+    if batch == 0:
+        return
+    n, d = (int(x) for x in a_loc[0].shape)
+    if len(a_full) != batch:
+        raise ValueError("a_loc and a_full must have one entry per layer")
+    for t, what in [(t, "a_loc") for t in a_loc] + [(t, "a_full") for t in a_full]:
+        if tuple(t.shape) != (n, d) or t.dtype != a_loc[0].dtype or not t.is_contiguous():
+            raise ValueError(f"every {what} entry must be a contiguous [{n}, {d}] tensor of one dtype")
+        _device_tensor(t, what)
+    ptrs = [_square_list(m, d, batch, name) for m, name in ((G, "G"), (X, "X"))]
+    fp = _square_list(F, d, batch, "F") if F is not None else None
+    st = lib().ispa_absorb_accumulate_batched(
+        _dtype_code(a_loc[0]), n, d, batch, _ptr_array(a_loc), _ptr_array(a_full), ptrs[0], ptrs[1], fp,
+        _stream_handle(stream))
+    _check(st, "ispa_absorb_accumulate_batched")
 
 
 def ispa_absorb_accumulate_fp8(a_loc, s_loc, a_full, s_full, head_dim: int, G, X, F=None, stream=None) -> None:

@@ -64,6 +64,7 @@ SIGNATURES = {
                                            KVSegment, c_vp, c_i64, c_f32, c_vp, c_vp, c_vp]),
     "ispa_absorb_accumulate_workspace": (c_sz, [c_i64, c_i32]),
     "ispa_absorb_accumulate": (c_int, [c_int, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "ispa_absorb_accumulate_batched": (c_int, [c_int, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "ispa_absorb_accumulate_fp8": (c_int, [c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                            c_sz, c_vp]),
     "ispa_absorb_solve_workspace": (c_sz, [c_i32, c_i32]),

@@ -510,6 +510,36 @@ ispa_status ispa_absorb_accumulate(ispa_dtype dt, int64_t n_rows, int32_t d, con
 }
 
 // ------------------------------------------------------------------------------------------------
+ispa_status ispa_absorb_accumulate_batched(ispa_dtype dt, int64_t n_rows, int32_t d, int32_t batch,
+                                           const void *const *a_loc, const void *const *a_full, float *const *G,
+                                           float *const *X, float *const *F, void *stream) {
+  if (dt != ISPA_BF16 && dt != ISPA_F32) return ISPA_E_UNSUPPORTED;
+  if (n_rows < 0 || d <= 0 || batch < 0) return ISPA_E_ARG;
+  if (d % 64 != 0) return ISPA_E_UNSUPPORTED;
+  if (n_rows > INT32_MAX) return ISPA_E_ARG;
+  if (batch == 0) return ISPA_OK;
+  ispa_status st;
+  if ((st = check_ptr_array(G, batch)) != ISPA_OK) return st;
+  if ((st = check_ptr_array(X, batch)) != ISPA_OK) return st;
+  if (F != nullptr && (st = check_ptr_array(F, batch)) != ISPA_OK) return st;
+  if (n_rows == 0) return ISPA_OK;
+  if (a_loc == nullptr || a_full == nullptr) return ISPA_E_ARG;
+  for (int32_t i = 0; i < batch; ++i)
+    if (a_loc[i] == nullptr || a_full[i] == nullptr || !aligned16(a_loc[i]) || !aligned16(a_full[i]))
+      return ISPA_E_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == ISPA_BF16)
+    return hip_status(launch_gram_bf16_batch(n_rows, d, batch, (const uint16_t *const *)a_loc,
+                                             (const uint16_t *const *)a_full, G, X, F, s));
+  for (int32_t i = 0; i < batch; ++i) {
+    st = ispa_absorb_accumulate(dt, n_rows, d, a_loc[i], a_full[i], G[i], X[i], F != nullptr ? F[i] : nullptr,
+                                nullptr, 0, stream);
+    if (st != ISPA_OK) return st;
+  }
+  return ISPA_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
 ispa_status ispa_absorb_accumulate_fp8(int64_t n_rows, int32_t d, int32_t head_dim, const uint8_t *a_loc,
                                        const float *s_loc, const uint8_t *a_full, const float *s_full, float *G,
                                        float *X, float *F, void *ws, size_t ws_bytes, void *stream) {

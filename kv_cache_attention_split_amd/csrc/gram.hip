@@ -13,6 +13,8 @@
 // registers, no LDS store instructions): while stage s is multiplied, stages s+1..s+3 are in flight.
 // Rows past the end of the chunk are copied from a 16-byte block of zeros, so the loop always runs
 // whole turns of the ring and a partial stage adds exact zeros.
+#include <type_traits>
+
 #include "ispa_internal.hpp"
 #include "device_common.hpp"
 
@@ -43,11 +45,17 @@ static __device__ __attribute__((aligned(16))) uint32_t g_zero_row[4];
     asm volatile("" ::: "memory");       \
   } while (0)
 
+// One launch covers the tiles of up to kMaxGramLayers layers (same n_rows and d): workgroup ids run
+// over (layer, tile) pairs, tiles of one layer consecutive, in the XCD-aware order (each XCD takes a
+// contiguous range, so the tiles that share a layer's rows share an L2; measured better than giving
+// every XCD a share of each layer, which keeps all XCDs on one layer but spreads an XCD's concurrent
+// tiles over several layers).
+constexpr int kMaxGramLayers = 48;
 struct GramArgs {
-  const uint16_t *a_loc, *a_full;
-  float *G, *X, *F;
+  const uint16_t *a_loc[kMaxGramLayers], *a_full[kMaxGramLayers];
+  float *G[kMaxGramLayers], *X[kMaxGramLayers], *F[kMaxGramLayers];
   int64_t n_rows;
-  int d, T, n_upper, with_f;
+  int d, T, n_upper, with_f, tiles;   // T: tiles per dimension; tiles: per layer
 };
 
 __device__ __forceinline__ void tri_decode(int idx, int T, int &ti, int &tj) {
@@ -103,8 +111,9 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wm = w >> 1, wn = w & 1;
 
-  const int n_tiles = g.n_upper * (g.with_f ? 2 : 1) + g.T * g.T;
-  int idx = xcd_remap(blockIdx.x, n_tiles);
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int layer = lin / g.tiles;
+  int idx = lin % g.tiles;
   int mat, ti, tj;   // mat: 0 = G, 1 = F, 2 = X
   if (idx < g.n_upper) {
     mat = 0;
@@ -118,9 +127,9 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
     ti = idx / g.T;
     tj = idx % g.T;
   }
-  const uint16_t *P = (mat == 1) ? g.a_full : g.a_loc;   // rows of the left factor
-  const uint16_t *Q = (mat == 0) ? g.a_loc : g.a_full;   // rows of the right factor
-  float *out = (mat == 0) ? g.G : (mat == 1) ? g.F : g.X;
+  const uint16_t *P = (mat == 1) ? g.a_full[layer] : g.a_loc[layer];   // rows of the left factor
+  const uint16_t *Q = (mat == 0) ? g.a_loc[layer] : g.a_full[layer];   // rows of the right factor
+  float *out = (mat == 0) ? g.G[layer] : (mat == 1) ? g.F[layer] : g.X[layer];
   const int i0 = ti * BT, j0 = tj * BT;
   const int d = g.d;
   const int64_t n_rows = g.n_rows;
@@ -256,6 +265,215 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int mc = i0 + wm * 64 + bi * 32 + 8 * q + 4 * hf;
+          f32x4 add;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) add[e] = acc[bi][bj][4 * q + e];
+          if (mr < d && mc < d) *(f32x4 *)&out[(int64_t)mr * d + mc] = cur[q] + add;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Wide tiles: one workgroup per 256 x 256 output tile, 4 waves of 128 x 128 (a 4 x 4 grid of 32 x 32
+// MFMA blocks each, 256 fp32 accumulators per lane; one workgroup per CU). Per 32-row stage a wave
+// reads 16 KB of operands for 32 MFMAs, half the LDS bytes per FLOP of the 128 x 128 form, and the
+// workgroup takes in half the rows per FLOP. A stage holds four 8 KB half-panels in the layout of
+// the 128 x 128 kernel (32 rows x 128 columns, chunk c of row r at c ^ 4 (r mod 4)): A columns i0..,
+// i0+128.., B columns j0.., j0+128..; wave (wm, wn) reads half-panels wm and 2 + wn only.
+// ---------------------------------------------------------------------------------------------
+constexpr int BTW = 256;                      // output tile
+constexpr int kStageW = 4 * kPart;            // 32 KB
+constexpr int kCopiesW = kStageW / 1024 / 4;  // 8 copy instructions per wave per stage
+
+struct HalfOpsW {
+  bf16x8 a[4], b[4];   // one 16-row step: [32-column block]
+};
+
+__global__ void __launch_bounds__(kThreads, 1) gram_bf16_wide_kernel(GramArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageW];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageW];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageW];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[kStageW];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wm = w >> 1, wn = w & 1;
+
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int layer = lin / g.tiles;
+  int idx = lin % g.tiles;
+  int mat, ti, tj;   // mat: 0 = G, 1 = F, 2 = X
+  if (idx < g.n_upper) {
+    mat = 0;
+    tri_decode(idx, g.T, ti, tj);
+  } else if (g.with_f && idx < 2 * g.n_upper) {
+    mat = 1;
+    tri_decode(idx - g.n_upper, g.T, ti, tj);
+  } else {
+    mat = 2;
+    idx -= g.n_upper * (g.with_f ? 2 : 1);
+    ti = idx / g.T;
+    tj = idx % g.T;
+  }
+  const uint16_t *P = (mat == 1) ? g.a_full[layer] : g.a_loc[layer];
+  const uint16_t *Q = (mat == 0) ? g.a_loc[layer] : g.a_full[layer];
+  float *out = (mat == 0) ? g.G[layer] : (mat == 1) ? g.F[layer] : g.X[layer];
+  const int i0 = ti * BTW, j0 = tj * BTW;
+  const int d = g.d;
+  const int64_t n_rows = g.n_rows;
+  const int nst = (int)((n_rows + BR - 1) / BR);
+
+  // Copy instruction ii of wave w fills 1 KB block blk = w + 4 ii of a stage: half-panel blk / 8, rows
+  // 4 (blk mod 8) .. +3; lane l lands at row 4 (blk mod 8) + l / 16, stored chunk l mod 16, which holds
+  // source chunk (l mod 16) ^ (4 (l / 16)). Columns past d are clamped (their outputs are not stored).
+  const uint8_t *src[kCopiesW];
+  int crow[kCopiesW];
+#pragma unroll
+  for (int ii = 0; ii < kCopiesW; ++ii) {
+    const int blk = w + 4 * ii;
+    const int part = blk >> 3;
+    const int r = 4 * (blk & 7) + (lane >> 4);
+    const int c = (lane & 15) ^ (4 * (lane >> 4));
+    int col = (part < 2 ? i0 + 128 * part : j0 + 128 * (part - 2)) + 8 * c;
+    col = col < d ? col : d - 8;
+    crow[ii] = r;
+    src[ii] = (const uint8_t *)((part < 2 ? P : Q) + (int64_t)r * d + col);
+  }
+  const int64_t stage_bytes = (int64_t)BR * d * 2;
+  uint64_t zero_row = (uint64_t)(uintptr_t)g_zero_row;
+  asm volatile("" : "+s"(zero_row));
+
+  // Stages whose rows all exist are copied with one address add per instruction (FULL); a stage that
+  // reaches past the last row selects the zero block per lane.
+  auto copy_stage = [&](auto full, int s, uint8_t *slot) {
+#pragma unroll
+    for (int ii = 0; ii < kCopiesW; ++ii) {
+      const uint8_t *p = src[ii] + (int64_t)s * stage_bytes;
+      if constexpr (!decltype(full)::value) {
+        const int64_t n = (int64_t)s * BR + crow[ii];
+        p = n < n_rows ? p : (const uint8_t *)(uintptr_t)zero_row;
+      }
+      copy_to_lds<16>(p, slot + 1024 * (w + 4 * ii));
+    }
+  };
+  auto read_half = [&](const uint8_t *slot, int t, HalfOpsW &o) {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) o.a[bi] = read_operand(slot + kPart * wm, bi * 32, 16 * t, lane);
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) o.b[bj] = read_operand(slot + kPart * (2 + wn), bj * 32, 16 * t, lane);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
+  auto mma = [&](const HalfOpsW &o) {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mfma_bf16_32x32x16(o.a[bi], o.b[bj], acc[bi][bj]);
+  };
+
+  // Stage s, pipelined by half-stage (16 rows): the first half's operands are in registers (h0); the
+  // second half is read while the first is multiplied; then, once every wave is done with the slot and
+  // this wave's copies of stage s+1 have landed, the slot is refilled with stage s+4 and the first half
+  // of stage s+1 is read while the second half of stage s is multiplied.
+  HalfOpsW h0, h1;
+  auto stage = [&](auto full, int s, uint8_t *cur, const uint8_t *nxt) {
+    read_half(cur, 1, h1);
+    mma(h0);
+    // one MFMA first (the wait for h0's reads then precedes h1's reads), h1's reads within the next
+    // eight MFMAs, and seven MFMAs left to cover their latency before the barrier's wait
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 7, 0);
+    ISPA_GRAM_WAIT_VMCNT(kCopiesW * (NS - 2));   // this wave's copies of stage s+1 have landed
+    ISPA_GRAM_LDS_BARRIER();                     // ... everyone's; all reads of stage s are done
+    copy_stage(full, s + NS, cur);
+    read_half(nxt, 0, h0);
+    mma(h1);
+    // one copy and one operand (two reads) per MFMA over the first eight, then seven MFMAs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+
+  using full_t = std::integral_constant<bool, true>;
+  using part_t = std::integral_constant<bool, false>;
+  copy_stage(part_t{}, 0, ring0);
+  copy_stage(part_t{}, 1, ring1);
+  copy_stage(part_t{}, 2, ring2);
+  copy_stage(part_t{}, 3, ring3);
+  ISPA_GRAM_WAIT_VMCNT(kCopiesW * (NS - 1));
+  ISPA_GRAM_LDS_BARRIER();
+  read_half(ring0, 0, h0);
+  // turns of the ring whose refills (stages s + 4 .. s + 7) hold only existing rows, then the rest
+  const int n_full = (int)(n_rows / BR);
+  int s = 0;
+  for (; s + 2 * NS <= n_full; s += NS) {
+    stage(full_t{}, s, ring0, ring1);
+    stage(full_t{}, s + 1, ring1, ring2);
+    stage(full_t{}, s + 2, ring2, ring3);
+    stage(full_t{}, s + 3, ring3, ring0);
+  }
+  for (; s < nst; s += NS) {
+    stage(part_t{}, s, ring0, ring1);
+    stage(part_t{}, s + 1, ring1, ring2);
+    stage(part_t{}, s + 2, ring2, ring3);
+    stage(part_t{}, s + 3, ring3, ring0);
+  }
+  ISPA_GRAM_WAIT_VMCNT(0);   // no copy may land in LDS after the workgroup has ended
+
+  // Add the tile to the running sums (lane (l32, hf) of block (bi, bj) holds rows 8 q + 4 hf + e of
+  // column l32), and mirror off-diagonal G and F tiles with 16-byte accesses.
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int cl = j0 + wn * 128 + bj * 32 + l32;
+      const int clc = cl < d ? cl : d - 1;
+      float cur[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rw = i0 + wm * 128 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        const int rwc = rw < d ? rw : d - 1;
+        cur[v] = out[(int64_t)rwc * d + clc];
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rw = i0 + wm * 128 + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        if (rw < d && cl < d) out[(int64_t)rw * d + cl] = cur[v] + acc[bi][bj][v];
+      }
+    }
+  if (mat != 2 && ti != tj) {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) {
+        const int mr = j0 + wn * 128 + bj * 32 + l32;
+        const int mrc = mr < d ? mr : d - 1;
+        f32x4 cur[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int mc = i0 + wm * 128 + bi * 32 + 8 * q + 4 * hf;
+          const int mcc = mc < d ? mc : d - 4;
+          cur[q] = *(const f32x4 *)&out[(int64_t)mrc * d + mcc];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int mc = i0 + wm * 128 + bi * 32 + 8 * q + 4 * hf;
           f32x4 add;
 #pragma unroll
           for (int e = 0; e < 4; ++e) add[e] = acc[bi][bj][4 * q + e];
@@ -507,23 +725,52 @@ hipError_t launch_gram_fp8(int64_t n_rows, int d, int head_dim, const uint8_t *a
   return hipGetLastError();
 }
 
+int gram_tiles(int d, int bt, bool with_f) {
+  const int T = (d + bt - 1) / bt;
+  return T * (T + 1) / 2 * (with_f ? 2 : 1) + T * T;
+}
+
+#ifndef ISPA_GRAM_WIDE_MIN
+#define ISPA_GRAM_WIDE_MIN 512   // wide-tile workgroups a launch needs before the wide kernel is used
+#endif
+
+hipError_t launch_gram_bf16_batch(int64_t n_rows, int d, int batch, const uint16_t *const *a_loc,
+                                  const uint16_t *const *a_full, float *const *G, float *const *X,
+                                  float *const *F, hipStream_t s) {
+  if (n_rows == 0 || batch <= 0 || d < 8) return hipSuccess;
+  const bool with_f = F != nullptr;
+  for (int p0 = 0; p0 < batch; p0 += kMaxGramLayers) {
+    const int cnt = batch - p0 < kMaxGramLayers ? batch - p0 : kMaxGramLayers;
+    const bool wide = (int64_t)gram_tiles(d, BTW, with_f) * cnt >= ISPA_GRAM_WIDE_MIN;
+    const int bt = wide ? BTW : BT;
+    GramArgs g;
+    for (int i = 0; i < cnt; ++i) {
+      g.a_loc[i] = a_loc[p0 + i];
+      g.a_full[i] = a_full[p0 + i];
+      g.G[i] = G[p0 + i];
+      g.X[i] = X[p0 + i];
+      g.F[i] = with_f ? F[p0 + i] : nullptr;
+    }
+    g.n_rows = n_rows;
+    g.d = d;
+    g.T = (d + bt - 1) / bt;
+    g.n_upper = g.T * (g.T + 1) / 2;
+    g.with_f = with_f;
+    g.tiles = gram_tiles(d, bt, with_f);
+    const dim3 grid((unsigned)(g.tiles * cnt));
+    if (wide)
+      hipLaunchKernelGGL(gram_bf16_wide_kernel, grid, dim3(kThreads), 0, s, g);
+    else
+      hipLaunchKernelGGL(gram_bf16_kernel, grid, dim3(kThreads), 0, s, g);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_gram_bf16(int64_t n_rows, int d, const uint16_t *a_loc, const uint16_t *a_full,
                             float *G, float *X, float *F, hipStream_t s) {
-  GramArgs g;
-  g.a_loc = a_loc;
-  g.a_full = a_full;
-  g.G = G;
-  g.X = X;
-  g.F = F;
-  g.n_rows = n_rows;
-  g.d = d;
-  g.T = (d + BT - 1) / BT;
-  g.n_upper = g.T * (g.T + 1) / 2;
-  g.with_f = F != nullptr;
-  const int n_tiles = g.n_upper * (g.with_f ? 2 : 1) + g.T * g.T;
-  if (n_rows == 0 || n_tiles == 0 || d < 8) return hipSuccess;
-  hipLaunchKernelGGL(gram_bf16_kernel, dim3(n_tiles), dim3(kThreads), 0, s, g);
-  return hipGetLastError();
+  return launch_gram_bf16_batch(n_rows, d, 1, &a_loc, &a_full, &G, &X, F != nullptr ? &F : nullptr, s);
 }
 
 }  // namespace ispa

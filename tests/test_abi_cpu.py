@@ -240,6 +240,24 @@ def ptrs(n, base=FAKE):
     return arr
 
 
+def test_accumulate_batched_argument_errors(L):
+    f = L.ispa_absorb_accumulate_batched
+    b = 3
+    P = ptrs(b)
+    assert f(2, 100, 1536, b, P, P, P, P, P, None) == _abi.ISPA_E_UNSUPPORTED      # dtype
+    assert f(1, 100, 1000, b, P, P, P, P, P, None) == _abi.ISPA_E_UNSUPPORTED      # d % 64
+    assert f(1, -1, 1536, b, P, P, P, P, P, None) == _abi.ISPA_E_ARG
+    assert f(1, 100, 1536, -1, P, P, P, P, P, None) == _abi.ISPA_E_ARG
+    assert f(1, 100, 1536, 0, None, None, None, None, None, None) == _abi.ISPA_OK
+    assert f(1, 100, 1536, b, None, P, P, P, P, None) == _abi.ISPA_E_ARG
+    assert f(1, 100, 1536, b, P, P, None, P, P, None) == _abi.ISPA_E_ARG
+    bad = ptrs(b)
+    bad[2] = MISALIGNED
+    assert f(1, 100, 1536, b, bad, P, P, P, P, None) == _abi.ISPA_E_ARG
+    assert f(1, 100, 1536, b, P, P, P, bad, P, None) == _abi.ISPA_E_ARG
+    assert f(1, 0, 1536, b, None, None, P, P, None, None) == _abi.ISPA_OK              # no rows: no-op
+
+
 def test_solve_argument_errors_and_workspace(L):
     d, b = 256, 3
     need = L.ispa_absorb_solve_workspace(d, b)

@@ -418,3 +418,74 @@ def test_solve_eps_failed_factorisation_is_nan():
     _, info, eps, _ = _solve_eps_gpu([G, Z], [X, Z.clone()], [F, Z.clone()], [W, W], 0.0)
     assert info[0] == 0 and info[1] == 1
     assert np.isfinite(eps[0]) and np.isnan(eps[1])
+
+
+def _batched_stats(rows, d, with_f=True):
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    al = [to_dev(r["a_loc"], "bf16") for r in rows]
+    af = [to_dev(r["a_full"], "bf16") for r in rows]
+    st = [[torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)] for _ in rows]
+    ispa.ispa_absorb_accumulate_batched(al, af, [s[0] for s in st], [s[1] for s in st],
+                                        [s[2] for s in st] if with_f else None)
+    torch.cuda.synchronize()
+    return al, af, st
+
+
+@pytest.mark.parametrize("d,n,batch,with_f", [(1536, 4680, 8, True), (1088, 517, 10, True),
+                                              (1536, 333, 10, False), (256, 300, 50, True)])
+def test_statistics_batched_against_oracle_and_single_calls(d, n, batch, with_f):
+    """Statistics of a batch of layers in one call (256 x 256 tiles once a launch has 512 of them: the
+    first three cases; 50 layers of d = 256 run as launches of 48 and 2 layers of 128 x 128 tiles):
+    every layer within 1e-5 of the oracle and bit for bit what one call per layer gives (which uses
+    128 x 128 tiles here: every element is the same fixed-order sum of exact products), G and F exactly
+    symmetric; d = 1088 ends inside a tile and 517 / 333 rows end inside a stage."""
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    _log(f"case: batched statistics d={d} rows={n} layers={batch} F={with_f}")
+    rows = [inputs.absorb_rows(3, layer, 3, d=d, n_rows=n) for layer in range(batch)]
+    al, af, st = _batched_stats(rows, d, with_f)
+    worst = 0.0
+    for i, r in enumerate(rows):
+        ref = oab.grams(r["a_loc"], r["a_full"])
+        for k, name in enumerate(("G", "X", "F")):
+            if name == "F" and not with_f:
+                assert not st[i][2].any()
+                continue
+            err = rel_fro(to_host64(st[i][k]), ref[name])
+            worst = max(worst, err)
+            assert err <= 1e-5, (i, name, err)
+        assert torch.equal(st[i][0], st[i][0].T)
+        if with_f:
+            assert torch.equal(st[i][2], st[i][2].T)
+        if i < 3 or i == batch - 1:
+            one = [torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)]
+            ispa.ispa_absorb_accumulate(al[i], af[i], one[0], one[1], one[2] if with_f else None)
+            torch.cuda.synchronize()
+            for k in range(3 if with_f else 2):
+                assert torch.equal(one[k], st[i][k]), (i, k)
+    _log(f"  worst rel_fro {worst:.2e}")
+
+
+def test_statistics_wide_tiles_accumulate_over_chunks():
+    """Four chunks accumulated through the batched call (8 layers of d = 1536, wide tiles): the running
+    sums equal the oracle's over the stacked rows, and the first two chunks (no history) leave X = G
+    bitwise."""
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    d, layers = 1536, 8
+    _log(f"case: batched statistics over 4 chunks, {layers} layers, d={d}")
+    st = [[torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)] for _ in range(layers)]
+    chunks = [[inputs.absorb_rows(3, l, c) for c in range(4)] for l in range(layers)]
+    for c in range(4):
+        al = [to_dev(chunks[l][c]["a_loc"], "bf16") for l in range(layers)]
+        af = [to_dev(chunks[l][c]["a_full"], "bf16") for l in range(layers)]
+        ispa.ispa_absorb_accumulate_batched(al, af, [s[0] for s in st], [s[1] for s in st], [s[2] for s in st])
+        if c == 1:
+            torch.cuda.synchronize()
+            assert all(torch.equal(s[1], s[0]) for s in st), "X != G with A_full == A_loc"
+    torch.cuda.synchronize()
+    for l in (0, layers - 1):
+        ref = oab.accumulate([(ch["a_loc"], ch["a_full"]) for ch in chunks[l]])
+        for k, name in enumerate(("G", "X", "F")):
+            assert rel_fro(to_host64(st[l][k]), ref[name]) <= 1e-5
