@@ -1,18 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the ISPA hot path on one MI355X.
 
-One step = one full ISPA warmup of a Wan-1.3B-shaped model (workload "wan1.3b-warmup"): 30 layers x
-4 chunks of dual-stream attention (12 heads x 128, 4680 queries per 3-frame chunk, history growing
-0 -> 9 frames) each followed by the warmup-statistics update, then the batched ridge solve of all
-30 layers (d = 1536, lambda = 1e-2), their reconstruction errors, and the selection of K = 15
-L-Layers (errors copied to the host and ranked there). Inputs are seeded synthetic tensors already
-resident in HBM when the timed region starts. `--workload-cfg 4` runs the same step at the 14B shape
-(40 layers x 40 heads, d = 5120, K = 20).
+One step = one full ISPA warmup of a Wan-1.3B-shaped model (workload "wan1.3b-warmup"): for each of
+the 4 chunks (4680 queries of a 3-frame chunk, history growing 0 -> 9 frames), the dual-stream
+attention of each of the 30 layers (12 heads x 128) into that layer's A_loc / A_full, then the
+warmup-statistics update of all 30 layers in one batched call; after the last chunk one batched ridge
+solve of all layers (d = 1536, lambda = 1e-2) with each layer's reconstruction error at its optimum,
+the errors copied to the host and the K = 15 L-Layers selected there. Inputs are seeded synthetic
+tensors already resident in HBM when the timed region starts. `--workload-cfg 4` runs the same step
+at the 14B shape (40 layers x 40 heads, d = 5120, K = 20).
 
-Prints one JSON line. `value` is the step's algorithmic TFLOP/s (attention 4 n_q n_keys H d_h per
-call, statistics 4 N d^2 per chunk, solve 13/3 d^3, error 4 d^3 per layer) over the measured step
-time; the attention kernel's own rate, its fraction of the bf16 MFMA peak, and the absorb time per
-layer are reported beside it, with the oracle timed on the host cores on a bounded sample.
+Prints one JSON line. `value` is the dual-stream attention's rate inside the step (algorithmic
+4 n_q n_keys H d_h FLOP per call over the average launch time from HIP events), the metric's first
+half; the absorb time per layer (statistics + solve + error), the step's own rate, the attention on
+the 60-frame history (workload 5) and on the 14B shape's last warmup chunk, and the statistics
+kernel's roofline are reported beside it, with the oracle timed on the host cores on a bounded sample.
 """
 from __future__ import annotations
 
@@ -43,6 +45,8 @@ def parse():
                     help="workload of the timed step: 3 = the Wan-1.3B warmup (default), 4 = the 14B warmup "
                          "(40 layers x 40 heads, d = 5120)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the attention timings on workloads 5 and 4 that follow the step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (HBM counter calibration)")
     ap.add_argument("--attn-only-cfg", type=int, default=None,
@@ -117,6 +121,23 @@ def attn_traffic():
     except OSError:
         return None
     return ATTN_TRAFFIC["bytes_per_launch"] if digest == ATTN_TRAFFIC["sha256"] else None
+
+
+# HBM bytes per statistics launch of the warmup step (one batched call: 30 layers x one 4680-row
+# chunk), from rocprofv3 FETCH_SIZE / WRITE_SIZE scaled as above, taken on the statistics source with
+# this SHA-256; reported only while the source is unchanged.
+GRAM_TRAFFIC = {"sha256": None, "bytes_per_launch": None}
+
+
+def gram_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "kv_cache_attention_split_amd", "csrc", "gram.hip")
+    try:
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return GRAM_TRAFFIC["bytes_per_launch"] if digest == GRAM_TRAFFIC["sha256"] else None
 
 
 def cpu_baseline(wl):
@@ -282,27 +303,33 @@ def attn_report(cfg, steps, warmup, torch):
 
 
 def gram_report(cfg, steps, warmup, torch):
-    """Statistics update of one 4680-row chunk at a workload's width d: warm median time and rate
-    (4 N d^2 FLOP: G and F as half products, X in full)."""
+    """Statistics update of one 4680-row chunk at a workload's width d: one layer per call, and all the
+    workload's layers in one batched call (warm median time and rate; 4 N d^2 FLOP per layer: G and F as
+    half products, X in full)."""
     import ispa_inputs as inputs
     import kv_cache_attention_split_amd as ispa
     wl = inputs.CONFIGS[cfg]
-    d, n = wl.d, inputs.CHUNK_TOKENS
+    d, n, L = wl.d, inputs.CHUNK_TOKENS, wl.n_layers
     g = torch.Generator(device="cuda").manual_seed(1234 + cfg)
-    a_loc = (0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16)
-    a_full = (0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16)
-    st = [torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)]
-    call = lambda: ispa.ispa_absorb_accumulate(a_loc, a_full, st[0], st[1], st[2])   # noqa: E731
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 0.5:
-        call()
-        torch.cuda.synchronize()
-    ms = float(np.median([_time_calls(call, steps, warmup, torch) for _ in range(3)]))
-    fl = 4.0 * n * d * d
-    print(json.dumps({"workload": wl.name, "statistics": {"rows": n, "d": d, "ms": round(ms, 4),
-                                                          "tflops": round(fl / ms / 1e9, 1),
-                                                          "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}}),
-          flush=True)
+    a_loc = [(0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16) for _ in range(L)]
+    a_full = [(0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16) for _ in range(L)]
+    st = [[torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)] for _ in range(L)]
+    calls = {
+        "one_layer": (1, lambda: ispa.ispa_absorb_accumulate(a_loc[0], a_full[0], st[0][0], st[0][1], st[0][2])),
+        "all_layers": (L, lambda: ispa.ispa_absorb_accumulate_batched(a_loc, a_full, [s[0] for s in st],
+                                                                      [s[1] for s in st], [s[2] for s in st])),
+    }
+    out = {"workload": wl.name, "rows": n, "d": d}
+    for name, (layers, call) in calls.items():
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            call()
+            torch.cuda.synchronize()
+        ms = float(np.median([_time_calls(call, steps, warmup, torch) for _ in range(3)]))
+        fl = 4.0 * n * d * d * layers
+        out[name] = {"layers": layers, "ms": round(ms, 4), "ms_per_layer": round(ms / layers, 4),
+                     "tflops": round(fl / ms / 1e9, 1), "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    print(json.dumps({"statistics": out}), flush=True)
 
 
 def absorb_report(cfg, steps, warmup, torch):
@@ -699,16 +726,16 @@ def main():
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t0
 
-    a_loc = torch.empty((n_q, d), dtype=torch.bfloat16, device="cuda")
-    a_full = torch.empty_like(a_loc)
+    # each layer's chunk outputs stay until the chunk's statistics are taken
+    a_loc = [torch.empty((n_q, d), dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    a_full = [torch.empty_like(x) for x in a_loc]
     lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
     stats = [[torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)] for _ in range(n_layers)]
     dW = [torch.empty((d, d), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
     info = torch.zeros((n_layers,), dtype=torch.int32, device="cuda")
     eps = torch.zeros((n_layers,), dtype=torch.float64, device="cuda")
     ref = torch.zeros((n_layers,), dtype=torch.float64, device="cuda")
-    ws_solve = torch.empty(ispa.ispa_absorb_solve_workspace(d, n_layers), dtype=torch.uint8, device="cuda")
-    ws_err = torch.empty(ispa.ispa_layer_error_workspace(d, n_layers), dtype=torch.uint8, device="cuda")
+    ws_solve = torch.empty(ispa.ispa_absorb_solve_eps_workspace(d, n_layers), dtype=torch.uint8, device="cuda")
     Gs = [s[0] for s in stats]
     Xs = [s[1] for s in stats]
     Fs = [s[2] for s in stats]
@@ -717,46 +744,46 @@ def main():
     seg_keys = [sum(wl.segment_sizes(c)[k] for k in ("n_sink", "n_cur", "n_hist"))
                 for c in range(len(wl.chunks))]
     flops_attn = sum(attn_flops(n_q, nk, H, dh) for nk in seg_keys) * n_layers
-    flops_stats = 4.0 * n_q * len(wl.chunks) * d * d * n_layers
+    flops_stats_chunk = 4.0 * n_q * d * d * n_layers        # one batched call
+    flops_stats = flops_stats_chunk * len(wl.chunks)
     flops_solve = 13.0 / 3.0 * d ** 3 * n_layers
-    flops_err = 4.0 * d ** 3 * n_layers
+    flops_err = 1.0 * d ** 3 * n_layers                     # W W^T, lower tiles
     flops_step = flops_attn + flops_stats + flops_solve + flops_err
 
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
-    timing = {"attn": [], "stats": [], "solve": [], "error": []}
+    timing = {"attn": [], "stats": [], "solve": []}
 
     def step(record: bool):
         for s in stats:
             for t in s:
                 t.zero_()
-        for li, L in enumerate(layers):
-            for c, ch in enumerate(wl.chunks):
+        for c, ch in enumerate(wl.chunks):
+            for li, L in enumerate(layers):
                 sk, sv = L.seg(ch.sink)
                 ck, cv = L.seg(ch.cur)
                 hk, hv = L.seg(ch.hist)
                 if record:
-                    e0, e1, e2 = ev(), ev(), ev()
+                    e0, e1 = ev(), ev()
                     e0.record()
-                ispa.ispa_attn_dual(L.q[c], sk, sv, ck, cv, hk, hv, wl.scale, a_loc, a_full,
+                ispa.ispa_attn_dual(L.q[c], sk, sv, ck, cv, hk, hv, wl.scale, a_loc[li], a_full[li],
                                     lse[0], lse[1], lse[2])
                 if record:
                     e1.record()
-                ispa.ispa_absorb_accumulate(a_loc, a_full, stats[li][0], stats[li][1], stats[li][2])
-                if record:
-                    e2.record()
                     timing["attn"].append((e0, e1, seg_keys[c]))
-                    timing["stats"].append((e1, e2))
+            if record:
+                e0, e1 = ev(), ev()
+                e0.record()
+            ispa.ispa_absorb_accumulate_batched(a_loc, a_full, Gs, Xs, Fs)
+            if record:
+                e1.record()
+                timing["stats"].append((e0, e1))
         if record:
-            e3, e4, e5 = ev(), ev(), ev()
+            e3, e4 = ev(), ev()
             e3.record()
-        ispa.ispa_absorb_solve(Gs, Xs, Ws, dW, wl.lam, info, ws_solve)
+        ispa.ispa_absorb_solve_eps(Gs, Xs, Fs, Ws, dW, wl.lam, info, eps, ref, ws_solve)
         if record:
             e4.record()
-        ispa.ispa_layer_error(Gs, Xs, Fs, Ws, dW, eps, ref, ws_err)
-        if record:
-            e5.record()
             timing["solve"].append((e3, e4))
-            timing["error"].append((e4, e5))
         eps_host = eps.cpu().numpy()        # synchronises: the ranking runs on the host
         return ispa.ispa_rank_layers(eps_host.tolist(), min(wl.k_select, n_layers))
 
@@ -771,8 +798,8 @@ def main():
     att_avg_ms = att_ms / len(att)
     att_flops_per_launch = flops_attn / len(att)
     stats_ms = sum(a.elapsed_time(b) for a, b in timing["stats"])
+    stats_avg_ms = stats_ms / len(timing["stats"])
     solve_ms = sum(a.elapsed_time(b) for a, b in timing["solve"])
-    err_ms = sum(a.elapsed_time(b) for a, b in timing["error"])
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -782,10 +809,16 @@ def main():
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     att_tflops = att_flops_per_launch / att_avg_ms / 1e9
+    stats_tflops = flops_stats_chunk / stats_avg_ms / 1e9
     info_h = info.cpu().tolist()
+    eps_h = eps.cpu().tolist()
+    ref_h = ref.cpu().tolist()
+    del a_loc, a_full, stats, Gs, Xs, Fs, dW, ws_solve
+    torch.cuda.empty_cache()
+    extra = {} if args.no_extra else extra_attention(wl.cfg, torch)
     out = {
         "metric": "dual-stream attn TFLOP/s (% MFMA peak); ΔW absorb ms/layer, 1.3B shape",
-        "value": round(flops_step / ms_step / 1e9, 2),
+        "value": round(att_tflops, 1),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -802,12 +835,13 @@ def main():
         "attn_tflops": round(att_tflops, 1),
         "attn_frac_mfma_peak": round(att_tflops / PEAK_BF16_TFLOPS, 4),
         "attn_ms_per_layer": round(att_ms / n_layers, 4),
-        "absorb_ms_per_layer": round((stats_ms + solve_ms + err_ms) / n_layers, 4),
+        "absorb_ms_per_layer": round((stats_ms + solve_ms) / n_layers, 4),
         "absorb_breakdown_ms_per_layer": {"statistics": round(stats_ms / n_layers, 4),
-                                          "solve": round(solve_ms / n_layers, 4),
-                                          "error": round(err_ms / n_layers, 4)},
-        "stats_tflops": round(flops_stats / stats_ms / 1e9, 1),
+                                          "solve_and_error": round(solve_ms / n_layers, 4)},
+        "stats_tflops": round(stats_tflops, 1),
+        "step_tflops": round(flops_step / ms_step / 1e9, 2),
         "solve_info_nonzero": int(sum(1 for x in info_h if x != 0)),
+        "eps_over_ref": [round(e / r, 6) for e, r in zip(eps_h, ref_h)][:4],
         "selected_l_layers": sel,
         "roofline": {"kernel": "attn_dual_bf16_pp_kernel", "bound": "mfma",
                      "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -815,11 +849,70 @@ def main():
                      "traffic": attn_traffic() if wl.cfg == 3 else None,
                      "avg_launch_ms": round(att_avg_ms, 5),
                      "flops_per_launch": att_flops_per_launch},
+        "roofline_statistics": {"kernel": stats_kernel_name(d, n_layers), "bound": "mfma",
+                                "achieved": round(stats_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(stats_tflops / PEAK_BF16_TFLOPS, 4),
+                                "traffic": gram_traffic() if wl.cfg == 3 and n_layers == wl.n_layers else None,
+                                "avg_launch_ms": round(stats_avg_ms, 5),
+                                "flops_per_launch": flops_stats_chunk},
+        **extra,
         "setup_s": round(t_setup, 1),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
+
+
+def stats_kernel_name(d, n_layers):
+    """The statistics kernel one batched call of n_layers layers at width d runs (the library's rule:
+    256 x 256 tiles once a launch of up to 48 layers has 512 of them)."""
+    T = (d + 255) // 256
+    wide = (T * (T + 1) + T * T) * min(n_layers, 48) >= 512
+    return "gram_bf16_wide_kernel" if wide else "gram_bf16_kernel"
+
+
+def extra_attention(step_cfg, torch):
+    """Dual-stream attention on the other workloads the metric names, timed after the step (HIP events,
+    median of 20 calls after a half-second warm-up each): the 60-frame history (workload 5, dual and
+    local-only) and the 14B shape's last warmup chunk (workload 4 chunk 4, layer 0)."""
+    import ispa_inputs as inputs
+    import kv_cache_attention_split_amd as ispa
+    out = {}
+    cases = [(5, 0, "attn_wan1.3b_long"), (4, 3, "attn_wan14b_chunk4")]
+    for cfg, chunk, key in cases:
+        wl = inputs.CONFIGS[cfg]
+        inp = inputs.attention_inputs(cfg, 0, chunk)
+        dev = {k: bf16_dev(inp[k], torch) for k in ("q", "sink_k", "sink_v", "cur_k", "cur_v", "hist_k", "hist_v")}
+        n_q = inp["q"].shape[0]
+        H, dh = wl.n_heads, wl.head_dim
+        a_l = torch.empty((n_q, H * dh), dtype=torch.bfloat16, device="cuda")
+        a_f = torch.empty_like(a_l)
+        lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
+        empty = dev["hist_k"][:0]
+        n_sc = inp["sink_k"].shape[0] + inp["cur_k"].shape[0]
+        n_all = n_sc + inp["hist_k"].shape[0]
+        forms = {"dual": (n_all, lambda: ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"],
+                                                             dev["cur_v"], dev["hist_k"], dev["hist_v"], wl.scale,
+                                                             a_l, a_f, lse[0], lse[1], lse[2]))}
+        if cfg == 5:
+            forms["local"] = (n_sc, lambda: ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"],
+                                                                dev["cur_v"], empty, empty, wl.scale, a_l, None, lse[0]))
+        res = {"workload": wl.name, "n_q": n_q, "heads": H}
+        for form, (nk, call) in forms.items():
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.5:
+                call()
+                torch.cuda.synchronize()
+            ms = _time_calls(call, 20, 2, torch)
+            tf = attn_flops(n_q, nk, H, dh) / ms / 1e9
+            res[form] = {"keys": nk, "ms": round(ms, 4), "tflops": round(tf, 1),
+                         "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        if "local" in res:
+            res["full_over_local_time"] = round(res["dual"]["ms"] / res["local"]["ms"], 3)
+        out[key] = res
+        del dev, a_l, a_f, lse
+        torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
