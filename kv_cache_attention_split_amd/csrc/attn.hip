@@ -97,12 +97,13 @@ __device__ __forceinline__ void dma_tile(const SegRun &run, int64_t j0, int head
   const uint16_t *base1 = VALUE ? run.v1 : run.k1;
   if (in_first || in_second) {
     // whole tile inside one sub-run: no clamping; each lane's 64-bit address is the tile base plus
-    // its row and chunk offset (rows < BK, strides < 2^23 elements)
+    // its row and chunk offset. Rows (< BK) and strides (< 2^23 elements) both fit in 24 bits, so the
+    // offset is one full-rate 24-bit multiply (exact: the product is below 2^29)
     const uint16_t *tb = (in_first ? base0 + j0 * run.s0 : base1 + (j0 - run.split) * run.s1) + head_off;
-    const int64_t st = in_first ? run.s0 : run.s1;
+    const uint32_t st = (uint32_t)(in_first ? run.s0 : run.s1);
 #pragma unroll
     for (int ii = 0; ii < NW; ++ii)
-      copy_to_lds<16>(tb + (int64_t)rr[ii] * st + cc8[ii], lds_tile + 1024 * (w + 4 * ii));
+      copy_to_lds<16>(tb + (__umul24((uint32_t)rr[ii], st) + (uint32_t)cc8[ii]), lds_tile + 1024 * (w + 4 * ii));
     return;
   }
 #pragma unroll
