@@ -105,11 +105,11 @@ class Layer:
 
 
 # HBM bytes per attention launch of the warmup step (average over its 4 chunk shapes), from
-# rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
+# rocprofv3 FETCH_SIZE x 1.9997 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
 # attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only
 # while the source is unchanged.
-ATTN_TRAFFIC = {"sha256": "12e459fde9f5702687ca7c0c093c07fc5178e132af1e5e2bf8efe2824f951124",
-                "bytes_per_launch": 158831604}
+ATTN_TRAFFIC = {"sha256": "1c913a30b57e0b913a543a7e095ffd519fd715f5bab3cdc9c8e6e90bf20f7096",
+                "bytes_per_launch": 157819171}
 
 
 def attn_traffic():
@@ -124,9 +124,10 @@ def attn_traffic():
 
 
 # HBM bytes per statistics launch of the warmup step (one batched call: 30 layers x one 4680-row
-# chunk), from rocprofv3 FETCH_SIZE / WRITE_SIZE scaled as above, taken on the statistics source with
-# this SHA-256; reported only while the source is unchanged.
-GRAM_TRAFFIC = {"sha256": None, "bytes_per_launch": None}
+# chunk, the 256 x 256 tile kernel), from the same FETCH_SIZE / WRITE_SIZE runs and factors, taken on
+# the statistics source with this SHA-256; reported only while the source is unchanged.
+GRAM_TRAFFIC = {"sha256": "acceeb00638ccf90b2ebd4fb5c814933a1525620ad2ecaf63af8fca92568a296",
+                "bytes_per_launch": 6343871925}
 
 
 def gram_traffic():
