@@ -15,6 +15,12 @@ the arithmetic of each step is pinned):
   * attention: the scores use the dequantised values q = e4m3_value * scale_q, k = e4m3_value *
     scale_k with exact products; values and probabilities stay at bf16 (only the score product is in
     FP8), so the FP8 attention oracle is the plain attention oracle on dequantised Q and K;
+  * attention with an FP8 value product as well: the values are quantised per head over the whole cache
+    like the keys, and the oracle is the plain attention oracle on dequantised Q, K and V. The device also
+    rounds each probability to e4m3 before the value product; that rounding depends on the running
+    maximum of an online softmax, which a plain definition does not have, so it is not part of the oracle
+    (parity unpinned as to the probability rounding; `p_rounding_sigma` gives the spread it causes under a
+    rounding model, for tolerances);
   * statistics: the attention outputs A_loc and A_full (rows [n, d], d = H * d_h) are quantised per
     head like the keys; G, X, F are the Gram sums of the dequantised rows (exact products), so the
     FP8 statistics oracle is the plain one on dequantised rows.
@@ -85,15 +91,42 @@ def dequantize(codes, scale) -> np.ndarray:
 
 
 def dual_stream_fp8(inp: Dict[str, np.ndarray], q_codes, q_scale, k_codes: Dict[str, np.ndarray], k_scale,
-                    scale: float = None, rows=None) -> Dict[str, np.ndarray]:
-    """The dual-stream outputs with the scores taken from dequantised e4m3 queries and keys (values
-    as given). `k_codes` maps "sink", "cur", "hist" to key codes; one key scale per head for all."""
+                    scale: float = None, rows=None, v_codes: Dict[str, np.ndarray] = None,
+                    v_scale=None) -> Dict[str, np.ndarray]:
+    """The dual-stream outputs with the scores taken from dequantised e4m3 queries and keys, and the
+    values as given or, with `v_codes` / `v_scale`, dequantised e4m3 values. `k_codes` and `v_codes` map
+    "sink", "cur", "hist" to codes; one key scale and one value scale per head for the whole cache."""
     from . import attention as oatt
     deq = dict(inp)
     deq["q"] = dequantize(q_codes, q_scale)
     for name in ("sink", "cur", "hist"):
         deq[name + "_k"] = dequantize(k_codes[name], k_scale)
+        if v_codes is not None:
+            deq[name + "_v"] = dequantize(v_codes[name], v_scale)
     return oatt.dual_stream(deq, scale=scale if scale is not None else float(inp["scale"]), rows=rows)
+
+
+def p_rounding_sigma(q, keys, values, scale: float, rows=None) -> np.ndarray:
+    """Standard deviation of each output element [n_q, H*d_h] that rounding every probability to e4m3
+    causes, under the model of independent rounding errors uniform over half a spacing: a probability
+    p = exp(s - max) >= 2^-6 (normal) is off by p * u with u uniform in +-2^-4 (std 2^-4 / sqrt(3)); a
+    subnormal one by an absolute error uniform in +-2^-10. Exact float64 probabilities relative to the
+    true maximum are used (the device's running maximum is never above it, so its probabilities are never
+    smaller and this overstates the subnormal part). keys / values [n_k, H, d_h]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(keys, dtype=np.float64)
+    v = np.asarray(values, dtype=np.float64)
+    if rows is not None:
+        q = q[rows]
+    n_q, H, dh = q.shape
+    out = np.zeros((n_q, H * dh))
+    for h in range(H):
+        s = scale * (q[:, h, :] @ k[:, h, :].T)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        err = np.where(p >= 2.0 ** -6, p * 2.0 ** -4, 2.0 ** -10) / np.sqrt(3.0)
+        L = p.sum(axis=1, keepdims=True)
+        out[:, h * dh:(h + 1) * dh] = np.sqrt((err / L) ** 2 @ (v[:, h, :] ** 2))
+    return out
 
 
 def grams_fp8(loc_codes, loc_scale, full_codes, full_scale, head_dim: int) -> Dict[str, np.ndarray]:
