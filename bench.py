@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 (e4m3) MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 
@@ -527,8 +528,9 @@ def future_report(steps, warmup, torch):
 
 
 def fp8_report(steps, warmup, torch):
-    """FP8 attention scores (e4m3 q and keys, per-head scales; bf16 values) against the bf16 kernel on
-    workloads 2 and 5 (dual stream), the quantiser's rate on the keys, and the FP8 statistics of one
+    """FP8 attention scores (e4m3 q and keys, per-head scales; bf16 values) and FP8 attention with the value
+    product in FP8 too (e4m3 values, per-head scales) against the bf16 kernel on workloads 2 and 5 (dual
+    stream), the quantiser's rate on the keys, and the FP8 statistics of one
     4680-row chunk against the bf16 ones at workload 3's and 4's width. Attention FLOP are counted as
     for bf16 (4 n_q n_k d_h per head); statistics FLOP 4 N d^2."""
     import ispa_inputs as inputs
@@ -541,16 +543,21 @@ def fp8_report(steps, warmup, torch):
         H, dh = wl.n_heads, wl.head_dim
         n_q = inp["q"].shape[0]
         keys = torch.cat([dev["sink_k"], dev["cur_k"], dev["hist_k"]], dim=0)
+        vals = torch.cat([dev["sink_v"], dev["cur_v"], dev["hist_v"]], dim=0)
         q_s = torch.empty(H, dtype=torch.float32, device="cuda")
         k_s = torch.empty(H, dtype=torch.float32, device="cuda")
+        v_s = torch.empty(H, dtype=torch.float32, device="cuda")
         ispa.ispa_fp8_head_scales(dev["q"], q_s)
         ispa.ispa_fp8_head_scales(keys, k_s)
+        ispa.ispa_fp8_head_scales(vals, v_s)
         q8 = torch.empty(dev["q"].shape, dtype=torch.uint8, device="cuda")
         ispa.ispa_fp8_quantize(dev["q"], q_s, q8)
-        k8 = {}
+        k8, v8 = {}, {}
         for n in ("sink", "cur", "hist"):
             k8[n] = torch.empty(dev[n + "_k"].shape, dtype=torch.uint8, device="cuda")
             ispa.ispa_fp8_quantize(dev[n + "_k"], k_s, k8[n])
+            v8[n] = torch.empty(dev[n + "_v"].shape, dtype=torch.uint8, device="cuda")
+            ispa.ispa_fp8_quantize(dev[n + "_v"], v_s, v8[n])
         a_loc = torch.empty((n_q, H * dh), dtype=torch.bfloat16, device="cuda")
         a_full = torch.empty_like(a_loc)
         lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
@@ -559,6 +566,9 @@ def fp8_report(steps, warmup, torch):
                                                 dev["hist_k"], dev["hist_v"], wl.scale, a_loc, a_full, *lse),
             "fp8": lambda: ispa.ispa_attn_dual_fp8(q8, q_s, k8["sink"], dev["sink_v"], k8["cur"], dev["cur_v"],
                                                    k8["hist"], dev["hist_v"], k_s, wl.scale, a_loc, a_full, *lse),
+            "fp8_pv": lambda: ispa.ispa_attn_dual_fp8_pv(q8, q_s, k8["sink"], v8["sink"], k8["cur"], v8["cur"],
+                                                         k8["hist"], v8["hist"], k_s, v_s, wl.scale, a_loc, a_full,
+                                                         *lse),
             "quantize_keys": lambda: ispa.ispa_fp8_quantize(keys, k_s, torch.empty(keys.shape, dtype=torch.uint8,
                                                                                    device="cuda")),
         }
@@ -574,6 +584,9 @@ def fp8_report(steps, warmup, torch):
         rows.append({"workload": wl.name, "keys": n_keys, "bf16_ms": round(ms["bf16"], 4),
                      "fp8_ms": round(ms["fp8"], 4), "speedup": round(ms["bf16"] / ms["fp8"], 3),
                      "fp8_tflops_bf16_count": round(fl / ms["fp8"] / 1e9, 1),
+                     "fp8_pv_ms": round(ms["fp8_pv"], 4), "fp8_pv_speedup": round(ms["bf16"] / ms["fp8_pv"], 3),
+                     "fp8_pv_tflops_bf16_count": round(fl / ms["fp8_pv"] / 1e9, 1),
+                     "fp8_pv_frac_fp8_peak": round(fl / ms["fp8_pv"] / 1e9 / PEAK_FP8_TFLOPS, 4),
                      "quantize_keys_ms": round(ms["quantize_keys"], 4),
                      "quantize_gbps": round(qbytes / ms["quantize_keys"] / 1e6, 1)})
     stats = []

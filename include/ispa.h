@@ -176,6 +176,19 @@ ispa_status ispa_kv_merge(ispa_dtype dt, int32_t width, const void *k, const voi
  *                  multiple of 16, < 2^23)
  *   head_dim       128 only (else ISPA_E_UNSUPPORTED)
  * Errors as for ispa_attn_dual.
+ *
+ * ispa_attn_dual_fp8_pv: as ispa_attn_dual_fp8, with the value product in FP8 as well (same W8A8 passage;
+ * the recipe is a reading, the page gives none):
+ *   sink, cur, hist  .k and .v e4m3 bytes, one row stride .row_stride in bytes (multiple of 16, < 2^23)
+ *   v_scale        device fp32 [H]: one scale per head for every value row of the cache (absmax / 448,
+ *                  as ispa_fp8_head_scales gives); values are e4m3_value * v_scale
+ *   Each probability exp(s - m) of the online softmax (m: its running maximum, never below the max by
+ *   more than 8 in log2 units, so p <= 256) is rounded to e4m3 (nearest even) for the value product;
+ *   the exp-sum that normalises the rows and the log-sum-exp outputs use the unrounded probabilities.
+ *   So A_loc and A_full differ from attention on the dequantised values by the probability rounding
+ *   (relative 2^-4 at most per normal probability) besides the bf16 output rounding; LSE rows are those
+ *   of ispa_attn_dual_fp8.
+ * Errors as for ispa_attn_dual (v_scale NULL or misaligned: ISPA_E_ARG).
  * ------------------------------------------------------------------------------------------- */
 ispa_status ispa_fp8_head_scales(ispa_dtype dt, const void *x, int64_t n, int32_t n_heads, int32_t head_dim,
                                  int64_t row_stride, float *scales, void *stream);
@@ -187,6 +200,11 @@ ispa_status ispa_attn_dual_fp8(int32_t n_heads, int32_t head_dim, float softmax_
                                ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
                                const float *k_scale, void *a_loc, void *a_full,
                                float *lse_loc, float *lse_hist, float *lse_full, void *stream);
+ispa_status ispa_attn_dual_fp8_pv(int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                  const uint8_t *q, int64_t n_q, int64_t q_row_stride, const float *q_scale,
+                                  ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                                  const float *k_scale, const float *v_scale, void *a_loc, void *a_full,
+                                  float *lse_loc, float *lse_hist, float *lse_full, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Future-query importance of cached keys (Future Forcing summary page, "Componenti Algorithmiche",

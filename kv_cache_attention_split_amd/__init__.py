@@ -19,6 +19,7 @@ from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVBias, KVSegment, l
 __all__ = [
     "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_future_scores",
     "ispa_future_scores_workspace", "ispa_future_scores_noalloc", "ispa_fp8_head_scales", "ispa_fp8_quantize", "ispa_attn_dual_fp8",
+    "ispa_attn_dual_fp8_pv",
     "ispa_absorb_accumulate", "ispa_absorb_accumulate_batched", "ispa_absorb_accumulate_fp8", "ispa_absorb_accumulate_workspace",
     "ispa_absorb_solve", "ispa_absorb_solve_workspace", "ispa_absorb_solve_eps",
     "ispa_absorb_solve_eps_workspace", "ispa_layer_error",
@@ -191,15 +192,18 @@ def ispa_fp8_quantize(x, scales, out, stream=None) -> None:
     _check(s, "ispa_fp8_quantize")
 
 
-def _seg_fp8(k, v, n_heads: int, head_dim: int) -> KVSegment:
+def _seg_fp8(k, v, n_heads: int, head_dim: int, v_fp8: bool = False) -> KVSegment:
     if k is None or k.shape[0] == 0:
         return KVSegment(None, None, 0, n_heads * head_dim)
     for t in (k, v):
         if t.dim() != 3 or t.shape[1] != n_heads or t.shape[2] != head_dim or t.stride(2) != 1 or \
                 t.stride(1) != head_dim:
             raise ValueError("K/V segment must be [n, H, d_h] with contiguous rows")
+    torch = _torch()
+    if k.dtype != torch.uint8 or v.dtype != (torch.uint8 if v_fp8 else torch.bfloat16):
+        raise ValueError("K must be uint8 e4m3 codes and V " + ("uint8 e4m3 codes" if v_fp8 else "bfloat16"))
     if k.shape[0] != v.shape[0] or k.stride(0) != v.stride(0):
-        raise ValueError("K (e4m3) and V (bf16) of a segment must have the same rows and row stride")
+        raise ValueError("K and V of a segment must have the same rows and row stride")
     return KVSegment(_ptr(k), _ptr(v), int(k.shape[0]), int(k.stride(0)))
 
 
@@ -216,6 +220,22 @@ def ispa_attn_dual_fp8(q, q_scale, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v,
         _ptr(k_scale), _ptr(a_loc), _ptr(a_full), _ptr(lse_loc), _ptr(lse_hist), _ptr(lse_full),
         _stream_handle(stream))
     _check(st, "ispa_attn_dual_fp8")
+
+
+def ispa_attn_dual_fp8_pv(q, q_scale, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v, k_scale, v_scale,
+                          softmax_scale: float, a_loc, a_full=None, lse_loc=None, lse_hist=None, lse_full=None,
+                          stream=None) -> None:
+    """Dual-stream attention with e4m3 q, keys and values (uint8 codes, float32 per-head scales) and the
+    value product in FP8 (see ispa_attn_dual_fp8_pv in include/ispa.h)."""
+    n_q, H, dh = (int(x) for x in q.shape)
+    if q.stride(2) != 1 or q.stride(1) != dh:
+        raise ValueError("q rows must be contiguous over (H, d_h)")
+    st = lib().ispa_attn_dual_fp8_pv(
+        H, dh, ctypes.c_float(softmax_scale), _ptr(q), n_q, int(q.stride(0)), _ptr(q_scale),
+        _seg_fp8(sink_k, sink_v, H, dh, True), _seg_fp8(cur_k, cur_v, H, dh, True),
+        _seg_fp8(hist_k, hist_v, H, dh, True), _ptr(k_scale), _ptr(v_scale), _ptr(a_loc), _ptr(a_full),
+        _ptr(lse_loc), _ptr(lse_hist), _ptr(lse_full), _stream_handle(stream))
+    _check(st, "ispa_attn_dual_fp8_pv")
 
 
 def ispa_future_scores_workspace(n_heads: int, n_p: int) -> int:

@@ -236,10 +236,12 @@ ispa_status ispa_fp8_quantize(ispa_dtype dt, const void *x, int64_t n, int32_t n
                                         out_row_stride, (hipStream_t)stream));
 }
 
-ispa_status ispa_attn_dual_fp8(int32_t n_heads, int32_t head_dim, float softmax_scale, const uint8_t *q, int64_t n_q,
-                               int64_t q_row_stride, const float *q_scale, ispa_kv_segment sink, ispa_kv_segment cur,
-                               ispa_kv_segment hist, const float *k_scale, void *a_loc, void *a_full,
-                               float *lse_loc, float *lse_hist, float *lse_full, void *stream) {
+namespace {
+// FP8 attention: e4m3 q and keys; values bf16 (v_scale NULL) or e4m3 with per-head scales
+ispa_status attn_fp8_impl(int32_t n_heads, int32_t head_dim, float softmax_scale, const uint8_t *q, int64_t n_q,
+                          int64_t q_row_stride, const float *q_scale, ispa_kv_segment sink, ispa_kv_segment cur,
+                          ispa_kv_segment hist, const float *k_scale, const float *v_scale, void *a_loc,
+                          void *a_full, float *lse_loc, float *lse_hist, float *lse_full, void *stream) {
   if (n_heads <= 0 || n_q < 0) return ISPA_E_ARG;
   if (head_dim != 128) return ISPA_E_UNSUPPORTED;
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return ISPA_E_ARG;
@@ -288,7 +290,27 @@ ispa_status ispa_attn_dual_fp8(int32_t n_heads, int32_t head_dim, float softmax_
   a.bias_to_score = 1.0f / softmax_scale;
   a.q_scale = q_scale;
   a.k_scale = k_scale;
+  a.v_scale = v_scale;
   return hip_status(launch_attn_fp8(a, head_dim, (hipStream_t)stream));
+}
+}  // namespace
+
+ispa_status ispa_attn_dual_fp8(int32_t n_heads, int32_t head_dim, float softmax_scale, const uint8_t *q, int64_t n_q,
+                               int64_t q_row_stride, const float *q_scale, ispa_kv_segment sink, ispa_kv_segment cur,
+                               ispa_kv_segment hist, const float *k_scale, void *a_loc, void *a_full,
+                               float *lse_loc, float *lse_hist, float *lse_full, void *stream) {
+  return attn_fp8_impl(n_heads, head_dim, softmax_scale, q, n_q, q_row_stride, q_scale, sink, cur, hist, k_scale,
+                       nullptr, a_loc, a_full, lse_loc, lse_hist, lse_full, stream);
+}
+
+ispa_status ispa_attn_dual_fp8_pv(int32_t n_heads, int32_t head_dim, float softmax_scale, const uint8_t *q,
+                                  int64_t n_q, int64_t q_row_stride, const float *q_scale, ispa_kv_segment sink,
+                                  ispa_kv_segment cur, ispa_kv_segment hist, const float *k_scale,
+                                  const float *v_scale, void *a_loc, void *a_full, float *lse_loc, float *lse_hist,
+                                  float *lse_full, void *stream) {
+  if (v_scale == nullptr || !aligned4(v_scale)) return ISPA_E_ARG;
+  return attn_fp8_impl(n_heads, head_dim, softmax_scale, q, n_q, q_row_stride, q_scale, sink, cur, hist, k_scale,
+                       v_scale, a_loc, a_full, lse_loc, lse_hist, lse_full, stream);
 }
 
 // ------------------------------------------------------------------------------------------------

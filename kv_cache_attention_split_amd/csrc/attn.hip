@@ -80,6 +80,7 @@ __device__ __forceinline__ const float *bias_ptr(const AttnArgs &a, bool hist, i
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef int s32x2 __attribute__((ext_vector_type(2)));
 
 // Stage one K or V tile (BK rows) into LDS with direct global->LDS loads: each wave instruction
 // fills 1 KiB (1024 / (2D) rows); lane l writes LDS position base + 16 l, so it fetches the global
@@ -124,12 +125,13 @@ template <int D>
 __device__ __forceinline__ int k8_off(int r, int byte) {
   return r * D + ((((byte >> 4) ^ ((r >> 1) & 7))) << 4) + (byte & 15);
 }
-template <int D, int BK>
+// The same copy serves e4m3 value tiles (VALUE), with the value tile's own chunk placement (v8_off).
+template <int D, int BK, bool VALUE = false>
 __device__ __forceinline__ void dma_tile_k8(const AttnArgs &a, bool hist, int64_t j0, int head_off, uint8_t *lds_tile,
                                             int w, const int (&rr)[BK * D / 4096], const int (&cc)[BK * D / 4096]) {
   constexpr int NW = BK * D / 4096;
-  const uint8_t *k0 = (const uint8_t *)(hist ? a.hist_k : a.sink_k);
-  const uint8_t *k1 = (const uint8_t *)(hist ? a.hist_k : a.cur_k);
+  const uint8_t *k0 = (const uint8_t *)(VALUE ? (hist ? a.hist_v : a.sink_v) : (hist ? a.hist_k : a.sink_k));
+  const uint8_t *k1 = (const uint8_t *)(VALUE ? (hist ? a.hist_v : a.cur_v) : (hist ? a.hist_k : a.cur_k));
   const int64_t s0 = hist ? a.hist_stride : a.sink_stride, s1 = hist ? a.hist_stride : a.cur_stride;
   const int64_t n = hist ? a.hist_n : a.sink_n + a.cur_n, split = hist ? n : a.sink_n;
 #pragma unroll
@@ -140,6 +142,18 @@ __device__ __forceinline__ void dma_tile_k8(const AttnArgs &a, bool hist, int64_
     const uint8_t *src = (second ? k1 + (j - split) * s1 : k0 + j * s0) + head_off + cc[ii];
     copy_to_lds<16>(src, lds_tile + 1024 * (w + 4 * ii));
   }
+}
+
+// e4m3 value tile (D = 128: 64 keys x 128 B): chunk c of key row r is stored at c ^ v8_swz(r), with
+// v8_swz(r) = 4 * bit3(r) + 2 * bit1(r). A V^T operand read (ds_read_b64_tr_b8) of one half-wave takes
+// the 8 keys 16m + 8a + 4h + 2b + p, (a, b, p) in {0,1}^3 (h fixed per half-wave, see vread8 in the
+// kernel), and two adjacent chunks 2j, 2j+1: the 16 (row, chunk) pairs land in the 16 distinct bank
+// groups 8p + (chunk ^ v8_swz) of a 256-byte LDS line.
+__device__ __forceinline__ int v8_swz(int r) { return (((r >> 3) & 1) << 2) | (((r >> 1) & 1) << 1); }
+template <int D>
+__device__ __forceinline__ int v8_off(int r, int byte) {
+  static_assert(D == 128, "e4m3 value tiles are laid out for 128-byte rows");
+  return r * D + ((((byte >> 4) ^ v8_swz(r))) << 4) + (byte & 15);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -490,11 +504,18 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
 // LSE_ONLY: only the log-sum-exp outputs are wanted (no value copies, no value product, no A rows).
 // FP8: q and the keys are e4m3 bytes (per-head scales): the scores run on v_mfma_f32_32x32x64_f8f6f4,
 // two k-steps of 64 per 32-key block, and a key tile is half the bytes; values stay bf16.
-template <int D, bool BIAS, bool LSE_ONLY = false, bool FP8 = false>
+// FP8V (with FP8): the values are e4m3 bytes too (one scale per head) and the probabilities are rounded
+// to e4m3 for the value product, one 32x32x64 MFMA per 32-column block and tile: P^T's 64 keys are the
+// 32 probabilities each lane holds after the softmax, in register order, and the V^T operand is read
+// with ds_read_b64_tr_b8 in that same key order. The exp-sum keeps the unrounded probabilities; the
+// value scale multiplies the normalised rows.
+template <int D, bool BIAS, bool LSE_ONLY = false, bool FP8 = false, bool FP8V = false>
 __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, int n_qt) {
+  static_assert(FP8 || !FP8V, "the FP8 value product comes with FP8 scores");
   constexpr int BK = 64;
   constexpr int TB = BK * D * 2;
   constexpr int TBK = FP8 ? BK * D : TB;     // bytes of a key tile
+  constexpr int TBV = FP8V ? BK * D : TB;    // bytes of a value tile
   constexpr int NKK = D / 16;
   constexpr int NK8 = D / 64;                // e4m3 k-steps
   constexpr int NDB = D / 32;
@@ -502,7 +523,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   constexpr int NPV = NDB * NB * 2;
 
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][TBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][TBV];
   __shared__ __attribute__((aligned(256))) float bbuf[2][BIAS ? BK : 1];   // bias of tiles, beside K
 
   const int tid = threadIdx.x;
@@ -518,6 +539,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   const int out_stride = a.n_heads * D;
   float sl2 = a.scale_log2;
   if constexpr (FP8) sl2 *= a.q_scale[head] * a.k_scale[head];   // scores of the dequantised values
+  const float v_mul = FP8V ? a.v_scale[head] : 1.0f;              // values of the dequantised codes
 
   bf16x8 qr[FP8 ? 1 : NKK];
   i32x8 qf[FP8 ? NK8 : 1];   // e4m3 q: lane holds dims 64ks + 32hf .. +31
@@ -575,8 +597,20 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     else
       dma_tile<D, BK, false>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, kbuf[buf], wl, drow, dcol8);
   };
+  int v8row[FP8V ? NW8 : 1], v8col[FP8V ? NW8 : 1];
+  if constexpr (FP8V) {
+#pragma unroll
+    for (int ii = 0; ii < NW8; ++ii) {
+      const int r = (wl + 4 * ii) * (1024 / D) + lane / (D / 16);
+      v8row[ii] = r;
+      v8col[ii] = 16 * ((lane % (D / 16)) ^ v8_swz(r));
+    }
+  }
   auto dma_v = [&](int t, int buf) {
-    dma_tile<D, BK, true>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, vbuf[buf], wl, drow, dcol8);
+    if constexpr (FP8V)
+      dma_tile_k8<D, BK, true>(a, t >= nt_loc, tile_j0(t), head_off, vbuf[buf], wl, v8row, v8col);
+    else
+      dma_tile<D, BK, true>(seg_run(a, t >= nt_loc), tile_j0(t), head_off, vbuf[buf], wl, drow, dcol8);
   };
   auto n_valid_of = [&](int t) -> int {
     const int64_t nseg = t >= nt_loc ? a.hist_n : n_loc;
@@ -607,6 +641,27 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
         (__attribute__((address_space(3))) s16x4 *)(vt + kv_off<D>(row + 8, col)));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  // e4m3 V^T operand of 32-column block db for the 64 keys of a tile: byte j of lane (column l32, half
+  // hf) must hold the key whose probability sits in byte j of the P^T operand, i.e. key
+  // 32 (j/16) + 8 ((j mod 16)/4) + 4 hf + j mod 4. Read m (bytes 8m .. 8m+7) therefore takes keys
+  // 16m + 8 (e/4) + 4 hf + e mod 4, e = 0..7: lane s of each 16-lane group addresses key e = s/2 of that
+  // list and bytes 32 db + 16 (g mod 2) + 8 (s mod 2) .. +7, and receives column 32 db + l32 of the 8
+  // keys. The lane's row and swizzle do not depend on m, so the 16 reads of a tile share 4 addresses.
+  int v8addr[FP8V ? NDB : 1];
+  if constexpr (FP8V) {
+    const int e = sl >> 1, hh = g >> 1;
+    const int r0 = 8 * (e >> 2) + 4 * hh + (e & 3);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) v8addr[db] = v8_off<D>(r0, 32 * db + 16 * (g & 1) + 8 * (sl & 1));
+  }
+  auto vread8 = [&](int u, int db) -> i32x8 {
+    const uint8_t *vt = vbuf[u & 1] + v8addr[db];
+    s32x2 r[4];
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm)
+      r[mm] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) s32x2 *)(vt + 16 * D * mm));
+    return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+  };
 
   f32x16 o[NDB];
 #pragma unroll
@@ -615,16 +670,17 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
   float m = -INFINITY, l = 0.f, l_loc = 0.f;
   f32x16 sc[NB];
-  bf16x8 pk[NB][2];
+  bf16x8 pk[FP8V ? 1 : NB][2];
+  i32x8 pf;   // FP8V: the tile's 32 probabilities of this lane as e4m3, in register order
 
   auto snapshot_local = [&]() {
     const float tot = l + swap_halves(l);
     const float inv = 1.0f / tot;
     const float lse = (m + __log2f(tot)) * kLn2;
-    if constexpr (!LSE_ONLY) write_rows<D>(o, inv, a.a_loc, qi, n_q, out_stride, head_off, hf);
+    if constexpr (!LSE_ONLY) write_rows<D>(o, inv * v_mul, a.a_loc, qi, n_q, out_stride, head_off, hf);
     write_lse(a.lse_loc, lse, head, qi, n_q, hf);
     if (nt_hist == 0) {
-      if constexpr (!LSE_ONLY) write_rows<D>(o, inv, a.a_full, qi, n_q, out_stride, head_off, hf);
+      if constexpr (!LSE_ONLY) write_rows<D>(o, inv * v_mul, a.a_full, qi, n_q, out_stride, head_off, hf);
       write_lse(a.lse_full, lse, head, qi, n_q, hf);
       write_lse(a.lse_hist, -INFINITY, head, qi, n_q, hf);
     }
@@ -703,7 +759,21 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
     }
-    if (!LSE_ONLY && i > 0) {
+    if (FP8V && i > 0) {
+      i32x8 vt[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vt[db] = vread8(i - 1, db);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] = mfma_e4m3_32x32x64(vt[db], pf, o[db]);
+      // four transposing reads per operand: two operands ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int g2 = 0; g2 < NDB - 2; ++g2) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    } else if (!LSE_ONLY && i > 0) {
       bf16x8 v0 = vread(i - 1, 0), v1 = vread(i - 1, 1);
 #pragma unroll
       for (int j = 0; j < NPV; ++j) {
@@ -756,6 +826,20 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
       m = need ? mnew : m;
       const float mneg = -m;
       float sum = 0.f;
+      if constexpr (FP8V) {
+        // byte j of pf = probability sc[j / 16][j mod 16] rounded to e4m3 (nearest even; p <= 2^8 < 448)
+#pragma unroll
+        for (int w4 = 0; w4 < 8; ++w4) {
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[w4 / 4][4 * (w4 % 4) + e], sl2, mneg));
+            sum += p[e];
+          }
+          const int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          pf[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+        }
+      } else
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -801,7 +885,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     const float th = l + swap_halves(l);
     const float tl = l_loc + swap_halves(l_loc);
     const float tot = th + tl;
-    write_rows<D>(o, 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
+    write_rows<D>(o, v_mul / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
     write_lse(a.lse_full, (m + __log2f(tot)) * kLn2, head, qi, n_q, hf);
     write_lse(a.lse_hist, th > 0.f ? (m + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
   }
@@ -975,7 +1059,11 @@ hipError_t launch_attn_fp8(const AttnArgs &a, int head_dim, hipStream_t s) {
   const int n_qt = (a.n_q + 255) / 256;
   const int grid = n_qt * a.n_heads;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, false, true>), dim3(grid), dim3(512), 0, s, a, n_qt);
+  if (a.v_scale != nullptr)
+    hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, false, true, true>), dim3(grid), dim3(512), 0, s, a,
+                       n_qt);
+  else
+    hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, false, true>), dim3(grid), dim3(512), 0, s, a, n_qt);
   return hipGetLastError();
 }
 

@@ -32,6 +32,9 @@ struct AttnArgs {
   float bias_to_score;
   // FP8 scores: q and the keys as OCP e4m3 bytes with one scale per head each (device [H])
   const float *q_scale, *k_scale;
+  // FP8 value product (with FP8 scores): the values as e4m3 bytes with one scale per head (device [H]);
+  // NULL = bf16 values
+  const float *v_scale;
   // log-sum-exp-only form: the keys are split into lse_splits ranges per (head, query tile); each writes
   // its (running max in log2 units, exp-sum) to lse_part[(split * n_heads + head) * n_q + query]
   float *lse_part;

@@ -172,6 +172,39 @@ def test_fp8_argument_errors(L):
     assert call(n_q=0) == _abi.ISPA_OK
 
 
+def test_fp8_pv_argument_errors(L):
+    at = L.ispa_attn_dual_fp8_pv
+
+    def call(dh=128, n_q=32, qs=256, sink=None, cur=None, hist=None, sq=FAKE2, sk=FAKE2, sv=FAKE2, a_loc=FAKE):
+        sink = sink if sink is not None else seg()
+        cur = cur if cur is not None else seg()
+        hist = hist if hist is not None else seg()
+        return at(2, dh, ctypes.c_float(0.088), FAKE, n_q, qs, sq, sink, cur, hist, sk, sv, a_loc, FAKE2, None,
+                  None, None, None)
+    assert call(sv=None) == _abi.ISPA_E_ARG                     # the value scales are required
+    assert call(sv=FAKE + 2) == _abi.ISPA_E_ARG
+    assert call(sv=None, n_q=0) == _abi.ISPA_E_ARG              # even when there is nothing to compute
+    assert call(dh=64) == _abi.ISPA_E_UNSUPPORTED
+    assert call(cur=seg(v=MISALIGNED)) == _abi.ISPA_E_ARG
+    assert call(cur=seg(stride=1 << 23)) == _abi.ISPA_E_UNSUPPORTED
+    assert call(sink=seg(n=0), cur=seg(n=0)) == _abi.ISPA_E_ARG
+    assert call(sk=None) == _abi.ISPA_E_ARG
+    assert call(n_q=0) == _abi.ISPA_OK
+
+
+def test_fp8_pv_binding_checks_code_types():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((4, 2, 128), dtype=torch.uint8)
+    s = torch.ones(2)
+    k = torch.zeros((8, 2, 128), dtype=torch.uint8)
+    vb = torch.zeros((8, 2, 128), dtype=torch.bfloat16)
+    out = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="e4m3"):
+        ispa.ispa_attn_dual_fp8_pv(q, s, None, None, k, vb, None, None, s, s, 0.088, out)
+    with pytest.raises(ValueError, match="bfloat16"):
+        ispa.ispa_attn_dual_fp8(q, s, None, None, k, k, None, None, s, 0.088, out)
+
+
 def test_accumulate_fp8_argument_errors(L):
     f = L.ispa_absorb_accumulate_fp8
 

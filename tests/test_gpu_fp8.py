@@ -118,6 +118,168 @@ def test_fp8_wan_shape_sampled_rows():
     _log(f"   {rep}")
 
 
+# ---- FP8 value product (ispa_attn_dual_fp8_pv) ----------------------------------------------------
+# Bound per output element: |device - oracle| <= 6 sigma_P + 2^-8 |oracle| + 1e-6, where sigma_P is the
+# spread that rounding each probability to e4m3 causes (oracle.fp8.p_rounding_sigma: uniform rounding
+# errors of half a spacing, independent over keys), 2^-8 |oracle| covers the bf16 rounding of the stored
+# rows (2^-9) with a factor 2, and 1e-6 the fp32 sums (e4m3 x e4m3 products are exact in fp32). Over a
+# whole output the error's rms stays below 2 ||sigma_P|| + 2^-8 ||oracle|| (the model overstates the
+# spread: exactly representable probabilities are not rounded). A value operand read in the wrong key
+# order or a dropped value scale moves rows by about their own size, far outside both.
+PV_SIGMAS = 6.0
+
+
+def _pv_codes(inp):
+    """Scales and codes from the oracle (host): q, the whole cache's keys and values (one scale per head)."""
+    q_s = ofp.head_scales(inp["q"])
+    keys = np.concatenate([inp["sink_k"], inp["cur_k"], inp["hist_k"]], axis=0)
+    vals = np.concatenate([inp["sink_v"], inp["cur_v"], inp["hist_v"]], axis=0)
+    k_s, v_s = ofp.head_scales(keys), ofp.head_scales(vals)
+    kc = {n: ofp.quantize(inp[n + "_k"], k_s) for n in ("sink", "cur", "hist")}
+    vc = {n: ofp.quantize(inp[n + "_v"], v_s) for n in ("sink", "cur", "hist")}
+    return ofp.quantize(inp["q"], q_s), q_s, kc, k_s, vc, v_s
+
+
+def _run_fp8_pv(inp, codes, want_full=True):
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    qc, qs, kc, ks, vc, vs = codes
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()   # noqa: E731
+    n_q, H, dh = inp["q"].shape
+    out = empty_outputs(n_q, H, dh, "bf16", want_full)
+    ispa.ispa_attn_dual_fp8_pv(up(qc), up(qs), up(kc["sink"]), up(vc["sink"]), up(kc["cur"]), up(vc["cur"]),
+                               up(kc["hist"]), up(vc["hist"]), up(ks), up(vs), float(inp["scale"]),
+                               out["a_loc"], out["a_full"], out["lse_loc"], out["lse_hist"], out["lse_full"])
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_fp8_pv(out, inp, codes, rows=None):
+    """Rows against the oracle on the dequantised codes within the bound above; LSE rows within the
+    attention tolerance. Returns the largest error in units of sigma_P and the rms ratios."""
+    from gpu_helpers import to_host64
+    qc, qs, kc, ks, vc, vs = codes
+    ref = ofp.dual_stream_fp8(inp, qc, qs, kc, ks, rows=rows, v_codes=vc, v_scale=vs)
+    qd = ofp.dequantize(qc, qs)
+    kd = {n: ofp.dequantize(kc[n], ks) for n in kc}
+    vd = {n: ofp.dequantize(vc[n], vs) for n in vc}
+    scale = float(inp["scale"])
+    loc = ("sink", "cur")
+    sig = {"A_loc": ofp.p_rounding_sigma(qd, np.concatenate([kd[n] for n in loc]),
+                                         np.concatenate([vd[n] for n in loc]), scale, rows=rows)}
+    if out["a_full"] is not None:
+        full = ("sink", "cur", "hist")
+        sig["A_full"] = ofp.p_rounding_sigma(qd, np.concatenate([kd[n] for n in full]),
+                                             np.concatenate([vd[n] for n in full]), scale, rows=rows)
+    rep = {}
+    for mine, theirs in (("a_loc", "A_loc"), ("a_full", "A_full")):
+        if out[mine] is None:
+            continue
+        got = to_host64(out[mine])
+        if rows is not None:
+            got = got[rows]
+        want, sg = ref[theirs], sig[theirs]
+        assert np.all(np.isfinite(got)), mine
+        err = np.abs(got - want)
+        excess = err - (PV_SIGMAS * sg + 2.0 ** -8 * np.abs(want) + 1e-6)
+        assert np.all(excess <= 0), (mine, float(excess.max()), float((err / (sg + 1e-30)).max()))
+        rms = np.sqrt(np.mean((got - want) ** 2))
+        limit = 2.0 * np.sqrt(np.mean(sg ** 2)) + 2.0 ** -8 * np.sqrt(np.mean(want ** 2))
+        assert rms <= limit, (mine, rms, limit)
+        rep[mine] = {"max_err_in_sigma": float((err / (sg + 1e-30)).max()),
+                     "rms_err_over_rms_sigma": float(rms / np.sqrt(np.mean(sg ** 2)))}
+    rep["lse"] = check_attention(dict(out, a_loc=None, a_full=None), ref, "bf16", rows=rows)
+    return rep
+
+
+@pytest.mark.parametrize("case", [dict(n_q=300, n_sink=40, n_cur=100, n_hist=333),
+                                  dict(n_q=257, n_sink=0, n_cur=64, n_hist=0),
+                                  dict(n_q=130, n_sink=17, n_cur=75, n_hist=129),
+                                  dict(n_q=1, n_sink=1, n_cur=0, n_hist=1)])
+def test_fp8_pv_attention_vs_oracle(case):
+    _log(f"case: fp8 value product, attention 2 x 128 {case}")
+    inp = inputs.attention_case(80 + case["n_q"], n_heads=2, head_dim=128, **case)
+    codes = _pv_codes(inp)
+    out = _run_fp8_pv(inp, codes)
+    _log(f"   {_check_fp8_pv(out, inp, codes)}")
+
+
+def test_fp8_pv_lse_equals_fp8_scores_kernel():
+    """The value product does not touch the scores: the log-sum-exp rows equal those of
+    ispa_attn_dual_fp8 on the same q and key codes bit for bit (same score arithmetic, same summation
+    order)."""
+    from gpu_helpers import to_host64
+    inp = inputs.attention_case(91, n_heads=3, head_dim=128, n_q=520, n_sink=64, n_cur=333, n_hist=700)
+    _log("case: fp8 value product vs fp8 scores kernel, LSE rows, 3 x 128, 520 queries, 1097 keys")
+    codes = _pv_codes(inp)
+    out = _run_fp8_pv(inp, codes)
+    ref_out, *_ = _run_fp8(inp)
+    for name in ("lse_loc", "lse_hist", "lse_full"):
+        np.testing.assert_array_equal(to_host64(out[name]), to_host64(ref_out[name]))
+
+
+def test_fp8_pv_local_only():
+    inp = inputs.attention_case(72, n_heads=2, head_dim=128, n_q=200, n_sink=32, n_cur=160, n_hist=96)
+    codes = _pv_codes(inp)
+    out = _run_fp8_pv(inp, codes, want_full=False)
+    _check_fp8_pv(out, inp, codes)
+
+
+def test_fp8_pv_wan_shape_sampled_rows():
+    inp = inputs.attention_inputs(2, 0, 0)               # 12 x 128, 4680 queries, 18,720 keys
+    _log("case: fp8 value product on workload 2 (12 x 128, 4680 queries, 18720 keys), sampled rows")
+    codes = _pv_codes(inp)
+    out = _run_fp8_pv(inp, codes)
+    rows = np.sort(np.random.default_rng(3).choice(inp["q"].shape[0], size=48, replace=False))
+    _log(f"   {_check_fp8_pv(out, inp, codes, rows=rows)}")
+
+
+def test_fp8_pv_device_quantiser_chain():
+    """The whole FP8 chain on the device: per-head scales of q, of the cache's keys and of its values
+    (one [n, H, d_h] cache whose sink, current and history segments are views), e4m3 codes, then the
+    attention. Scales and codes equal the oracle's bit for bit; the rows meet the bound above against
+    the oracle on those codes."""
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    inp = inputs.attention_inputs(2, 0, 0)
+    _log("case: fp8 device quantiser chain on workload 2 (12 x 128, 4680 queries, 18720 keys)")
+    names = ("sink", "cur", "hist")
+    n = {nm: inp[nm + "_k"].shape[0] for nm in names}
+    bounds = np.cumsum([0] + [n[nm] for nm in names])
+    n_q, H, dh = inp["q"].shape
+    dev = {}
+    for what in ("k", "v"):
+        cache = np.concatenate([inp[nm + "_" + what] for nm in names], axis=0)
+        x = to_dev(cache.reshape(cache.shape[0], H * dh), "bf16").reshape(cache.shape[0], H, dh)
+        sc = torch.full((H,), float("nan"), dtype=torch.float32, device="cuda")
+        ispa.ispa_fp8_head_scales(x, sc)
+        cd = torch.empty((cache.shape[0], H, dh), dtype=torch.uint8, device="cuda")
+        ispa.ispa_fp8_quantize(x, sc, cd)
+        dev[what] = (sc, cd)
+    qx = to_dev(inp["q"].reshape(n_q, H * dh), "bf16").reshape(n_q, H, dh)
+    qs = torch.full((H,), float("nan"), dtype=torch.float32, device="cuda")
+    ispa.ispa_fp8_head_scales(qx, qs)
+    qc = torch.empty((n_q, H, dh), dtype=torch.uint8, device="cuda")
+    ispa.ispa_fp8_quantize(qx, qs, qc)
+    seg = {what: {nm: dev[what][1][bounds[i]:bounds[i + 1]] for i, nm in enumerate(names)} for what in ("k", "v")}
+    out = empty_outputs(n_q, H, dh, "bf16", True)
+    ispa.ispa_attn_dual_fp8_pv(qc, qs, seg["k"]["sink"], seg["v"]["sink"], seg["k"]["cur"], seg["v"]["cur"],
+                               seg["k"]["hist"], seg["v"]["hist"], dev["k"][0], dev["v"][0], float(inp["scale"]),
+                               out["a_loc"], out["a_full"], out["lse_loc"], out["lse_hist"], out["lse_full"])
+    torch.cuda.synchronize()
+    codes = _pv_codes(inp)
+    q_c, q_s, kc, ks, vc, vs = codes
+    np.testing.assert_array_equal(qs.cpu().numpy(), q_s)
+    np.testing.assert_array_equal(qc.cpu().numpy(), q_c)
+    np.testing.assert_array_equal(dev["k"][0].cpu().numpy(), ks)
+    np.testing.assert_array_equal(dev["v"][0].cpu().numpy(), vs)
+    for i, nm in enumerate(names):
+        np.testing.assert_array_equal(seg["k"][nm].cpu().numpy(), kc[nm])
+        np.testing.assert_array_equal(seg["v"][nm].cpu().numpy(), vc[nm])
+    rows = np.sort(np.random.default_rng(4).choice(n_q, size=32, replace=False))
+    _log(f"   {_check_fp8_pv(out, inp, codes, rows=rows)}")
+
+
 def _grams_fp8_gpu(loc_codes, s_loc, full_codes, s_full, head_dim, with_f=True, chunks=1):
     import kv_cache_attention_split_amd as ispa
     torch = torch_mod()
