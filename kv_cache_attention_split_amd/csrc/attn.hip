@@ -134,6 +134,19 @@ __device__ __forceinline__ void dma_tile_k8(const AttnArgs &a, bool hist, int64_
   const uint8_t *k1 = (const uint8_t *)(VALUE ? (hist ? a.hist_v : a.cur_v) : (hist ? a.hist_k : a.cur_k));
   const int64_t s0 = hist ? a.hist_stride : a.sink_stride, s1 = hist ? a.hist_stride : a.cur_stride;
   const int64_t n = hist ? a.hist_n : a.sink_n + a.cur_n, split = hist ? n : a.sink_n;
+  const int64_t j1 = j0 + BK;
+  const bool in_first = j1 <= split && j1 <= n;
+  const bool in_second = j0 >= split && j1 <= n;
+  if (in_first || in_second) {
+    // whole tile inside one segment: a uniform tile base plus the lane's row and chunk offset, one
+    // 24-bit multiply (rows < 64, byte strides < 2^23)
+    const uint8_t *tb = (in_first ? k0 + j0 * s0 : k1 + (j0 - split) * s1) + head_off;
+    const uint32_t st = (uint32_t)(in_first ? s0 : s1);
+#pragma unroll
+    for (int ii = 0; ii < NW; ++ii)
+      copy_to_lds<16>(tb + (__umul24((uint32_t)rr[ii], st) + (uint32_t)cc[ii]), lds_tile + 1024 * (w + 4 * ii));
+    return;
+  }
 #pragma unroll
   for (int ii = 0; ii < NW; ++ii) {
     int64_t j = j0 + rr[ii];
@@ -326,7 +339,7 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
   // Store A_loc / lse_loc once the local tiles are all in the accumulator; the history then keeps
   // adding to the same state with its exp-sum kept apart.
   auto snapshot_local = [&]() {
-    const float tot = l + swap_halves(l);
+    const float tot = halves_sum(l);
     const float inv = 1.0f / tot;
     const float lse = (m + __log2f(tot)) * kLn2;
     write_rows<D>(o, inv, a.a_loc, qi, n_q, out_stride, head_off, hf);
@@ -371,20 +384,18 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
     }
     const int n_valid = n_valid_of(t);
     if (n_valid < BK) {
+      const int nv = n_valid - 4 * hf;   // key 32b + 8(v/4) + 4hf + v%4 < n_valid
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = 32 * b + 8 * (v >> 2) + 4 * hf + (v & 3);
-          sc[b][v] = key < n_valid ? sc[b][v] : -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v) sc[b][v] = 32 * b + 8 * (v >> 2) + (v & 3) < nv ? sc[b][v] : -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[b][v]);
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = halves_max(mx);
     const float mnew = mx * sl2;
     const bool need = mnew > m + kRescaleThreshold;
     const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
@@ -482,8 +493,8 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
   }
 
   if (nt_hist > 0) {
-    const float th = l + swap_halves(l);
-    const float tl = l_loc + swap_halves(l_loc);
+    const float th = halves_sum(l);
+    const float tl = halves_sum(l_loc);
     const float tot = th + tl;
     write_rows<D>(o, 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
     write_lse(a.lse_full, (m + __log2f(tot)) * kLn2, head, qi, n_q, hf);
@@ -671,10 +682,10 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   float m = -INFINITY, l = 0.f, l_loc = 0.f;
   f32x16 sc[NB];
   bf16x8 pk[FP8V ? 1 : NB][2];
-  i32x8 pf;   // FP8V: the tile's 32 probabilities of this lane as e4m3, in register order
+  i32x8 pf = {};   // FP8V: the tile's 32 probabilities of this lane as e4m3, in register order
 
   auto snapshot_local = [&]() {
-    const float tot = l + swap_halves(l);
+    const float tot = halves_sum(l);
     const float inv = 1.0f / tot;
     const float lse = (m + __log2f(tot)) * kLn2;
     if constexpr (!LSE_ONLY) write_rows<D>(o, inv * v_mul, a.a_loc, qi, n_q, out_stride, head_off, hf);
@@ -697,6 +708,15 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   ISPA_LDS_BARRIER();
   if (grp == 1) ISPA_LDS_BARRIER();
 
+  // e4m3 key operand of block b, k-step ks: row 32b + l32, bytes 64ks + 32hf .. +31 (two chunks)
+  auto kread8 = [&](int buf, int b, int ks) -> i32x8 {
+    const uint8_t *kt = kbuf[buf];
+    const int r = 32 * b + l32;
+    const u32x4 x0 = *(const u32x4 *)(kt + k8_off<D>(r, 64 * ks + 32 * hf));
+    const u32x4 x1 = *(const u32x4 *)(kt + k8_off<D>(r, 64 * ks + 32 * hf + 16));
+    return i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+  };
+
   for (int i = t0; i <= t1; ++i) {
     // ---- matrix phase: scores of tile i, value product of tile i-1 ----
     if (i < t1) {
@@ -718,17 +738,9 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
           for (int v = 0; v < 16; ++v) sc[b][v] = 0.f;
       }
       if constexpr (FP8) {
-        // e4m3 key operand of block b, k-step ks: row 32b + l32, bytes 64ks + 32hf .. +31 (two chunks)
         i32x8 ka[NB * NK8];
 #pragma unroll
-        for (int j = 0; j < NB * NK8; ++j) {
-          const int b = j / NK8, ks = j % NK8;
-          const uint8_t *kt = kbuf[i & 1];
-          const int r = 32 * b + l32;
-          const u32x4 x0 = *(const u32x4 *)(kt + k8_off<D>(r, 64 * ks + 32 * hf));
-          const u32x4 x1 = *(const u32x4 *)(kt + k8_off<D>(r, 64 * ks + 32 * hf + 16));
-          ka[j] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-        }
+        for (int j = 0; j < NB * NK8; ++j) ka[j] = kread8(i & 1, j / NK8, j % NK8);
 #pragma unroll
         for (int j = 0; j < NB * NK8; ++j) sc[j / NK8] = mfma_e4m3_32x32x64(ka[j], qf[j % NK8], sc[j / NK8]);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -806,20 +818,20 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     if (i < t1) {
       const int n_valid = n_valid_of(i);
       if (n_valid < BK) {
+        // key 32b + 8(v/4) + 4hf + v%4 < n_valid, with the lane's part moved to the bound so that the
+        // key offsets stay immediates
+        const int nv = n_valid - 4 * hf;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = 32 * b + 8 * (v >> 2) + 4 * hf + (v & 3);
-            sc[b][v] = key < n_valid ? sc[b][v] : -INFINITY;
-          }
+          for (int v = 0; v < 16; ++v) sc[b][v] = 32 * b + 8 * (v >> 2) + (v & 3) < nv ? sc[b][v] : -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[b][v]);
-      mx = fmaxf(mx, swap_halves(mx));
+      mx = halves_max(mx);
       const float mnew = mx * sl2;
       const bool need = mnew > m + kRescaleThreshold;
       const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
@@ -836,7 +848,8 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
             p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[w4 / 4][4 * (w4 % 4) + e], sl2, mneg));
             sum += p[e];
           }
-          const int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          // both halves of the word are written: the previous tile's word serves as the untouched input
+          const int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf[w4], false);
           pf[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
         }
       } else
@@ -876,14 +889,14 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
 
   if constexpr (LSE_ONLY) {
     // partial state of this key range: running max (log2 units) and exp-sum, merged by lse_merge_kernel
-    const float tot = l + swap_halves(l);
+    const float tot = halves_sum(l);
     if (hf == 0 && qi < n_q) {
       float *dst = a.lse_part + 2 * (((int64_t)split * a.n_heads + head) * n_q + qi);
       *(f32x2 *)dst = f32x2{m, tot};
     }
   } else if (nt_hist > 0) {
-    const float th = l + swap_halves(l);
-    const float tl = l_loc + swap_halves(l_loc);
+    const float th = halves_sum(l);
+    const float tl = halves_sum(l_loc);
     const float tot = th + tl;
     write_rows<D>(o, v_mul / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
     write_lse(a.lse_full, (m + __log2f(tot)) * kLn2, head, qi, n_q, hf);
@@ -1031,10 +1044,13 @@ hipError_t launch_attn_bf16_t(const AttnArgs &a, int head_dim, hipStream_t s) {
   const int n_qt = (a.n_q + 127) / 128;
   const int grid = n_qt * a.n_heads;
   if (grid == 0) return hipSuccess;
-  if (head_dim == 128)
-    hipLaunchKernelGGL((attn_dual_bf16_kernel<128, BIAS>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
-  else
+  if (head_dim == 128) {
+    // only built when the ping-pong kernel is switched off at compile time
+    if constexpr (!ISPA_ATTN_PP)
+      hipLaunchKernelGGL((attn_dual_bf16_kernel<128, BIAS>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
+  } else {
     hipLaunchKernelGGL((attn_dual_bf16_kernel<64, BIAS>), dim3(grid), dim3(kThreads), 0, s, a, n_qt);
+  }
   return hipGetLastError();
 }
 

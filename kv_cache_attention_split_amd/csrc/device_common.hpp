@@ -74,9 +74,27 @@ __device__ __forceinline__ void copy_to_lds(const void *src, void *lds) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
 }
 
-// Lanes l and l^32 exchange a value (the two halves of a wave hold the same MFMA column).
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// Sum and maximum of the values held by lanes l and l^32 (the two halves of a wave hold the same MFMA
+// column), returned in both lanes. v_permlane32_swap_b32 exchanges the upper half of its first operand
+// with the lower half of its second inside the VALU (no LDS round trip); with x in both operands the
+// two registers then hold x of the lower half and x of the upper half in every lane, so the symmetric
+// sum and maximum of the two are the reductions over the lane pair. The instruction is written in an
+// asm statement: this compiler's builtin for it returns the first result in both elements. The s_nop
+// gives the two wait states required between a VALU write of an operand and the swap.
+__device__ __forceinline__ void halves_pair(float x, float &a, float &b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float halves_max(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return fmaxf(a, b);
 }
 
 }  // namespace ispa

@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(kThreads, 1) future_colsum_kernel(ScoreArgs a)
   }
   ISPA_FS_WAIT_VMCNT(0);   // no copy may land in LDS after the workgroup has ended
 
-  const float tot = col + swap_halves(col);
+  const float tot = halves_sum(col);
   const int64_t j = (int64_t)kt * KT + w * 32 + l32;
   if (hf == 0 && j < n_keys) a.scores[(int64_t)head * a.scores_hs + j] = tot / (float)a.n_p;
 }
