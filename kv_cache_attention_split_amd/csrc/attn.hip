@@ -826,57 +826,71 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
 #pragma unroll
           for (int v = 0; v < 16; ++v) sc[b][v] = 32 * b + 8 * (v >> 2) + (v & 3) < nv ? sc[b][v] : -INFINITY;
       }
-      float mx = -INFINITY;
+      // probabilities of the tile against the running maximum m, packed for the value product; returns
+      // the lane's sum of its 32 unrounded probabilities
+      auto probs = [&](float mneg) -> float {
+        float sum = 0.f;
+        if constexpr (FP8V) {
+          // byte j of pf = probability sc[j / 16][j mod 16] rounded to e4m3 (nearest even; p <= 2^8 < 448)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+          for (int w4 = 0; w4 < 8; ++w4) {
+            float p[4];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[b][v]);
-      mx = halves_max(mx);
-      const float mnew = mx * sl2;
-      const bool need = mnew > m + kRescaleThreshold;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
-      m = need ? mnew : m;
-      const float mneg = -m;
-      float sum = 0.f;
-      if constexpr (FP8V) {
-        // byte j of pf = probability sc[j / 16][j mod 16] rounded to e4m3 (nearest even; p <= 2^8 < 448)
-#pragma unroll
-        for (int w4 = 0; w4 < 8; ++w4) {
-          float p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[w4 / 4][4 * (w4 % 4) + e], sl2, mneg));
-            sum += p[e];
+            for (int e = 0; e < 4; ++e) {
+              p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[w4 / 4][4 * (w4 % 4) + e], sl2, mneg));
+              sum += p[e];
+            }
+            // both halves of the word are written: the previous tile's word serves as the untouched input
+            const int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf[w4], false);
+            pf[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
           }
-          // both halves of the word are written: the previous tile's word serves as the untouched input
-          const int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf[w4], false);
-          pf[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-        }
-      } else
+        } else
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          float p[8];
+          for (int h2 = 0; h2 < 2; ++h2) {
+            float p[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][8 * h2 + e], sl2, mneg));
-            sum += p[e];
+            for (int e = 0; e < 8; ++e) {
+              p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][8 * h2 + e], sl2, mneg));
+              sum += p[e];
+            }
+            u32x4 u;
+            u[0] = pack_bf16x2(p[0], p[1]);
+            u[1] = pack_bf16x2(p[2], p[3]);
+            u[2] = pack_bf16x2(p[4], p[5]);
+            u[3] = pack_bf16x2(p[6], p[7]);
+            pk[b][h2] = __builtin_bit_cast(bf16x8, u);
           }
-          u32x4 u;
-          u[0] = pack_bf16x2(p[0], p[1]);
-          u[1] = pack_bf16x2(p[2], p[3]);
-          u[2] = pack_bf16x2(p[4], p[5]);
-          u[3] = pack_bf16x2(p[6], p[7]);
-          pk[b][h2] = __builtin_bit_cast(bf16x8, u);
+        return sum;
+      };
+      // Lazy maximum: m moves only when the tile's row maximum lies more than 8 (log2 units) above it.
+      // A row whose maximum moves has a probability of 2^8 (to within the last bit of exp2) against the
+      // current m, so where every lane's sum of its probabilities is at most 255 no row moves and the
+      // one pass stands (all probabilities <= 255). Otherwise (the first tile, or scores far above m)
+      // the row maxima are formed, m is raised where needed, the accumulator is rescaled and the
+      // probabilities are recomputed: the results are those of forming the maximum on every tile.
+      float sum = probs(-m);
+      if (__ballot(!(sum <= 255.0f)) != 0ull) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[b][v]);
+        mx = halves_max(mx);
+        const float mnew = mx * sl2;
+        const bool need = mnew > m + kRescaleThreshold;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
+        m = need ? mnew : m;
+        sum = probs(-m);
+        if (__ballot(need) != 0ull) {
+          l *= alpha;
+          l_loc *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
         }
-      if (__ballot(need) != 0ull) {
-        l *= alpha;
-        l_loc *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
       }
       l += sum;
     }

@@ -49,6 +49,28 @@ def test_bf16_small_full_compare(case):
     _log(f"  {rep}")
 
 
+def score_jump_case(seed: int):
+    """Keys of a few 64-key tiles scaled up (x2, x3, x4, x6), so that the running maximum of many rows
+    jumps by a few to many log2 units in the middle of the local and the history keys: the softmax
+    raises its reference, rescales the accumulator, or recomputes a tile without raising it."""
+    inp = inputs.attention_case(seed, 2, 128, 260, 16, 200, 400, dtype="bf16")
+    hk = inp["hist_k"].copy()
+    for t, f in ((1, 2.0), (3, 3.0), (5, 6.0)):
+        hk[64 * t:64 * (t + 1)] *= f
+    ck = inp["cur_k"].copy()
+    ck[100:164] *= 4.0
+    inp["hist_k"], inp["cur_k"] = inputs.round_bf16(hk), inputs.round_bf16(ck)
+    return inp
+
+
+def test_bf16_score_jumps_mid_stream():
+    inp = score_jump_case(11)
+    _log("case: bf16 2 x 128, 260 queries, 16/200/400 keys with scaled key tiles (maximum jumps)")
+    _, out = run_attn(inp)
+    rep = check_attention(out, oatt.dual_stream(inp), "bf16")
+    _log(f"  {rep}")
+
+
 def test_fp32_head128_and_ragged():
     inp = inputs.attention_case(7, 2, 128, 150, 33, 40, 97, dtype="f32")
     _log("case: fp32 H=2 dh=128 n_q=150 33/40/97")
