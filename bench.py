@@ -888,7 +888,9 @@ def stats_kernel_name(d, n_layers):
 def extra_attention(step_cfg, torch):
     """Dual-stream attention on the other workloads the metric names, timed after the step (HIP events,
     median of 20 calls after a half-second warm-up each): the 60-frame history (workload 5, dual and
-    local-only) and the 14B shape's last warmup chunk (workload 4 chunk 4, layer 0)."""
+    local-only) and the 14B shape's last warmup chunk (workload 4 chunk 4, layer 0); on both, also the
+    FP8 form with e4m3 q, keys and values (per-head scales computed and codes written on the device
+    before timing; FLOP counted as for bf16, fraction of the FP8 peak)."""
     import ispa_inputs as inputs
     import kv_cache_attention_split_amd as ispa
     out = {}
@@ -911,6 +913,21 @@ def extra_attention(step_cfg, torch):
         if cfg == 5:
             forms["local"] = (n_sc, lambda: ispa.ispa_attn_dual(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"],
                                                                 dev["cur_v"], empty, empty, wl.scale, a_l, None, lse[0]))
+
+        def e4m3(x):
+            sc = torch.empty(H, dtype=torch.float32, device="cuda")
+            ispa.ispa_fp8_head_scales(x, sc)
+            codes = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+            ispa.ispa_fp8_quantize(x, sc, codes)
+            return sc, codes
+        q_s, q8 = e4m3(dev["q"])
+        k_s, k8 = e4m3(torch.cat([dev["sink_k"], dev["cur_k"], dev["hist_k"]]))
+        v_s, v8 = e4m3(torch.cat([dev["sink_v"], dev["cur_v"], dev["hist_v"]]))
+        b = [0, inp["sink_k"].shape[0], n_sc, n_all]
+        seg8 = [(k8[b[i]:b[i + 1]], v8[b[i]:b[i + 1]]) for i in range(3)]
+        forms["fp8_values"] = (n_all, lambda: ispa.ispa_attn_dual_fp8_pv(
+            q8, q_s, seg8[0][0], seg8[0][1], seg8[1][0], seg8[1][1], seg8[2][0], seg8[2][1], k_s, v_s, wl.scale,
+            a_l, a_f, lse[0], lse[1], lse[2]))
         res = {"workload": wl.name, "n_q": n_q, "heads": H}
         for form, (nk, call) in forms.items():
             t0 = time.perf_counter()
@@ -920,9 +937,10 @@ def extra_attention(step_cfg, torch):
             ms = _time_calls(call, 20, 2, torch)
             tf = attn_flops(n_q, nk, H, dh) / ms / 1e9
             res[form] = {"keys": nk, "ms": round(ms, 4), "tflops": round(tf, 1),
-                         "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                         "frac_mfma_peak": round(tf / (PEAK_FP8_TFLOPS if form == "fp8_values" else PEAK_BF16_TFLOPS), 4)}
         if "local" in res:
             res["full_over_local_time"] = round(res["dual"]["ms"] / res["local"]["ms"], 3)
+        res["fp8_values_speedup"] = round(res["dual"]["ms"] / res["fp8_values"]["ms"], 3)
         out[key] = res
         del dev, a_l, a_f, lse
         torch.cuda.empty_cache()

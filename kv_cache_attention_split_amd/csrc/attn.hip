@@ -215,6 +215,9 @@ __device__ __forceinline__ void write_lse(float *out, float val, int head, int q
 #ifndef ISPA_ATTN_WGS
 #define ISPA_ATTN_WGS 2
 #endif
+#ifndef ISPA_ATTN_VCOPY_VEC
+#define ISPA_ATTN_VCOPY_VEC 1   // ping-pong kernel, bf16 values: value copies in the vector phase
+#endif
 
 template <int D, bool BIAS>
 __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel(AttnArgs a, int n_qt) {
@@ -507,10 +510,13 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
 // 4-7 (group B) run the same loop, B one barrier behind A; every iteration has a matrix phase
 // (scores of tile i, value product of tile i-1) and a vector phase (softmax of tile i), separated by
 // workgroup barriers, so on each SIMD one wave's MFMAs run while the other wave's softmax runs.
-// Both groups read the same K/V tiles one phase apart; group A issues the global->LDS copies at the
-// end of its matrix phase, after that phase's LDS reads: the compiler turns every LDS-read wait into
-// a full wait while a global->LDS copy is in flight, which would serialise the operand reads. With
-// no copy in flight the reads run four operands ahead of the MFMAs (scheduling groups below).
+// Both groups read the same K/V tiles one phase apart; group A issues the global->LDS copies after
+// its matrix phase's LDS reads, and (bf16 values) the value copies at the start of its vector phase,
+// which has no LDS access: the compiler turns every LDS-read wait into a full wait while a global->LDS
+// copy is in flight, so no copy may be pending across a phase with LDS reads. A burst of copies
+// stalls the issuing wave for hundreds of cycles; splitting it between the two phases keeps either
+// phase from growing past the other group's phase beside it. In the matrix phase no copy is in flight
+// and the operand reads run four operands ahead of the MFMAs (scheduling groups below).
 // ------------------------------------------------------------------------------------------------
 // LSE_ONLY: only the log-sum-exp outputs are wanted (no value copies, no value product, no A rows).
 // FP8: q and the keys are e4m3 bytes (per-head scales): the scores run on v_mfma_f32_32x32x64_f8f6f4,
@@ -527,6 +533,8 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   constexpr int TB = BK * D * 2;
   constexpr int TBK = FP8 ? BK * D : TB;     // bytes of a key tile
   constexpr int TBV = FP8V ? BK * D : TB;    // bytes of a value tile
+  // where group A issues the value copies: beside the softmax where the matrix phase is the longer one
+  constexpr bool VCOPY_VEC = !LSE_ONLY && !FP8V && ISPA_ATTN_VCOPY_VEC;
   constexpr int NKK = D / 16;
   constexpr int NK8 = D / 64;                // e4m3 k-steps
   constexpr int NDB = D / 32;
@@ -804,15 +812,19 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    // copies issued after this phase's LDS reads (see the kernel comment)
+    // copies after this phase's LDS reads: K(i+1) and the bias of tile i+1 here; V(i) here as well when
+    // the copies go in the matrix phase (VCOPY_VEC false), else at the start of the vector phase, which
+    // has no LDS access (the compiler adds no wait for it) and runs beside group B's matrix phase, which
+    // reads only the other buffers (K(i), V(i-1))
     if (grp == 0) {
       if (i + 1 < t1) {
         dma_k(i + 1, (i + 1) & 1);
         if (BIAS && wl == 0) dma_b(i + 1, (i + 1) & 1);
       }
-      if (!LSE_ONLY && i < t1) dma_v(i, i & 1);
+      if (!VCOPY_VEC && !LSE_ONLY && i < t1) dma_v(i, i & 1);
     }
-    ISPA_LDS_BARRIER();   // copies in flight stay in flight across this barrier
+    ISPA_LDS_BARRIER();
+    if (VCOPY_VEC && grp == 0 && i < t1) dma_v(i, i & 1);
     // ---- vector phase: softmax of tile i ----
     if (!LSE_ONLY && i - 1 == nt_loc - 1) snapshot_local();   // accumulator holds tiles 0 .. nt_loc-1
     if (i < t1) {
