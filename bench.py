@@ -109,8 +109,8 @@ class Layer:
 # rocprofv3 FETCH_SIZE x 1.9997 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
 # attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only
 # while the source is unchanged.
-ATTN_TRAFFIC = {"sha256": "1c913a30b57e0b913a543a7e095ffd519fd715f5bab3cdc9c8e6e90bf20f7096",
-                "bytes_per_launch": 157819171}
+ATTN_TRAFFIC = {"sha256": "c905790295106ca7f72b6719eb42911677374e4d069f1fc88b60ea27ae912d12",
+                "bytes_per_launch": 157863344}
 
 
 def attn_traffic():
