@@ -248,6 +248,7 @@ def _time_calls(call, n, warmup, torch, cold_scratch=None):
 def attn_report(cfg, steps, warmup, torch):
     """Attention on one workload in three forms, warm and cold cache:
     dual   = the dual-stream call (A_loc, A_full, three LSE rows);
+    balanced = the same call with the balanced schedule over the compute units (where it applies);
     local  = local-only call (sink + current keys, A_loc and lse_loc only);
     single = one local-only call over all keys (sink and history joined into one segment), i.e.
              single-pass full attention with no merge and one output; dual / single - 1 is the
@@ -278,6 +279,12 @@ def attn_report(cfg, steps, warmup, torch):
         "single": (n_all, lambda: ispa.ispa_attn_dual(dev["q"], joined_k, joined_v, dev["cur_k"], dev["cur_v"],
                                                       empty, empty, wl.scale, a_loc, None, lse[0])),
     }
+    ws_bytes = ispa.ispa_attn_dual_balanced_workspace(dev["q"], n_sc, n_all - n_sc)
+    if ws_bytes > 0:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        calls["balanced"] = (n_all, lambda: ispa.ispa_attn_dual_balanced(
+            dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"], dev["hist_k"], dev["hist_v"], wl.scale,
+            a_loc, a_full, lse[0], lse[1], lse[2], ws=ws))
     # clocks ramp up over the first tenths of a second of load: run every form for about half a
     # second before timing, then time the forms in interleaved rounds and keep the median round
     t0 = time.perf_counter()

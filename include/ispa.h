@@ -87,6 +87,39 @@ ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, flo
                            void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * ispa_attn_dual with a balanced schedule over the compute units (same passage; the merge of key-range
+ * partial states is the page's log-sum-exp decomposition applied within a branch). When the
+ * (head, 256-query tile) units would leave a tenth or more of the GPU's compute units idle in their
+ * last round (12 heads x 19 query tiles on 256 units), one workgroup per compute unit takes an equal
+ * share of the key tiles of all units; a unit cut between workgroups is computed in key ranges whose
+ * partial online-softmax states (accumulator, running maximum, local and history exp-sums) go to
+ * `ws`, and the workgroup that completes a unit's last range merges the ranges in key order.
+ * Otherwise the call is ispa_attn_dual and `ws` is not touched.
+ *
+ *   arguments, outputs and errors as for ispa_attn_dual, plus
+ *   ws, ws_bytes  device scratch of at least ispa_attn_dual_balanced_workspace(...) bytes, 256-byte
+ *                 aligned (may be NULL when that size is 0); its contents need no clearing and are
+ *                 scratch after the call. Too small or misaligned: ISPA_E_WORKSPACE.
+ * Results are within the attention tolerances of ispa_attn_dual and identical from call to call
+ * (ranges are merged in a fixed order, whichever workgroup finishes last); they are not bitwise
+ * those of ispa_attn_dual, whose single pass adds the same terms in another order. Speed: on MI355X
+ * at 12 heads x 4680 queries x 18,720 keys this schedule takes 0.71 ms against 0.57 ms for
+ * ispa_attn_dual (ranges that start at arbitrary keys of arbitrary heads lose the L2 reuse of the
+ * plain schedule, whose units of one head walk the keys together on one XCD).
+ * ispa_attn_dual_balanced_workspace: bytes for a call with these sizes on the current device (0 when
+ * the plain schedule is used: dt other than ISPA_BF16, head_dim other than 128, or units filling the
+ * compute units); n_local_keys = sink.n + cur.n, n_hist_keys = hist.n (0 for a local-only call).
+ * ------------------------------------------------------------------------------------------- */
+size_t ispa_attn_dual_balanced_workspace(ispa_dtype dt, int32_t n_heads, int32_t head_dim, int64_t n_q,
+                                         int64_t n_local_keys, int64_t n_hist_keys);
+ispa_status ispa_attn_dual_balanced(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                    const void *q, int64_t n_q, int64_t q_row_stride,
+                                    ispa_kv_segment sink, ispa_kv_segment cur, ispa_kv_segment hist,
+                                    void *a_loc, void *a_full,
+                                    float *lse_loc, float *lse_hist, float *lse_full,
+                                    void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Dual-stream attention with a per-key additive logit bias (FAST-AR summary page, section 2 part A
  * "TempCache", Lemma 5.1: a group of m identical keys is replaced by one key whose value is the
  * group's mean value and whose logit is raised by ln m, with no change to the attention output or

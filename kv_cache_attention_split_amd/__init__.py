@@ -17,7 +17,7 @@ from ._abi import (ISPA_BF16, ISPA_F32, ISPA_OK, IspaError, KVBias, KVSegment, l
                    status_string)
 
 __all__ = [
-    "ispa_attn_dual", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_future_scores",
+    "ispa_attn_dual", "ispa_attn_dual_balanced", "ispa_attn_dual_balanced_workspace", "ispa_attn_dual_biased", "ispa_kv_merge", "ispa_future_scores",
     "ispa_future_scores_workspace", "ispa_future_scores_noalloc", "ispa_fp8_head_scales", "ispa_fp8_quantize", "ispa_attn_dual_fp8",
     "ispa_attn_dual_fp8_pv",
     "ispa_absorb_accumulate", "ispa_absorb_accumulate_batched", "ispa_absorb_accumulate_fp8", "ispa_absorb_accumulate_workspace",
@@ -94,6 +94,47 @@ def ispa_attn_dual(q, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v, softmax_scal
         _seg(sink_k, sink_v, H, dh), _seg(cur_k, cur_v, H, dh), _seg(hist_k, hist_v, H, dh),
         _ptr(a_loc), _ptr(a_full), _ptr(lse_loc), _ptr(lse_hist), _ptr(lse_full), _stream_handle(stream))
     _check(st, "ispa_attn_dual")
+
+
+def _seg_len(k) -> int:
+    return 0 if k is None else int(k.shape[0])
+
+
+def ispa_attn_dual_balanced_workspace(q, n_local_keys: int, n_hist_keys: int) -> int:
+    """Scratch bytes for ispa_attn_dual_balanced with queries like `q` ([n_q, H, d_h]) on the current
+    device (0: the plain schedule is used and no scratch is needed)."""
+    n_q, H, dh = (int(x) for x in q.shape)
+    return int(lib().ispa_attn_dual_balanced_workspace(_dtype_code(q), H, dh, n_q, int(n_local_keys),
+                                                       int(n_hist_keys)))
+
+
+def ispa_attn_dual_balanced(q, sink_k, sink_v, cur_k, cur_v, hist_k, hist_v, softmax_scale: float,
+                            a_loc, a_full=None, lse_loc=None, lse_hist=None, lse_full=None, ws=None,
+                            stream=None) -> None:
+    """ispa_attn_dual with the balanced schedule over the compute units (see include/ispa.h). ws: uint8
+    device scratch of ispa_attn_dual_balanced_workspace bytes (allocated for the call if None)."""
+    n_q, H, dh = (int(x) for x in q.shape)
+    if q.stride(2) != 1 or q.stride(1) != dh:
+        raise ValueError("q rows must be contiguous over (H, d_h)")
+    for o in (a_loc, a_full):
+        if o is not None and (tuple(o.shape) != (n_q, H * dh) or not o.is_contiguous() or o.dtype != q.dtype):
+            raise ValueError("outputs must be contiguous [n_q, H*d_h] of q's dtype")
+    torch = _torch()
+    for o in (lse_loc, lse_hist, lse_full):
+        if o is not None and (tuple(o.shape) != (H, n_q) or not o.is_contiguous() or o.dtype != torch.float32):
+            raise ValueError("LSE outputs must be contiguous float32 [H, n_q]")
+    n_hist = _seg_len(hist_k) if a_full is not None else 0
+    need = ispa_attn_dual_balanced_workspace(q, _seg_len(sink_k) + _seg_len(cur_k), n_hist)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if ws is not None and (ws.dtype != torch.uint8 or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous uint8 tensor")
+    st = lib().ispa_attn_dual_balanced(
+        _dtype_code(q), H, dh, ctypes.c_float(softmax_scale), _ptr(q), n_q, int(q.stride(0)),
+        _seg(sink_k, sink_v, H, dh), _seg(cur_k, cur_v, H, dh), _seg(hist_k, hist_v, H, dh),
+        _ptr(a_loc), _ptr(a_full), _ptr(lse_loc), _ptr(lse_hist), _ptr(lse_full), _ptr(ws),
+        0 if ws is None else int(ws.numel()), _stream_handle(stream))
+    _check(st, "ispa_attn_dual_balanced")
 
 
 def _bias_arg(t, n: int, n_heads: int):

@@ -49,6 +49,9 @@ c_int = ctypes.c_int
 SIGNATURES = {
     "ispa_attn_dual": (c_int, [c_int, c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, KVSegment, KVSegment,
                                KVSegment, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "ispa_attn_dual_balanced_workspace": (c_sz, [c_int, c_i32, c_i32, c_i64, c_i64, c_i64]),
+    "ispa_attn_dual_balanced": (c_int, [c_int, c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, KVSegment, KVSegment,
+                                        KVSegment, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "ispa_attn_dual_biased": (c_int, [c_int, c_i32, c_i32, c_f32, c_vp, c_i64, c_i64, KVSegment, KVSegment,
                                       KVSegment, ctypes.POINTER(KVBias), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "ispa_kv_merge": (c_int, [c_int, c_i32, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_i64,

@@ -5,6 +5,7 @@
 #include "ispa_internal.hpp"
 
 #include <algorithm>
+#include <functional>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -114,11 +115,30 @@ ispa_status check_bias(const float *b, int64_t n, int64_t head_stride) {
   return ISPA_OK;
 }
 
+// compute units of the current device (cached per device); 0 if it cannot be read
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+// the balanced schedule's grid for this call (0: the plain launch)
+int balanced_grid(ispa_dtype dt, int32_t head_dim, int32_t n_heads, int64_t n_q, const ispa_kv_segment &sink,
+                  const ispa_kv_segment &cur, const ispa_kv_segment &hist, bool want_full) {
+  if (dt != ISPA_BF16 || head_dim != 128 || n_heads <= 0 || n_q <= 0) return 0;
+  return attn_balanced_grid(n_q, n_heads, sink.n + cur.n, want_full ? hist.n : 0, device_cus());
+}
+
 ispa_status attn_dual_impl(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
                            const void *q, int64_t n_q, int64_t q_row_stride, ispa_kv_segment sink,
                            ispa_kv_segment cur, ispa_kv_segment hist, const ispa_kv_bias *bias,
                            void *a_loc, void *a_full, float *lse_loc, float *lse_hist, float *lse_full,
-                           void *stream) {
+                           void *stream, bool balanced = false, void *ws = nullptr, size_t ws_bytes = 0) {
   if (dt != ISPA_BF16 && dt != ISPA_F32) return ISPA_E_UNSUPPORTED;
   if (n_heads <= 0 || n_q < 0) return ISPA_E_ARG;
   if (head_dim != 64 && head_dim != 128) return ISPA_E_UNSUPPORTED;
@@ -144,7 +164,13 @@ ispa_status attn_dual_impl(ispa_dtype dt, int32_t n_heads, int32_t head_dim, flo
   if (a_loc == nullptr || !aligned16(a_loc)) return ISPA_E_ARG;
   if (a_full != nullptr && !aligned16(a_full)) return ISPA_E_ARG;
 
-  AttnArgs a;
+  int grid = 0;
+  if (balanced) {
+    grid = balanced_grid(dt, head_dim, n_heads, n_q, sink, cur, hist, a_full != nullptr);
+    const size_t need = attn_balanced_ws_bytes(n_q, n_heads, grid);
+    if (need > 0 && (ws == nullptr || ws_bytes < need || ((uintptr_t)ws & 255) != 0)) return ISPA_E_WORKSPACE;
+  }
+  AttnArgs a{};
   a.q = q;
   a.q_stride = q_row_stride;
   a.sink_k = sink.k;
@@ -176,6 +202,7 @@ ispa_status attn_dual_impl(ispa_dtype dt, int32_t n_heads, int32_t head_dim, flo
   a.hist_bhs = bias != nullptr ? bias->hist_head_stride : 0;
   a.bias_to_score = 1.0f / softmax_scale;
   hipStream_t s = (hipStream_t)stream;
+  if (grid > 0) return hip_status(launch_attn_bf16_balanced(a, head_dim, grid, ws, s));
   const hipError_t e = dt == ISPA_BF16 ? launch_attn_bf16(a, head_dim, s) : launch_attn_f32(a, head_dim, s);
   return hip_status(e);
 }
@@ -188,6 +215,25 @@ ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, flo
                            float *lse_loc, float *lse_hist, float *lse_full, void *stream) {
   return attn_dual_impl(dt, n_heads, head_dim, softmax_scale, q, n_q, q_row_stride, sink, cur, hist,
                         nullptr, a_loc, a_full, lse_loc, lse_hist, lse_full, stream);
+}
+
+size_t ispa_attn_dual_balanced_workspace(ispa_dtype dt, int32_t n_heads, int32_t head_dim, int64_t n_q,
+                                         int64_t n_local_keys, int64_t n_hist_keys) {
+  if (n_local_keys < 0 || n_hist_keys < 0) return 0;
+  const ispa_kv_segment none{nullptr, nullptr, 0, 0};
+  const ispa_kv_segment loc{nullptr, nullptr, n_local_keys, 0};
+  const ispa_kv_segment hist{nullptr, nullptr, n_hist_keys, 0};
+  const int grid = balanced_grid(dt, head_dim, n_heads, n_q, none, loc, hist, true);
+  return attn_balanced_ws_bytes(n_q, n_heads, grid);
+}
+
+ispa_status ispa_attn_dual_balanced(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                                    const void *q, int64_t n_q, int64_t q_row_stride, ispa_kv_segment sink,
+                                    ispa_kv_segment cur, ispa_kv_segment hist, void *a_loc, void *a_full,
+                                    float *lse_loc, float *lse_hist, float *lse_full, void *ws, size_t ws_bytes,
+                                    void *stream) {
+  return attn_dual_impl(dt, n_heads, head_dim, softmax_scale, q, n_q, q_row_stride, sink, cur, hist,
+                        nullptr, a_loc, a_full, lse_loc, lse_hist, lse_full, stream, true, ws, ws_bytes);
 }
 
 ispa_status ispa_attn_dual_biased(ispa_dtype dt, int32_t n_heads, int32_t head_dim, float softmax_scale,
@@ -703,78 +749,71 @@ ispa_status solve_impl(int32_t d, int32_t batch, float lambda, const float *cons
       }
     }
 
-    // forward substitution L Y = B, left-looking by block rows (top to bottom):
-    //   Y_k = Linv_k (B_k - L[k, :k] Y[:k]); each update is one wide GEMM with K = k0, so B is
-    //   read and written once per block row instead of once per earlier block
-    for (int k = 0; k < nt; ++k) {
+    // Triangular sweeps, recursive over block rows: a range of block rows is split in two halves; the
+    // first half is solved, its contribution to the second half is one GEMM over the whole half, then
+    // the second half is solved. The same products as a block-row-by-block-row sweep, in fewer and
+    // larger GEMMs (the top split of d = 1536 is 768 x 1536 x 768 per layer). A single block row is
+    // the product with the diagonal block's inverse, in place.
+    auto leaf = [&](int k, bool trans) -> hipError_t {
       const int k0 = k * nb;
-      if (k0 > 0) {
-        GemmBatch b{};
-        GemmShape sh{};
-        sh.M = nb; sh.N = d; sh.K = k0;
-        sh.lda = d; sh.ldb = d; sh.ldc = d;
-        sh.ta = 0; sh.tb = 0;
-        sh.alpha = -1.f; sh.beta = 1.f;
-        for (int i = 0; i < cnt; ++i) {
-          b.A[i] = Lp(i) + (int64_t)k0 * d;     // L[k0 + r][kk], kk < k0
-          b.B[i] = Bp(i);                       // Y[kk][c], kk < k0
-          b.C[i] = Bp(i) + (int64_t)k0 * d;
-        }
-        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      GemmBatch b{};
+      GemmShape sh{};
+      sh.M = nb; sh.N = d; sh.K = nb;
+      sh.lda = nb; sh.ldb = d; sh.ldc = d;
+      sh.ta = trans ? 1 : 0; sh.tb = 0;
+      sh.alpha = 1.f; sh.beta = 0.f;
+      sh.inplace = 1;                        // C = B: each column's nb rows in one workgroup
+      for (int i = 0; i < cnt; ++i) {
+        b.A[i] = Vp(i) + k * linv_blk;
+        b.B[i] = Bp(i) + (int64_t)k0 * d;
+        b.C[i] = Bp(i) + (int64_t)k0 * d;
       }
-      {
-        GemmBatch b{};
-        GemmShape sh{};
-        sh.M = nb; sh.N = d; sh.K = nb;
-        sh.lda = nb; sh.ldb = d; sh.ldc = d;
-        sh.ta = 0; sh.tb = 0;
-        sh.alpha = 1.f; sh.beta = 0.f;
-        sh.inplace = 1;                        // C = B: each column's nb rows in one workgroup
-        for (int i = 0; i < cnt; ++i) {
-          b.A[i] = Vp(i) + k * linv_blk;
-          b.B[i] = Bp(i) + (int64_t)k0 * d;
-          b.C[i] = Bp(i) + (int64_t)k0 * d;
-        }
-        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      return launch_gemm_f32(b, cnt, sh, nullptr, 0, s);
+    };
+    // forward, L Y = B on block rows [k0, k1): Y_hi -= L[hi, lo] Y_lo between the halves
+    std::function<hipError_t(int, int)> fwd = [&](int k0, int k1) -> hipError_t {
+      if (k1 - k0 == 1) return leaf(k0, false);
+      const int km = k0 + (k1 - k0) / 2;
+      hipError_t e = fwd(k0, km);
+      if (e != hipSuccess) return e;
+      GemmBatch b{};
+      GemmShape sh{};
+      sh.M = (k1 - km) * nb; sh.N = d; sh.K = (km - k0) * nb;
+      sh.lda = d; sh.ldb = d; sh.ldc = d;
+      sh.ta = 0; sh.tb = 0;
+      sh.alpha = -1.f; sh.beta = 1.f;
+      for (int i = 0; i < cnt; ++i) {
+        b.A[i] = Lp(i) + (int64_t)(km * nb) * d + k0 * nb;   // L[hi rows][lo columns]
+        b.B[i] = Bp(i) + (int64_t)(k0 * nb) * d;             // Y[lo rows]
+        b.C[i] = Bp(i) + (int64_t)(km * nb) * d;
       }
-    }
+      e = launch_gemm_f32(b, cnt, sh, nullptr, 0, s);
+      return e != hipSuccess ? e : fwd(km, k1);
+    };
+    // back, L^T X = Y on block rows [k0, k1): Y_lo -= L[hi, lo]^T X_hi between the halves
+    std::function<hipError_t(int, int)> back = [&](int k0, int k1) -> hipError_t {
+      if (k1 - k0 == 1) return leaf(k0, true);
+      const int km = k0 + (k1 - k0) / 2;
+      hipError_t e = back(km, k1);
+      if (e != hipSuccess) return e;
+      GemmBatch b{};
+      GemmShape sh{};
+      sh.M = (km - k0) * nb; sh.N = d; sh.K = (k1 - km) * nb;
+      sh.lda = d; sh.ldb = d; sh.ldc = d;
+      sh.ta = 1; sh.tb = 0;
+      sh.alpha = -1.f; sh.beta = 1.f;
+      for (int i = 0; i < cnt; ++i) {
+        b.A[i] = Lp(i) + (int64_t)(km * nb) * d + k0 * nb;   // opA[r][kk] = L[km nb + kk][k0 nb + r]
+        b.B[i] = Bp(i) + (int64_t)(km * nb) * d;             // X[hi rows]
+        b.C[i] = Bp(i) + (int64_t)(k0 * nb) * d;
+      }
+      e = launch_gemm_f32(b, cnt, sh, nullptr, 0, s);
+      return e != hipSuccess ? e : back(k0, km);
+    };
+    ISPA_TRY(fwd(0, nt));
     // ||Y||^2 = <dW, B> at the optimum (B^T (L L^T)^-1 B), before the back sweep overwrites Y
     if (er != nullptr) ISPA_TRY(launch_sumsq_tiles(Bp(0), per_f, d, cnt, term(2, p0), er->stride, s));
-    // back substitution L^T dW = Y, left-looking by block rows (bottom to top):
-    //   X_k = Linv_k^T (Y_k - L[k+1:, k]^T X[k+1:])
-    for (int k = nt - 1; k >= 0; --k) {
-      const int k0 = k * nb;
-      const int rem = d - k0 - nb;
-      if (rem > 0) {
-        GemmBatch b{};
-        GemmShape sh{};
-        sh.M = nb; sh.N = d; sh.K = rem;
-        sh.lda = d; sh.ldb = d; sh.ldc = d;
-        sh.ta = 1; sh.tb = 0;
-        sh.alpha = -1.f; sh.beta = 1.f;
-        for (int i = 0; i < cnt; ++i) {
-          b.A[i] = Lp(i) + (int64_t)(k0 + nb) * d + k0;   // opA[r][kk] = L[k0 + nb + kk][k0 + r]
-          b.B[i] = Bp(i) + (int64_t)(k0 + nb) * d;        // X[k0 + nb + kk][c]
-          b.C[i] = Bp(i) + (int64_t)k0 * d;
-        }
-        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
-      }
-      {
-        GemmBatch b{};
-        GemmShape sh{};
-        sh.M = nb; sh.N = d; sh.K = nb;
-        sh.lda = nb; sh.ldb = d; sh.ldc = d;
-        sh.ta = 1; sh.tb = 0;
-        sh.alpha = 1.f; sh.beta = 0.f;
-        sh.inplace = 1;                        // C = B, as in the forward sweep
-        for (int i = 0; i < cnt; ++i) {
-          b.A[i] = Vp(i) + k * linv_blk;
-          b.B[i] = Bp(i) + (int64_t)k0 * d;
-          b.C[i] = Bp(i) + (int64_t)k0 * d;
-        }
-        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
-      }
-    }
+    ISPA_TRY(back(0, nt));
     if (er != nullptr) {
       // eps = <W, H W> - <dW, B> - lambda ||dW||^2 with H = (F + G) - (X + X^T): H goes to the factor's
       // region (L is no longer needed), then one product W W^T, lower tiles only, reduced against H and

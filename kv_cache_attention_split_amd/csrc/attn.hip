@@ -505,6 +505,117 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
   }
 }
 
+// Balanced schedule (SPLIT form of the ping-pong kernel): a workspace slot per piece of a cut unit.
+// A workgroup's range (shorter than a unit) holds at most three pieces: the end of one unit, cut at the
+// local end when it begins inside the local keys, and the start of the next.
+constexpr int kSplitPieces = 3;
+constexpr size_t kSplitScal = 16 * 512 * 4;                 // floats of one stored accumulator
+constexpr size_t kSplitSlotFloats = kSplitScal + 4 * 512;
+
+// Pieces of unit u (tiles [u nt, (u+1) nt) of the sequence) in the range of workgroup p: `n` pieces
+// [a0[k], a1[k]) (key tiles of the unit) in slots slot[k]. A piece that begins inside the local keys
+// (but not at the unit's start) and runs past their end is cut there.
+struct UnitPieces {
+  int n, a0[2], a1[2], slot[2];
+};
+__device__ __forceinline__ UnitPieces unit_pieces(int64_t u, int p, int G, int64_t total, int nt, int nt_loc) {
+  UnitPieces r;
+  r.n = 0;
+  const int64_t s0 = total * p / G, s1 = total * (p + 1) / G;
+  const int64_t u0 = u * nt, u1 = u0 + nt;
+  const int64_t b0 = s0 > u0 ? s0 : u0, b1 = s1 < u1 ? s1 : u1;
+  if (b0 >= b1) return r;
+  int k = 0;   // pieces of this workgroup before unit u
+  if (s0 < u0) {
+    const int t = (int)(s0 - (s0 / nt) * nt);   // start of the workgroup's first unit piece
+    k = (t > 0 && t < nt_loc && nt > nt_loc) ? 2 : 1;
+  }
+  const int x0 = (int)(b0 - u0), x1 = (int)(b1 - u0);
+  if (x0 > 0 && x0 < nt_loc && x1 > nt_loc) {
+    r.n = 2;
+    r.a0[0] = x0, r.a1[0] = nt_loc, r.slot[0] = kSplitPieces * p + k;
+    r.a0[1] = nt_loc, r.a1[1] = x1, r.slot[1] = kSplitPieces * p + k + 1;
+  } else {
+    r.n = 1;
+    r.a0[0] = x0, r.a1[0] = x1, r.slot[0] = kSplitPieces * p + k;
+  }
+  return r;
+}
+
+// Merge of a cut unit's pieces (the workgroup that finished its last piece; all 512 threads; bf16
+// values, head_dim 128). Pieces are visited in sequence order; each holds its accumulator o and running
+// maximum m (log2 units) with the exp-sum l of its keys, or, for the unit's first piece when it
+// completed the local keys (and wrote A_loc itself), l of its history keys and l_loc of its local keys.
+// A_full and lse_full merge every piece; lse_hist the history pieces; A_loc and lse_loc, when the
+// local keys were cut, the pieces inside them.
+__device__ __forceinline__ void merge_unit(const AttnArgs &a, int vid, int nt, int nt_loc, int nt_hist, int64_t total,
+                                           int n_qt, int tid) {
+  constexpr int D = 128, NDB = 4;
+  const int lane = tid & 63, hf = lane >> 5;
+  const int head = vid / n_qt, qt = vid % n_qt;
+  const int qi = qt * 256 + (tid >> 6) * 32 + (lane & 31);
+  const int head_off = head * D, out_stride = a.n_heads * D, n_q = a.n_q;
+  const int64_t u0 = (int64_t)vid * nt;
+  const int G = gridDim.x;
+  const int first = (int)(((u0 + 1) * G - 1) / total);
+  const int last = (int)(((u0 + nt) * G - 1) / total);
+  // pass 1 (LOCAL = false): every piece -> A_full, lse_full, lse_hist; pass 2 (LOCAL = true, when the
+  // local keys were cut): the pieces inside the local keys -> A_loc, lse_loc
+  auto pass = [&](auto local_c) {
+    constexpr bool LOCAL = decltype(local_c)::value;
+    float mx = -INFINITY;
+    for (int p = first; p <= last; ++p) {
+      const UnitPieces pc = unit_pieces(vid, p, G, total, nt, nt_loc);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (k >= pc.n || (LOCAL && pc.a1[k] > nt_loc)) continue;
+        mx = fmaxf(mx, a.split_ws[(size_t)pc.slot[k] * kSplitSlotFloats + kSplitScal + tid]);
+      }
+    }
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+    float ls = 0.f, lh = 0.f;
+    for (int p = first; p <= last; ++p) {
+      const UnitPieces pc = unit_pieces(vid, p, G, total, nt, nt_loc);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (k >= pc.n || (LOCAL && pc.a1[k] > nt_loc)) continue;
+        const float *sl = a.split_ws + (size_t)pc.slot[k] * kSplitSlotFloats;
+        const float m = sl[kSplitScal + tid], l = sl[kSplitScal + 512 + tid];
+        const float c = __builtin_amdgcn_exp2f(m - mx);
+        ls += (LOCAL ? l : l + sl[kSplitScal + 1024 + tid]) * c;
+        if (!LOCAL && pc.a1[k] > nt_loc) lh += l * c;   // a piece with history keys: l is their sum
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 x = *(const f32x4 *)(sl + 4 * ((db * 4 + g4) * 512 + tid));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[db][4 * g4 + e] += x[e] * c;
+          }
+      }
+    }
+    const float tot = halves_sum(ls);
+    if constexpr (LOCAL) {
+      write_rows<D>(acc, 1.0f / tot, a.a_loc, qi, n_q, out_stride, head_off, hf);
+      write_lse(a.lse_loc, (mx + __log2f(tot)) * kLn2, head, qi, n_q, hf);
+    } else {
+      write_rows<D>(acc, 1.0f / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
+      write_lse(a.lse_full, (mx + __log2f(tot)) * kLn2, head, qi, n_q, hf);
+      const float th = halves_sum(lh);
+      write_lse(a.lse_hist, nt_hist > 0 && th > 0.f ? (mx + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
+    }
+  };
+  pass(std::integral_constant<bool, false>{});
+  // the local keys were cut when the unit's first piece ended inside them
+  const UnitPieces p0 = unit_pieces(vid, first, G, total, nt, nt_loc);
+  if (p0.a1[0] < nt_loc) pass(std::integral_constant<bool, true>{});
+  if (tid == 0) a.split_count[vid] = 0;   // ready for the next call
+}
+
 // ------------------------------------------------------------------------------------------------
 // Ping-pong kernel: 8 waves (two per SIMD), 256 queries per workgroup. Waves 0-3 (group A) and
 // 4-7 (group B) run the same loop, B one barrier behind A; every iteration has a matrix phase
@@ -526,9 +637,10 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
 // 32 probabilities each lane holds after the softmax, in register order, and the V^T operand is read
 // with ds_read_b64_tr_b8 in that same key order. The exp-sum keeps the unrounded probabilities; the
 // value scale multiplies the normalised rows.
-template <int D, bool BIAS, bool LSE_ONLY = false, bool FP8 = false, bool FP8V = false>
+template <int D, bool BIAS, bool LSE_ONLY = false, bool FP8 = false, bool FP8V = false, bool SPLIT = false>
 __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, int n_qt) {
   static_assert(FP8 || !FP8V, "the FP8 value product comes with FP8 scores");
+  static_assert(!(SPLIT && LSE_ONLY), "the LSE-only form has its own key split");
   constexpr int BK = 64;
   constexpr int TB = BK * D * 2;
   constexpr int TBK = FP8 ? BK * D : TB;     // bytes of a key tile
@@ -544,18 +656,55 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][TBK];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][TBV];
   __shared__ __attribute__((aligned(256))) float bbuf[2][BIAS ? BK : 1];   // bias of tiles, beside K
+  __shared__ int s_merge;   // SPLIT: this workgroup finished a unit's last segment and merges it
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int grp = w >> 2, wl = w & 3;
-  const int nsplit = LSE_ONLY ? a.lse_splits : 1;   // key ranges per (head, query tile)
-  const int lin = xcd_remap(blockIdx.x, n_qt * a.n_heads * nsplit);
-  const int vid = lin / nsplit, split = lin % nsplit;
+  const int n_q = a.n_q;
+  const int out_stride = a.n_heads * D;
+  const int64_t n_loc = a.sink_n + a.cur_n;
+  const int nt_loc = (int)((n_loc + BK - 1) / BK);
+  const int nt_hist = (int)((a.hist_n + BK - 1) / BK);
+  const int nt = nt_loc + nt_hist;            // key tiles of every (head, query tile) unit
+  const int nsplit = LSE_ONLY ? a.lse_splits : 1;   // key ranges per unit in the LSE-only form
+
+  // SPLIT (balanced schedule): the units' tiles form one sequence, unit after unit; workgroup `pos`
+  // takes the contiguous range [total pos / G, total (pos+1) / G) of it, so every workgroup has the
+  // same number of tiles. A unit cut by a range boundary is processed in segments; each writes its
+  // partial online-softmax state to a workspace slot, and the workgroup that finishes a unit's last
+  // segment merges the unit's segments in sequence order (the log-sum-exp decomposition of the
+  // softmax) and writes its rows. Otherwise one pass: the workgroup's own unit (and key range).
+  const int64_t total = (int64_t)n_qt * a.n_heads * nt;
+  const int pos = SPLIT ? xcd_remap(blockIdx.x, gridDim.x) : 0;
+  int64_t seg_pos = SPLIT ? total * pos / gridDim.x : 0;
+  const int64_t seg_end = SPLIT ? total * (pos + 1) / gridDim.x : 1;
+  int pending0 = -1, pending1 = -1;   // SPLIT: units whose last piece this workgroup completed
+  int n_pieces = 0;
+  while (seg_pos < seg_end) {
+  int vid, split = 0, t0, t1;
+  if constexpr (SPLIT) {
+    vid = (int)(seg_pos / nt);
+    t0 = (int)(seg_pos - (int64_t)vid * nt);
+    const int64_t e = seg_end - (int64_t)vid * nt;
+    t1 = (int)(e < nt ? e : nt);
+    // a piece that begins inside the local keys (not at the start) ends at the local end
+    if (t0 > 0 && t0 < nt_loc && t1 > nt_loc) t1 = nt_loc;
+  } else {
+    const int lin = xcd_remap(blockIdx.x, n_qt * a.n_heads * nsplit);
+    vid = lin / nsplit;
+    split = lin % nsplit;
+    // tiles of this workgroup: all of them, or one contiguous range per split in the LSE-only form
+    t0 = LSE_ONLY ? (int)((int64_t)split * nt / nsplit) : 0;
+    t1 = LSE_ONLY ? (int)((int64_t)(split + 1) * nt / nsplit) : nt;
+  }
+  // workspace slot of this piece: the workgroup's slots in piece order
+  const int slot = kSplitPieces * pos + (n_pieces < kSplitPieces ? n_pieces : kSplitPieces - 1);
+  ++n_pieces;
+  seg_pos = SPLIT ? (int64_t)vid * nt + t1 : seg_end;
   const int head = vid / n_qt, qt = vid % n_qt;
   const int head_off = head * D;
   const int qi = qt * 256 + w * 32 + l32;
-  const int n_q = a.n_q;
-  const int out_stride = a.n_heads * D;
   float sl2 = a.scale_log2;
   if constexpr (FP8) sl2 *= a.q_scale[head] * a.k_scale[head];   // scores of the dequantised values
   const float v_mul = FP8V ? a.v_scale[head] : 1.0f;              // values of the dequantised codes
@@ -582,13 +731,6 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     }
   }
 
-  const int64_t n_loc = a.sink_n + a.cur_n;
-  const int nt_loc = (int)((n_loc + BK - 1) / BK);
-  const int nt_hist = (int)((a.hist_n + BK - 1) / BK);
-  const int nt = nt_loc + nt_hist;
-  // tiles of this workgroup: all of them, or one contiguous range per split in the LSE-only form
-  const int t0 = LSE_ONLY ? (int)((int64_t)split * nt / nsplit) : 0;
-  const int t1 = LSE_ONLY ? (int)((int64_t)(split + 1) * nt / nsplit) : nt;
 
   constexpr int NW = BK * D * 2 / 4096;   // copy instructions per group-A wave per tile
   int drow[NW], dcol8[NW];
@@ -692,6 +834,17 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   bf16x8 pk[FP8V ? 1 : NB][2];
   i32x8 pf = {};   // FP8V: the tile's 32 probabilities of this lane as e4m3, in register order
 
+  // SPLIT workspace slot: the state (o as 16 float4 per thread, thread-minor) at 0 and per-thread
+  // scalars at kSplitScal + k * 512 (k: 0 m, 1 l, 2 l_loc)
+  float *const slot_ws = SPLIT ? a.split_ws + (size_t)slot * kSplitSlotFloats : nullptr;
+  auto store_state = [&](float *dst) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(f32x4 *)(dst + 4 * ((db * 4 + g4) * 512 + tid)) =
+            f32x4{o[db][4 * g4], o[db][4 * g4 + 1], o[db][4 * g4 + 2], o[db][4 * g4 + 3]};
+  };
   auto snapshot_local = [&]() {
     const float tot = halves_sum(l);
     const float inv = 1.0f / tot;
@@ -710,7 +863,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   // prologue: K(t0) for everyone; group B then falls one barrier behind
   if (grp == 0) {
     if (!LSE_ONLY || t0 < t1) dma_k(t0, t0 & 1);
-    if (BIAS && wl == 0) dma_b(0, 0);
+    if (BIAS && wl == 0) dma_b(t0, t0 & 1);
     ISPA_WAIT_VMCNT(0);
   }
   ISPA_LDS_BARRIER();
@@ -779,7 +932,8 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
     }
-    if (FP8V && i > 0) {
+    // the value product of tile i-1 belongs to this range only when i-1 >= t0
+    if (FP8V && i > t0) {
       i32x8 vt[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) vt[db] = vread8(i - 1, db);
@@ -793,7 +947,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    } else if (!LSE_ONLY && i > 0) {
+    } else if (!LSE_ONLY && i > t0) {
       bf16x8 v0 = vread(i - 1, 0), v1 = vread(i - 1, 1);
 #pragma unroll
       for (int j = 0; j < NPV; ++j) {
@@ -826,7 +980,9 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     ISPA_LDS_BARRIER();
     if (VCOPY_VEC && grp == 0 && i < t1) dma_v(i, i & 1);
     // ---- vector phase: softmax of tile i ----
-    if (!LSE_ONLY && i - 1 == nt_loc - 1) snapshot_local();   // accumulator holds tiles 0 .. nt_loc-1
+    // accumulator holds tiles 0 .. nt_loc-1: the local keys end here (a piece that begins later inside
+    // the local keys ends at their end, and its state is merged)
+    if (!LSE_ONLY && i == nt_loc && t0 == 0) snapshot_local();
     if (i < t1) {
       const int n_valid = n_valid_of(i);
       if (n_valid < BK) {
@@ -920,13 +1076,45 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
       float *dst = a.lse_part + 2 * (((int64_t)split * a.n_heads + head) * n_q + qi);
       *(f32x2 *)dst = f32x2{m, tot};
     }
-  } else if (nt_hist > 0) {
-    const float th = halves_sum(l);
-    const float tl = halves_sum(l_loc);
-    const float tot = th + tl;
-    write_rows<D>(o, v_mul / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
-    write_lse(a.lse_full, (m + __log2f(tot)) * kLn2, head, qi, n_q, hf);
-    write_lse(a.lse_hist, th > 0.f ? (m + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
+  } else if (!SPLIT || (t0 == 0 && t1 == nt)) {
+    if (nt_hist > 0) {
+      const float th = halves_sum(l);
+      const float tl = halves_sum(l_loc);
+      const float tot = th + tl;
+      write_rows<D>(o, v_mul / tot, a.a_full, qi, n_q, out_stride, head_off, hf);
+      write_lse(a.lse_full, (m + __log2f(tot)) * kLn2, head, qi, n_q, hf);
+      write_lse(a.lse_hist, th > 0.f ? (m + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
+    }
+  } else {
+    // a cut unit: store this piece's state, count it, and merge if it was the unit's last
+    store_state(slot_ws);
+    slot_ws[kSplitScal + tid] = m;
+    slot_ws[kSplitScal + 512 + tid] = l;
+    slot_ws[kSplitScal + 2 * 512 + tid] = l_loc;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const int64_t u0 = (int64_t)vid * nt;
+      const int first = (int)(((u0 + 1) * gridDim.x - 1) / total);
+      const int last = (int)(((u0 + nt) * gridDim.x - 1) / total);
+      int npc = 0;
+      for (int p = first; p <= last; ++p) npc += unit_pieces(vid, p, gridDim.x, total, nt, nt_loc).n;
+      const int done = atomicAdd(a.split_count + vid, 1);
+      s_merge = done == npc - 1;
+    }
+    __syncthreads();
+    if (s_merge) {
+      if (pending0 < 0) pending0 = vid;
+      else pending1 = vid;
+    }
+  }
+  }   // segments
+  if constexpr (SPLIT) {
+    if (pending0 >= 0) {
+      __threadfence();
+      merge_unit(a, pending0, nt, nt_loc, nt_hist, total, n_qt, tid);
+    }
+    if (pending1 >= 0) merge_unit(a, pending1, nt, nt_loc, nt_hist, total, n_qt, tid);
   }
 }
 
@@ -1106,6 +1294,46 @@ hipError_t launch_attn_fp8(const AttnArgs &a, int head_dim, hipStream_t s) {
                        n_qt);
   else
     hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, false, true>), dim3(grid), dim3(512), 0, s, a, n_qt);
+  return hipGetLastError();
+}
+
+// Balanced schedule: one workgroup per compute unit over the tile sequence of all units, when the
+// units alone would leave a tenth or more of the compute units idle in their last round.
+int attn_balanced_grid(int64_t n_q, int n_heads, int64_t n_keys_loc, int64_t n_keys_hist, int cus) {
+  const int64_t units = ((n_q + 255) / 256) * (int64_t)n_heads;
+  const int64_t nt = (n_keys_loc + 63) / 64 + (n_keys_hist + 63) / 64;
+  if (units <= 0 || cus <= 0 || nt < 2) return 0;
+  // one round only (a workgroup's range is then shorter than a unit: at most three pieces), and at
+  // least four tiles per workgroup
+  if (units >= cus || units * 10 >= (int64_t)cus * 9 || units * nt < 4 * (int64_t)cus) return 0;
+  return cus;
+}
+
+size_t attn_balanced_ws_bytes(int64_t n_q, int n_heads, int grid) {
+  if (grid <= 0) return 0;
+  const int64_t units = ((n_q + 255) / 256) * (int64_t)n_heads;
+  const size_t slots = (size_t)kSplitPieces * grid * kSplitSlotFloats * sizeof(float);
+  return slots + (((size_t)units * sizeof(int) + 255) / 256) * 256;
+}
+
+namespace {
+__global__ void __launch_bounds__(256) zero_counts_kernel(int *c, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) c[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_attn_bf16_balanced(const AttnArgs &a, int head_dim, int grid, void *ws, hipStream_t s) {
+  if (head_dim != 128 || has_bias(a) || grid <= 0 || ws == nullptr) return hipErrorInvalidValue;
+  const int n_qt = (a.n_q + 255) / 256;
+  const int64_t units = (int64_t)n_qt * a.n_heads;
+  if (units == 0) return hipSuccess;
+  AttnArgs b = a;
+  b.split_ws = (float *)ws;
+  b.split_count = (int *)((char *)ws + (size_t)kSplitPieces * grid * kSplitSlotFloats * sizeof(float));
+  hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, b.split_count, units);
+  hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, false, false, false, true>), dim3(grid), dim3(512), 0, s,
+                     b, n_qt);
   return hipGetLastError();
 }
 

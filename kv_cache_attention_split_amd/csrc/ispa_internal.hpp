@@ -39,9 +39,19 @@ struct AttnArgs {
   // its (running max in log2 units, exp-sum) to lse_part[(split * n_heads + head) * n_q + query]
   float *lse_part;
   int lse_splits;
+  // balanced schedule (launch_attn_bf16_balanced): per-segment state slots and per-unit counters
+  float *split_ws;
+  int *split_count;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs &a, int head_dim, hipStream_t s);
+// Balanced schedule of the bf16 head_dim-128 kernel (no bias): `grid` workgroups share the tiles of
+// all (head, query tile) units equally; cut units merge their segments' partial states through `ws`
+// (attn_balanced_ws_bytes bytes, 256-byte aligned). attn_balanced_grid gives 0 where the plain launch
+// already fills the compute units (then no workspace is needed).
+int attn_balanced_grid(int64_t n_q, int n_heads, int64_t n_keys_loc, int64_t n_keys_hist, int cus);
+size_t attn_balanced_ws_bytes(int64_t n_q, int n_heads, int grid);
+hipError_t launch_attn_bf16_balanced(const AttnArgs &a, int head_dim, int grid, void *ws, hipStream_t s);
 // Log-sum-exp rows only (a.a_loc and a.a_full must be NULL, no bias): no value copies or products.
 // For head_dim 128 the keys are split over lse_splits_for(n_q, n_heads) workgroups per query tile and
 // a.lse_part must hold that many [n_heads, n_q] float2 partial states; a.lse_full receives the merge.

@@ -214,169 +214,205 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
 // Diagonal block: Cholesky factor and its inverse (one workgroup per layer).
 // ------------------------------------------------------------------------------------------------
 
-// Register-blocked: a 16 x 16 grid of threads, thread (ty, tx) owning the R x R sub-block at rows
-// ty*R.., columns tx*R.. (R = nb / 16). Each elimination step publishes one column (factorisation)
-// or one row (inverse) through LDS, then every thread updates its own sub-block in registers: one
-// barrier per step and no dependent LDS chains.
+// Orders a wave's own LDS writes before its later LDS reads (a wave's LDS operations complete in
+// order; the fences keep the compiler from moving accesses across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 32 x 32 blocks of LDS arrays with row stride SS, in the layout of the 32x32 fp32 MFMA: register v of
+// lane (l32, hf) is row 8 (v / 4) + 4 hf + v % 4, column l32.
+template <int SS>
+__device__ __forceinline__ f32x16 blk_load(const float *C, int l32, int hf) {
+  f32x16 v;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = C[(8 * (r >> 2) + 4 * hf + (r & 3)) * SS + l32];
+  return v;
+}
+template <int SS>
+__device__ __forceinline__ void blk_store(float *C, const f32x16 &v, int l32, int hf) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) C[(8 * (r >> 2) + 4 * hf + (r & 3)) * SS + l32] = v[r];
+}
+// acc += sgn A op(B), op(B) = B^T when TB; k = 16 hf + s in MFMA s. With an odd stride SS both a row
+// (A, B^T) and a column (B) of a block are conflict-free reads.
+template <int SS, bool TB>
+__device__ __forceinline__ void blk_mma(f32x16 &acc, const float *A, const float *B, float sgn, int l32, int hf) {
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int k = 16 * hf + s;
+    const float a = sgn * A[l32 * SS + k];
+    const float b = TB ? B[l32 * SS + k] : B[k * SS + l32];
+    acc = mfma_f32_32x32x2(a, b, acc);
+  }
+}
+
+// One wave factors a 32 x 32 diagonal block in registers (lane (c, h) holds rows 16 h .. 16 h + 15 of
+// column c) and forms the inverse of its factor in the same sweep. Step j: the owners of column j
+// publish it through LDS (the only cross-lane exchange that needs memory), every lane applies
+// A[r][c] -= A[r][j] A[c][j] / A[j][j] (r, c > j) and, for the inverse of the unit-lower factor U
+// (U[r][j] = A[r][j] / A[j][j]), Y[r][c] -= U[r][j] Y[j][c] (r > j), Y[j][c] coming from the lane of
+// the other half with a half swap. At the end L = U D^1/2 and L^-1 = D^-1/2 Y are written to the
+// blocks Sb and Xb (row stride SS, zeros above the diagonal). Returns 1 + the first non-positive pivot
+// (0 if none); such a pivot is replaced by 1 to keep the rest finite.
+template <int SS>
+__device__ __forceinline__ int leaf_factor(float *Sb, float *Xb, float *colbuf, int l32_in, int hf_in) {
+  // lane coordinates made opaque here, so that the per-step lane masks are formed inside the sweep
+  // instead of being hoisted out of the caller's loop (hundreds of live 64-bit masks)
+  int c = l32_in, h = hf_in;
+  asm volatile("" : "+v"(c));
+  asm volatile("" : "+v"(h));
+  const bool up = h != 0;
+  float a[16], y[16], pr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    a[i] = Sb[(16 * h + i) * SS + c];
+    y[i] = (16 * h + i == c) ? 1.f : 0.f;
+    pr[i] = 1.f;
+  }
+  float pc = 1.f;
+  int lbad = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    float *cb = colbuf + 32 * (j & 1);   // two buffers: step j's reads and step j+1's writes never share one
+    if (c == j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *(f32x4 *)&cb[16 * h + 4 * q] = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+    }
+    wave_lds_sync();
+    f32x4 v4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v4[q] = *(const f32x4 *)&cb[16 * h + 4 * q];
+    float p = cb[j];
+    const float vc = cb[c];
+    if (!(p > 0.f)) {
+      lbad = lbad ? lbad : j + 1;
+      p = 1.f;
+    }
+    const float ip = 1.f / p;
+    const float ca = (c > j) ? vc * ip : 0.f;    // A[c][j] / A[j][j] for the columns still to come
+    float ylo, yhi;
+    halves_pair(y[j & 15], ylo, yhi);
+    const float cy = ((j < 16) ? ylo : yhi) * ip; // Y[j][c] / A[j][j]
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // A[r][j] for the rows below the pivot (r = 16 h + i > j), zero above
+      const float x = v4[i >> 2][i & 3];
+      const float v = (i > j) ? x : ((16 + i > j) ? (up ? x : 0.f) : 0.f);
+      a[i] = fmaf(-v, ca, a[i]);
+      y[i] = fmaf(-v, cy, y[i]);
+    }
+    if (c == j) pc = p;
+    if (j < 16) pr[j & 15] = up ? pr[j & 15] : p;
+    else pr[j & 15] = up ? p : pr[j & 15];
+  }
+  const float sc = sqrtf(pc);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 16 * h + i;
+    Sb[r * SS + c] = r > c ? a[i] / sc : (r == c ? sc : 0.f);
+    Xb[r * SS + c] = y[i] * (1.f / sqrtf(pr[i]));
+  }
+  return lbad;
+}
+
+// Blocked over 32 x 32 leaves with the block and its inverse in LDS (row stride NB + 1). Per leaf
+// column jb: wave 0 factors the leaf (after applying the previous column's update to it) while the
+// other waves apply the previous column's update to the rest of the trailing blocks and form the
+// previous row of L^-1 (X_ij = -L_ii^-1 sum_{k=j..i-1} L_ik X_kj); then the panel L_ij = A_ij L_jj^-T.
+// Every product is 32 x 32 x 32 on the fp32 MFMA. Nine workgroup barriers for nb = 128.
 template <int NB>
 __global__ void __launch_bounds__(kThreads) potrf_diag_kernel(float *Lbase, int64_t L_stride, int d,
                                                               int k0, float *Linv_base,
                                                               int64_t Linv_stride, int32_t *info) {
-  constexpr int R = NB / 16;
+  constexpr int NL = NB / 32;
+  constexpr int SS = NB + 1;
   extern __shared__ float smem[];
-  float *colst = smem;              // [NB][NB]: column j of the updated block at step j (col-major)
-  float *rowst = smem + NB * NB;    // [NB][NB]: row j of U^-1 at step j
+  float *S = smem;               // [NB][SS]: the block, then L in place (lower blocks)
+  float *X = smem + NB * SS;     // [NB][SS]: L^-1 (lower blocks); upper blocks (0, 1 + t) hold products
+  __shared__ __attribute__((aligned(16))) float colbuf[64];
   __shared__ int bad;
   const int layer = blockIdx.x;
   float *L = Lbase + layer * L_stride;
   float *Linv = Linv_base + layer * Linv_stride;
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  const int r0 = ty * R, c0 = tx * R;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   if (tid == 0) bad = 0;
-  float a[R][R];
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-#pragma unroll
-    for (int k = 0; k < R; ++k) a[i][k] = L[(int64_t)(k0 + r0 + i) * d + k0 + c0 + k];
-
-  // R consecutive floats of LDS (R-aligned) as vector reads
-  auto lds_row = [&](const float *p, float (&v)[R]) {
-#pragma unroll
-    for (int q = 0; q < R / 4; ++q) {
-      const f32x4 x = ((const f32x4 *)p)[q];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
-    }
-  };
-  auto lds_store_row = [&](float *p, const float (&v)[R]) {
-#pragma unroll
-    for (int q = 0; q < R / 4; ++q) {
-      f32x4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = v[4 * q + e];
-      ((f32x4 *)p)[q] = x;
-    }
-  };
-
-  // factorisation: at step j every thread applies A[r][c] -= A[r][j] A[c][j] / A[j][j] to its
-  // sub-block (entries of rows / columns <= j get a zero factor, so they stay unchanged; the upper
-  // triangle is updated too, harmlessly, since only the lower is read). Look-ahead: the owners of
-  // column j+1 update that column first and publish it to LDS before the rest of the update, so
-  // that the LDS write is in flight while the other FMAs run and one barrier per step suffices
-  // (each column has its own LDS row). The step loop is unrolled by R so that column j is the
-  // fixed register j mod R of its owners.
-  if (tx == 0) {
-    float col[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) col[i] = a[i][0];
-    lds_store_row(&colst[r0], col);
-  }
-  for (int jb = 0; jb < NB; jb += R)
-#pragma unroll
-  for (int kk = 0; kk < R; ++kk) {
-    const int j = jb + kk;
-    __syncthreads();   // column j is in LDS
-    float cr[R], cc[R];
-    lds_row(&colst[j * NB + r0], cr);
-    lds_row(&colst[j * NB + c0], cc);
-    float piv = colst[j * NB + j];
-    if (!(piv > 0.f)) piv = 1.f;   // recorded below; keeps the rest finite
-    const float ip = 1.f / piv;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      cr[i] = (r0 + i > j) ? cr[i] * ip : 0.f;
-      cc[i] = (c0 + i > j) ? cc[i] : 0.f;
-    }
-    const int kn = (kk + 1) % R;                          // register of column j+1 (constant once unrolled)
-    const bool own_next = (tx == (j + 1) / R) && (j + 1 < NB);
-    if (own_next) {
-      float col[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        a[i][kn] = fmaf(-cr[i], cc[kn], a[i][kn]);
-        col[i] = a[i][kn];
-      }
-      lds_store_row(&colst[(j + 1) * NB + r0], col);
-    }
-    cc[kn] = own_next ? 0.f : cc[kn];                    // that column is done
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int k = 0; k < R; ++k) a[i][k] = fmaf(-cr[i], cc[k], a[i][k]);
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int r = e / NB, c = e % NB;
+    S[r * SS + c] = L[(int64_t)(k0 + r) * d + k0 + c];
   }
   __syncthreads();
-  if (tid == 0) {
-    for (int j = 0; j < NB; ++j)
-      if (!(colst[j * NB + j] > 0.f)) {
-        bad = j + 1;
-        break;
+  auto SB = [&](int i, int k) { return S + 32 * i * SS + 32 * k; };
+  auto XB = [&](int i, int k) { return X + 32 * i * SS + 32 * k; };
+  // A_ik -= L_ij L_kj^T
+  auto trailing = [&](int i, int k, int j) {
+    f32x16 acc = blk_load<SS>(SB(i, k), l32, hf);
+    blk_mma<SS, true>(acc, SB(i, j), SB(k, j), -1.f, l32, hf);
+    blk_store<SS>(SB(i, k), acc, l32, hf);
+  };
+  // X_ij = -L_ii^-1 (sum_{k=j..i-1} L_ik X_kj), the sum staged in upper block (0, 1 + slot) of X
+  auto xblock = [&](int i, int j, int slot) {
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll 1
+    for (int k = j; k < i; ++k) blk_mma<SS, false>(acc, SB(i, k), XB(k, j), 1.f, l32, hf);
+    float *T = XB(0, 1 + slot);
+    blk_store<SS>(T, acc, l32, hf);
+    wave_lds_sync();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    blk_mma<SS, false>(acc, XB(i, i), T, -1.f, l32, hf);
+    blk_store<SS>(XB(i, j), acc, l32, hf);
+  };
+#pragma unroll 1
+  for (int jb = 0; jb < NL; ++jb) {
+    if (w == 0) {
+      if (jb > 0) {
+        trailing(jb, jb, jb - 1);
+        wave_lds_sync();
       }
-  }
-  // inverse of the unit-lower factor U[r][j] = colst[j][r] / piv_j by a forward sweep:
-  // Y = I; for each j, rows i > j: Y[i][c] -= U[i][j] Y[j][c]. Same look-ahead: the owners of
-  // row j+1 of Y update and publish it first.
-  float y[R][R];
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-#pragma unroll
-    for (int k = 0; k < R; ++k) y[i][k] = (r0 + i == c0 + k) ? 1.f : 0.f;
-  if (ty == 0) {
-    float row[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k) row[k] = y[0][k];
-    lds_store_row(&rowst[c0], row);
-  }
-  for (int jb = 0; jb < NB; jb += R)
-#pragma unroll
-  for (int ii = 0; ii < R; ++ii) {
-    const int j = jb + ii;
-    if (j == NB - 1) break;     // uniform: the last row has nothing below it
-    __syncthreads();            // row j of Y is in LDS
-    // row j of Y is zero beyond column j (Y is lower triangular); rows <= j get u = 0
-    float u[R], yr[R];
-    lds_row(&colst[j * NB + r0], u);
-    lds_row(&rowst[j * NB + c0], yr);
-    float piv = colst[j * NB + j];
-    if (!(piv > 0.f)) piv = 1.f;
-    const float ip = 1.f / piv;
-#pragma unroll
-    for (int i = 0; i < R; ++i) u[i] = (r0 + i > j) ? u[i] * ip : 0.f;
-    const int in = (ii + 1) % R;                          // register row of row j+1 (constant once unrolled)
-    const bool own_next = (ty == (j + 1) / R) && (j + 1 < NB - 1);
-    if (own_next) {
-      float row[R];
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        y[in][k] = fmaf(-u[in], yr[k], y[in][k]);
-        row[k] = y[in][k];
-      }
-      lds_store_row(&rowst[(j + 1) * NB + c0], row);
+      const int lb = leaf_factor<SS>(SB(jb, jb), XB(jb, jb), colbuf, l32, hf);
+      if (lb && lane == 0 && bad == 0) bad = 32 * jb + lb;
+    } else if (jb > 0) {
+      int t = 0;
+#pragma unroll 1
+      for (int k = jb; k < NL; ++k)
+#pragma unroll 1
+        for (int i = k; i < NL; ++i) {
+          if (i == jb && k == jb) continue;
+          if (t++ % 3 == w - 1) trailing(i, k, jb - 1);
+        }
+#pragma unroll 1
+      for (int j = 0; j < jb - 1; ++j)
+        if (t++ % 3 == w - 1) xblock(jb - 1, j, j);
     }
-    u[in] = own_next ? 0.f : u[in];                      // that row is done
+    __syncthreads();
+    if (jb + 1 < NL) {
+#pragma unroll 1
+      for (int i = jb + 1; i < NL; ++i)
+        if (w == (i - jb - 1) % 4) {
+          f32x16 acc;
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int k = 0; k < R; ++k) y[i][k] = fmaf(-u[i], yr[k], y[i][k]);
-  }
-  // L = U D^1/2 (lower part of the block), Linv = D^-1/2 Y
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int r = r0 + i;
-    float pr = colst[r * NB + r];
-    if (!(pr > 0.f)) pr = 1.f;
-    const float isr = 1.f / sqrtf(pr);
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const int c = c0 + k;
-      Linv[r * NB + c] = y[i][k] * isr;
-      float pc = colst[c * NB + c];
-      if (!(pc > 0.f)) pc = 1.f;
-      if (c < r) L[(int64_t)(k0 + r) * d + k0 + c] = colst[c * NB + r] / sqrtf(pc);
-      else if (c == r) L[(int64_t)(k0 + r) * d + k0 + c] = sqrtf(pr);
+          for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+          blk_mma<SS, true>(acc, SB(i, jb), XB(jb, jb), 1.f, l32, hf);   // A_ij L_jj^-T
+          blk_store<SS>(SB(i, jb), acc, l32, hf);
+        }
+      __syncthreads();
     }
   }
+#pragma unroll 1
+  for (int j = 0; j < NL - 1; ++j)
+    if (w == j % 4) xblock(NL - 1, j, j);
   __syncthreads();
+  for (int e = tid; e < NB * NB; e += kThreads) {
+    const int r = e / NB, c = e % NB;
+    if (c <= r) L[(int64_t)(k0 + r) * d + k0 + c] = S[r * SS + c];
+    Linv[r * NB + c] = c <= r ? X[r * SS + c] : 0.f;
+  }
   if (tid == 0 && bad != 0 && info[layer] == 0) info[layer] = k0 + bad;
 }
 
@@ -571,13 +607,13 @@ hipError_t launch_shift_copy(const CPtrBatch &G, float *L, int64_t L_stride, int
 
 hipError_t launch_potrf_diag(float *L, int64_t L_stride, int d, int k0, int nb, float *Linv,
                              int64_t Linv_stride, int32_t *info, int count, hipStream_t s) {
-  const size_t shmem = 2 * (size_t)nb * nb * sizeof(float);
+  const size_t shmem = 2 * (size_t)nb * (nb + 1) * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute((const void *)potrf_diag_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        2 * 128 * 128 * (int)sizeof(float));
+                        2 * 128 * 129 * (int)sizeof(float));
     hipFuncSetAttribute((const void *)potrf_diag_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        2 * 64 * 64 * (int)sizeof(float));
+                        2 * 64 * 65 * (int)sizeof(float));
     attr_set = true;
   }
   if (nb == 128)

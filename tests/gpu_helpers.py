@@ -124,3 +124,48 @@ def admissible_selection(sel, eps_ref, k: int, tol: float) -> None:
     worst_in = float(eps_ref[sel].max())
     best_out = float(eps_ref[rest].min())
     assert worst_in <= r * best_out, (sel, worst_in, best_out)
+
+
+def bf16_p_sigma(inp, rows=None):
+    """Spread of each output element [n_q or len(rows), H*d_h] that rounding the probabilities to bf16
+    (the value product's operand) causes: independent errors uniform over half a bf16 spacing, 2^-8
+    relative, so std p 2^-8 / sqrt(3); probabilities from exact float64 scores against the true maximum
+    (the device's running maximum never exceeds it). Returns {"A_loc": ..., "A_full": ...}."""
+    q = np.asarray(inp["q"], np.float64)
+    if rows is not None:
+        q = q[rows]
+    scale = float(inp["scale"])
+    segs = {"A_loc": ("sink", "cur"), "A_full": ("sink", "cur", "hist")}
+    out = {}
+    n_q, H, dh = q.shape
+    for name, names in segs.items():
+        k = np.concatenate([np.asarray(inp[n + "_k"], np.float64) for n in names])
+        v = np.concatenate([np.asarray(inp[n + "_v"], np.float64) for n in names])
+        sig = np.zeros((n_q, H * dh))
+        for h in range(H):
+            sc = scale * (q[:, h, :] @ k[:, h, :].T)
+            p = np.exp(sc - sc.max(axis=1, keepdims=True))
+            L = p.sum(axis=1, keepdims=True)
+            err = p * 2.0 ** -8 / np.sqrt(3.0)
+            sig[:, h * dh:(h + 1) * dh] = np.sqrt((err / L) ** 2 @ (v[:, h, :] ** 2))
+        out[name] = sig
+    return out
+
+
+def check_attention_tight(out, ref, sig, rows=None, sigmas=6.0):
+    """bf16 rows against the oracle within the arithmetic's own bound: `sigmas` x the bf16 probability-
+    rounding spread plus the bf16 rounding of the stored row (2^-9 |A|, doubled) plus 1e-6. Returns the
+    largest error in units of sigma."""
+    worst = {}
+    for mine, theirs in (("a_loc", "A_loc"), ("a_full", "A_full")):
+        if out[mine] is None:
+            continue
+        got = to_host64(out[mine])
+        if rows is not None:
+            got = got[rows]
+        want, sg = ref[theirs], sig[theirs]
+        err = np.abs(got - want)
+        excess = err - (sigmas * sg + 2.0 ** -8 * np.abs(want) + 1e-6)
+        assert np.all(excess <= 0), (mine, float(excess.max()), float((err / (sg + 1e-30)).max()))
+        worst[mine] = float(((err - 2.0 ** -8 * np.abs(want)).clip(0) / (sg + 1e-30)).max())
+    return worst

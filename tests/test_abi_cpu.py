@@ -172,6 +172,26 @@ def test_fp8_argument_errors(L):
     assert call(n_q=0) == _abi.ISPA_OK
 
 
+def test_balanced_argument_errors(L):
+    f = L.ispa_attn_dual_balanced
+
+    def call(dt=1, H=2, dh=128, n_q=32, sink=None, cur=None, hist=None, a_loc=FAKE, ws=None, wsb=0):
+        sink = sink if sink is not None else seg()
+        cur = cur if cur is not None else seg()
+        hist = hist if hist is not None else seg()
+        return f(dt, H, dh, ctypes.c_float(0.088), FAKE, n_q, 256, sink, cur, hist, a_loc, FAKE2, None, None, None,
+                 ws, wsb, None)
+    assert call(H=0) == _abi.ISPA_E_ARG
+    assert call(dh=96) == _abi.ISPA_E_UNSUPPORTED
+    assert call(dt=7) == _abi.ISPA_E_UNSUPPORTED
+    assert call(sink=seg(n=0), cur=seg(n=0)) == _abi.ISPA_E_ARG
+    assert call(a_loc=None) == _abi.ISPA_E_ARG
+    assert call(n_q=0) == _abi.ISPA_OK
+    assert L.ispa_attn_dual_balanced_workspace(1, 0, 128, 4680, 100, 100) == 0
+    assert L.ispa_attn_dual_balanced_workspace(1, 12, 128, 4680, -1, 100) == 0
+    assert L.ispa_attn_dual_balanced_workspace(0, 12, 128, 4680, 9360, 9360) == 0   # fp32: plain schedule
+
+
 def test_fp8_pv_argument_errors(L):
     at = L.ispa_attn_dual_fp8_pv
 

@@ -12,7 +12,7 @@ import pytest
 import ispa_inputs as inputs
 from oracle import attention as oatt
 
-from gpu_helpers import (check_attention, run_attn, to_dev, to_host64, empty_outputs, torch_mod,
+from gpu_helpers import (bf16_p_sigma, check_attention, check_attention_tight, run_attn, to_dev, to_host64, empty_outputs, torch_mod,
                          max_abs, rel_fro)
 
 pytestmark = pytest.mark.gpu
@@ -261,3 +261,98 @@ def test_workload5_merge_equals_single_pass():
     assert max_abs(to_host64(out["lse_full"]), to_host64(single["lse_loc"])) <= 1e-4
     lse = np.logaddexp(to_host64(out["lse_loc"]), to_host64(out["lse_hist"]))
     assert max_abs(lse, to_host64(out["lse_full"])) <= 1e-4
+
+
+# ---- balanced schedule (ispa_attn_dual_balanced) ----------------------------------------------------
+def run_attn_balanced(inp, want_full=True):
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    dt = inp["dtype"]
+    dev = {k: to_dev(inp[k], dt) for k in ("q", "sink_k", "sink_v", "cur_k", "cur_v", "hist_k", "hist_v")}
+    n_q, H, dh = inp["q"].shape
+    out = empty_outputs(n_q, H, dh, dt, want_full)
+    n_loc = inp["sink_k"].shape[0] + inp["cur_k"].shape[0]
+    n_hist = inp["hist_k"].shape[0] if want_full else 0
+    need = ispa.ispa_attn_dual_balanced_workspace(dev["q"], n_loc, n_hist)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ispa.ispa_attn_dual_balanced(dev["q"], dev["sink_k"], dev["sink_v"], dev["cur_k"], dev["cur_v"], dev["hist_k"],
+                                 dev["hist_v"], float(inp["scale"]), out["a_loc"], out["a_full"], out["lse_loc"],
+                                 out["lse_hist"], out["lse_full"], ws=ws)
+    torch.cuda.synchronize()
+    return need, out
+
+
+def _same_outputs(x, y):
+    torch = torch_mod()
+    return all((x[k] is None and y[k] is None) or torch.equal(x[k], y[k]) for k in x)
+
+
+@pytest.mark.parametrize("cfg,chunk", [(2, 0), (3, 0)])
+def test_balanced_workload_rows(cfg, chunk):
+    """12 heads x 19 query tiles leave 28 of 256 compute units idle: the balanced schedule cuts units
+    between workgroups (config 2: local and history keys; config 3 chunk 1: local keys only, so the
+    local branch itself is merged). Sampled rows of all heads against the oracle, the plain call within
+    the same bounds, and the call repeated bit for bit."""
+    inp, rows = _sampled(cfg, chunk=chunk, n_rows=40, seed=7)
+    _log(f"case: balanced schedule, workload {cfg} chunk {chunk + 1}, sampled rows ({len(rows)})")
+    need, out = run_attn_balanced(inp)
+    assert need > 0, "expected the balanced schedule at 12 heads"
+    ref = oatt.dual_stream(inp, rows=rows)
+    rep = check_attention(out, ref, "bf16", rows=rows)
+    sig = bf16_p_sigma(inp, rows=rows)
+    _log(f"  {rep}; worst element in bf16-rounding sigmas: balanced {check_attention_tight(out, ref, sig, rows)}")
+    _, out2 = run_attn_balanced(inp)
+    assert _same_outputs(out, out2), "balanced schedule not repeatable"
+    # the plain call meets the same bound, and the two differ by two independent roundings of the
+    # probabilities (each against its own running maximum): sqrt(2) sigma, and the LSEs by fp32 sums
+    _, plain = run_attn(inp)
+    _log(f"  plain: {check_attention_tight(plain, ref, sig, rows)}")
+    for k, name in (("a_loc", "A_loc"), ("a_full", "A_full")):
+        x, y = to_host64(out[k])[rows], to_host64(plain[k])[rows]
+        excess = np.abs(x - y) - (6.0 * np.sqrt(2.0) * sig[name] + 2.0 ** -7 * np.abs(y) + 2e-6)
+        assert np.all(excess <= 0), (k, float(excess.max()))
+    for k in ("lse_loc", "lse_hist", "lse_full"):
+        x, y = to_host64(out[k]), to_host64(plain[k])
+        fin = np.isfinite(y)
+        assert np.array_equal(np.isfinite(x), fin)
+        assert np.all(np.abs(x[fin] - y[fin]) <= 1e-5), (k, float(np.abs(x[fin] - y[fin]).max()))
+
+
+def test_balanced_many_pieces_full_compare():
+    """Few units (2 heads x 3 query tiles) over many key tiles: every unit is cut into about forty
+    pieces, local and history keys alike; all rows against the oracle."""
+    inp = inputs.attention_case(23, 2, 128, 600, 40, 3000, 9000, dtype="bf16", rho=0.95)
+    _log("case: balanced schedule, 2 x 128, 600 queries, 40/3000/9000 keys (many pieces per unit)")
+    need, out = run_attn_balanced(inp)
+    assert need > 0
+    ref = oatt.dual_stream(inp)
+    rep = check_attention(out, ref, "bf16")
+    sig = bf16_p_sigma(inp)
+    _log(f"  {rep}; worst element in bf16-rounding sigmas: {check_attention_tight(out, ref, sig)}")
+    _, plain = run_attn(inp)
+    for k in ("lse_loc", "lse_hist", "lse_full"):
+        assert np.all(np.abs(to_host64(out[k]) - to_host64(plain[k])) <= 1e-5), k
+
+
+def test_balanced_local_only_and_empty_history():
+    inp = inputs.attention_case(24, 2, 128, 600, 16, 12000, 700, dtype="bf16")
+    _log("case: balanced schedule, local-only call and a call with an empty history")
+    need, out = run_attn_balanced(inp, want_full=False)
+    assert need > 0
+    ref = oatt.dual_stream(inp)
+    check_attention(out, ref, "bf16")
+    check_attention_tight(out, ref, bf16_p_sigma(inp))
+    inp0 = dict(inp, hist_k=inp["hist_k"][:0], hist_v=inp["hist_v"][:0])
+    _, out0 = run_attn_balanced(inp0)
+    torch = torch_mod()
+    assert torch.equal(out0["a_full"], out0["a_loc"]) and torch.equal(out0["lse_full"], out0["lse_loc"])
+    assert bool(torch.all(torch.isneginf(out0["lse_hist"])))
+    check_attention(out0, oatt.dual_stream(inp0), "bf16")
+
+
+def test_balanced_plain_when_units_fill_the_gpu():
+    """40 heads x 19 query tiles fill 256 compute units in three rounds: no workspace, the plain call."""
+    import kv_cache_attention_split_amd as ispa
+    torch = torch_mod()
+    q = torch.empty((4680, 40, 128), dtype=torch.bfloat16, device="cuda")
+    assert ispa.ispa_attn_dual_balanced_workspace(q, 9360, 9360) == 0
