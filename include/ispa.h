@@ -89,12 +89,13 @@ ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, flo
 /* ---------------------------------------------------------------------------------------------
  * ispa_attn_dual with a balanced schedule over the compute units (same passage; the merge of key-range
  * partial states is the page's log-sum-exp decomposition applied within a branch). When the
- * (head, 256-query tile) units would leave a tenth or more of the GPU's compute units idle in their
- * last round (12 heads x 19 query tiles on 256 units), one workgroup per compute unit takes an equal
- * share of the key tiles of all units; a unit cut between workgroups is computed in key ranges whose
- * partial online-softmax states (accumulator, running maximum, local and history exp-sums) go to
- * `ws`, and the workgroup that completes a unit's last range merges the ranges in key order.
- * Otherwise the call is ispa_attn_dual and `ws` is not touched.
+ * (head, 256-query tile) units would leave a tenth or more of the GPU's compute units idle and fill at
+ * least half of each XCD's (128 <= units < 230 on 256 compute units; 12 heads x 19 query tiles is 228),
+ * one workgroup per compute unit runs: each unit keeps a workgroup for its first key tiles and the
+ * spare workgroups of the same XCD share the units' remaining tiles. Cut units' partial online-softmax
+ * states (accumulator, running maximum, local and history exp-sums) go to `ws`, and the workgroup that
+ * completes a unit's last piece merges the pieces in key order. Otherwise the call is ispa_attn_dual
+ * and `ws` is not touched.
  *
  *   arguments, outputs and errors as for ispa_attn_dual, plus
  *   ws, ws_bytes  device scratch of at least ispa_attn_dual_balanced_workspace(...) bytes, 256-byte
@@ -103,12 +104,13 @@ ispa_status ispa_attn_dual(ispa_dtype dt, int32_t n_heads, int32_t head_dim, flo
  * Results are within the attention tolerances of ispa_attn_dual and identical from call to call
  * (ranges are merged in a fixed order, whichever workgroup finishes last); they are not bitwise
  * those of ispa_attn_dual, whose single pass adds the same terms in another order. Speed: on MI355X
- * at 12 heads x 4680 queries x 18,720 keys this schedule takes 0.71 ms against 0.57 ms for
- * ispa_attn_dual (ranges that start at arbitrary keys of arbitrary heads lose the L2 reuse of the
- * plain schedule, whose units of one head walk the keys together on one XCD).
+ * at 12 heads x 4680 queries x 18,720 keys this schedule takes 0.62 ms against 0.59 ms for
+ * ispa_attn_dual on the same GPU: storing and merging the partial states costs about as much as the
+ * idle compute units it puts to work.
  * ispa_attn_dual_balanced_workspace: bytes for a call with these sizes on the current device (0 when
- * the plain schedule is used: dt other than ISPA_BF16, head_dim other than 128, or units filling the
- * compute units); n_local_keys = sink.n + cur.n, n_hist_keys = hist.n (0 for a local-only call).
+ * the plain schedule is used: dt other than ISPA_BF16, head_dim other than 128, fewer than 16 key
+ * tiles of 64, or a unit count outside the range above); n_local_keys = sink.n + cur.n, n_hist_keys =
+ * hist.n (0 for a local-only call). 557,056 bytes per unit (4 state slots) and a counter.
  * ------------------------------------------------------------------------------------------- */
 size_t ispa_attn_dual_balanced_workspace(ispa_dtype dt, int32_t n_heads, int32_t head_dim, int64_t n_q,
                                          int64_t n_local_keys, int64_t n_hist_keys);

@@ -505,72 +505,92 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
   }
 }
 
-// Balanced schedule (SPLIT form of the ping-pong kernel): a workspace slot per piece of a cut unit.
-// A workgroup's range (shorter than a unit) holds at most three pieces: the end of one unit, cut at the
-// local end when it begins inside the local keys, and the start of the next.
-constexpr int kSplitPieces = 3;
+// Balanced schedule (SPLIT form of the ping-pong kernel). XCD x (workgroup id mod 8) keeps the units the
+// plain schedule gives it, [us, us + nx), and their lockstep walk over the keys, so that each K/V tile
+// is still fetched about once per XCD: main workgroup j (id x + 8 j, j < nx) takes key tiles [0, R) of
+// unit us + j, and the XCD's E = S - nx spare workgroups (S per XCD) share the remaining tiles [R, nt)
+// of those units, laid end to end, in E equal ranges. Every piece stores its online-softmax state to
+// workspace slot 4 u + k (k = 0 the main piece, then the remaining tiles' pieces in key order); the
+// workgroup that completes a unit's last piece merges them in that order. Which workgroup runs on which
+// XCD decides the speed only: the partition is a function of the workgroup id.
+#ifndef ISPA_SPLIT_MARGIN
+#define ISPA_SPLIT_MARGIN 6
+#endif
+constexpr int kSplitSlots = 4;                               // per unit
 constexpr size_t kSplitScal = 16 * 512 * 4;                 // floats of one stored accumulator
 constexpr size_t kSplitSlotFloats = kSplitScal + 4 * 512;
 
-// Pieces of unit u (tiles [u nt, (u+1) nt) of the sequence) in the range of workgroup p: `n` pieces
-// [a0[k], a1[k]) (key tiles of the unit) in slots slot[k]. A piece that begins inside the local keys
-// (but not at the unit's start) and runs past their end is cut there.
-struct UnitPieces {
-  int n, a0[2], a1[2], slot[2];
+struct SplitGeom {
+  int us, nx, R, L, E;   // units [us, us + nx); main tiles [0, R); L = nt - R tiles left per unit; E spares
+  int64_t len;           // nx L: the XCD's remaining tiles, end to end
 };
-__device__ __forceinline__ UnitPieces unit_pieces(int64_t u, int p, int G, int64_t total, int nt, int nt_loc) {
-  UnitPieces r;
-  r.n = 0;
-  const int64_t s0 = total * p / G, s1 = total * (p + 1) / G;
-  const int64_t u0 = u * nt, u1 = u0 + nt;
-  const int64_t b0 = s0 > u0 ? s0 : u0, b1 = s1 < u1 ? s1 : u1;
-  if (b0 >= b1) return r;
-  int k = 0;   // pieces of this workgroup before unit u
-  if (s0 < u0) {
-    const int t = (int)(s0 - (s0 / nt) * nt);   // start of the workgroup's first unit piece
-    k = (t > 0 && t < nt_loc && nt > nt_loc) ? 2 : 1;
+__device__ __forceinline__ SplitGeom split_geom(int x, int units, int S, int nt) {
+  SplitGeom g;
+  const int per = units / 8, rem = units % 8;
+  g.us = x * per + (x < rem ? x : rem);
+  g.nx = per + (x < rem ? 1 : 0);
+  // main workgroups take ISPA_SPLIT_MARGIN tiles more than an equal share: the spare ones, which run
+  // several pieces, then tend to finish first, and each main workgroup merges its own unit
+  const int r = (int)((int64_t)g.nx * nt / S) + ISPA_SPLIT_MARGIN;
+  g.R = r < nt - 1 ? r : nt - 1;
+  g.L = nt - g.R;
+  g.E = S - g.nx;
+  g.len = (int64_t)g.nx * g.L;
+  return g;
+}
+
+// Cuts strictly inside the remaining tiles (R, nt) of the XCD's unit k, in order: the spare-range
+// boundary that falls there (ranges are at least L tiles long when nx >= E, so at most one) and the
+// local end (a piece never holds keys of both branches unless it starts at tile 0).
+struct UnitCuts {
+  int n, c0, c1;
+};
+__device__ __forceinline__ UnitCuts unit_cuts(const SplitGeom &g, int k, int nt, int nt_loc) {
+  const int64_t u0 = (int64_t)k * g.L;
+  // the first range start floor(e len / E) above u0
+  const int64_t e = ((u0 + 1) * g.E + g.len - 1) / g.len;
+  int bc = -1;
+  if (e < g.E) {
+    const int64_t bnd = e * g.len / g.E;
+    if (bnd < u0 + g.L) bc = g.R + (int)(bnd - u0);
   }
-  const int x0 = (int)(b0 - u0), x1 = (int)(b1 - u0);
-  if (x0 > 0 && x0 < nt_loc && x1 > nt_loc) {
+  const int lc = (g.R < nt_loc && nt_loc < nt) ? nt_loc : -1;
+  UnitCuts r;
+  if (bc >= 0 && lc >= 0 && bc != lc) {
     r.n = 2;
-    r.a0[0] = x0, r.a1[0] = nt_loc, r.slot[0] = kSplitPieces * p + k;
-    r.a0[1] = nt_loc, r.a1[1] = x1, r.slot[1] = kSplitPieces * p + k + 1;
+    r.c0 = bc < lc ? bc : lc;
+    r.c1 = bc < lc ? lc : bc;
   } else {
-    r.n = 1;
-    r.a0[0] = x0, r.a1[0] = x1, r.slot[0] = kSplitPieces * p + k;
+    r.n = (bc >= 0 || lc >= 0) ? 1 : 0;
+    r.c0 = r.c1 = bc >= 0 ? bc : lc;
   }
   return r;
 }
 
-// Merge of a cut unit's pieces (the workgroup that finished its last piece; all 512 threads; bf16
-// values, head_dim 128). Pieces are visited in sequence order; each holds its accumulator o and running
-// maximum m (log2 units) with the exp-sum l of its keys, or, for the unit's first piece when it
-// completed the local keys (and wrote A_loc itself), l of its history keys and l_loc of its local keys.
-// A_full and lse_full merge every piece; lse_hist the history pieces; A_loc and lse_loc, when the
-// local keys were cut, the pieces inside them.
-__device__ __forceinline__ void merge_unit(const AttnArgs &a, int vid, int nt, int nt_loc, int nt_hist, int64_t total,
-                                           int n_qt, int tid) {
+// Merge of unit us + k's pieces (all 512 threads; bf16 values, head_dim 128) in slot order. Each piece
+// holds its accumulator o and running maximum m (log2 units) with the exp-sum l of its keys; the main
+// piece, when it completed the local keys (and wrote A_loc itself), holds l of its history keys and
+// l_loc of its local keys. A_full and lse_full merge every piece, lse_hist the pieces with history keys,
+// and A_loc and lse_loc, when the main piece ends inside the local keys, the pieces inside them.
+__device__ __forceinline__ void merge_unit(const AttnArgs &a, const SplitGeom &sg, int k, int nt, int nt_loc,
+                                           int nt_hist, int n_qt, int tid) {
   constexpr int D = 128, NDB = 4;
+  const int vid = sg.us + k;
   const int lane = tid & 63, hf = lane >> 5;
   const int head = vid / n_qt, qt = vid % n_qt;
   const int qi = qt * 256 + (tid >> 6) * 32 + (lane & 31);
   const int head_off = head * D, out_stride = a.n_heads * D, n_q = a.n_q;
-  const int64_t u0 = (int64_t)vid * nt;
-  const int G = gridDim.x;
-  const int first = (int)(((u0 + 1) * G - 1) / total);
-  const int last = (int)(((u0 + nt) * G - 1) / total);
-  // pass 1 (LOCAL = false): every piece -> A_full, lse_full, lse_hist; pass 2 (LOCAL = true, when the
-  // local keys were cut): the pieces inside the local keys -> A_loc, lse_loc
+  const UnitCuts cu = unit_cuts(sg, k, nt, nt_loc);
+  const int np = 2 + cu.n;
+  // last key tile (exclusive) of piece p
+  auto hi = [&](int p) { return p == 0 ? sg.R : (p == 1 && cu.n >= 1) ? cu.c0 : (p == 2 && cu.n == 2) ? cu.c1 : nt; };
+  const float *base = a.split_ws + (size_t)kSplitSlots * vid * kSplitSlotFloats;
   auto pass = [&](auto local_c) {
     constexpr bool LOCAL = decltype(local_c)::value;
     float mx = -INFINITY;
-    for (int p = first; p <= last; ++p) {
-      const UnitPieces pc = unit_pieces(vid, p, G, total, nt, nt_loc);
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        if (k >= pc.n || (LOCAL && pc.a1[k] > nt_loc)) continue;
-        mx = fmaxf(mx, a.split_ws[(size_t)pc.slot[k] * kSplitSlotFloats + kSplitScal + tid]);
-      }
+    for (int p = 0; p < np; ++p) {
+      if (LOCAL && hi(p) > nt_loc) continue;
+      mx = fmaxf(mx, base[(size_t)p * kSplitSlotFloats + kSplitScal + tid]);
     }
     f32x16 acc[NDB];
 #pragma unroll
@@ -578,25 +598,21 @@ __device__ __forceinline__ void merge_unit(const AttnArgs &a, int vid, int nt, i
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
     float ls = 0.f, lh = 0.f;
-    for (int p = first; p <= last; ++p) {
-      const UnitPieces pc = unit_pieces(vid, p, G, total, nt, nt_loc);
+    for (int p = 0; p < np; ++p) {
+      if (LOCAL && hi(p) > nt_loc) continue;
+      const float *sl = base + (size_t)p * kSplitSlotFloats;
+      const float m = sl[kSplitScal + tid], l = sl[kSplitScal + 512 + tid];
+      const float c = __builtin_amdgcn_exp2f(m - mx);
+      ls += (LOCAL ? l : l + sl[kSplitScal + 1024 + tid]) * c;
+      if (!LOCAL && hi(p) > nt_loc) lh += l * c;   // a piece with history keys: l is their sum
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        if (k >= pc.n || (LOCAL && pc.a1[k] > nt_loc)) continue;
-        const float *sl = a.split_ws + (size_t)pc.slot[k] * kSplitSlotFloats;
-        const float m = sl[kSplitScal + tid], l = sl[kSplitScal + 512 + tid];
-        const float c = __builtin_amdgcn_exp2f(m - mx);
-        ls += (LOCAL ? l : l + sl[kSplitScal + 1024 + tid]) * c;
-        if (!LOCAL && pc.a1[k] > nt_loc) lh += l * c;   // a piece with history keys: l is their sum
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 x = *(const f32x4 *)(sl + 4 * ((db * 4 + g4) * 512 + tid));
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 x = *(const f32x4 *)(sl + 4 * ((db * 4 + g4) * 512 + tid));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[db][4 * g4 + e] += x[e] * c;
-          }
-      }
+          for (int e = 0; e < 4; ++e) acc[db][4 * g4 + e] += x[e] * c;
+        }
     }
     const float tot = halves_sum(ls);
     if constexpr (LOCAL) {
@@ -610,9 +626,7 @@ __device__ __forceinline__ void merge_unit(const AttnArgs &a, int vid, int nt, i
     }
   };
   pass(std::integral_constant<bool, false>{});
-  // the local keys were cut when the unit's first piece ended inside them
-  const UnitPieces p0 = unit_pieces(vid, first, G, total, nt, nt_loc);
-  if (p0.a1[0] < nt_loc) pass(std::integral_constant<bool, true>{});
+  if (sg.R < nt_loc) pass(std::integral_constant<bool, true>{});
   if (tid == 0) a.split_count[vid] = 0;   // ready for the next call
 }
 
@@ -656,7 +670,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][TBK];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][TBV];
   __shared__ __attribute__((aligned(256))) float bbuf[2][BIAS ? BK : 1];   // bias of tiles, beside K
-  __shared__ int s_merge;   // SPLIT: this workgroup finished a unit's last segment and merges it
+  __shared__ uint64_t s_merge;   // SPLIT: the units (bit k - k_lo) whose merge falls to this workgroup
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -669,27 +683,43 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   const int nt = nt_loc + nt_hist;            // key tiles of every (head, query tile) unit
   const int nsplit = LSE_ONLY ? a.lse_splits : 1;   // key ranges per unit in the LSE-only form
 
-  // SPLIT (balanced schedule): the units' tiles form one sequence, unit after unit; workgroup `pos`
-  // takes the contiguous range [total pos / G, total (pos+1) / G) of it, so every workgroup has the
-  // same number of tiles. A unit cut by a range boundary is processed in segments; each writes its
-  // partial online-softmax state to a workspace slot, and the workgroup that finishes a unit's last
-  // segment merges the unit's segments in sequence order (the log-sum-exp decomposition of the
-  // softmax) and writes its rows. Otherwise one pass: the workgroup's own unit (and key range).
-  const int64_t total = (int64_t)n_qt * a.n_heads * nt;
-  const int pos = SPLIT ? xcd_remap(blockIdx.x, gridDim.x) : 0;
-  int64_t seg_pos = SPLIT ? total * pos / gridDim.x : 0;
-  const int64_t seg_end = SPLIT ? total * (pos + 1) / gridDim.x : 1;
-  int pending0 = -1, pending1 = -1;   // SPLIT: units whose last piece this workgroup completed
-  int n_pieces = 0;
+  // SPLIT (balanced schedule, see split_geom): a main workgroup runs one piece, [0, R) of its unit; a
+  // spare one walks its range of the XCD's remaining tiles piece by piece (a piece ends at a unit's end
+  // and at the local end). Otherwise one pass: the workgroup's own unit (and key range).
+  const int jw = (int)(blockIdx.x >> 3);
+  const SplitGeom sg = SPLIT ? split_geom((int)(blockIdx.x & 7), n_qt * a.n_heads, (int)(gridDim.x >> 3), nt)
+                             : SplitGeom{0, 0, 0, 0, 1, 1};
+  const bool spare = SPLIT && jw >= sg.nx;
+  int64_t seg_pos = spare ? (int64_t)(jw - sg.nx) * sg.len / sg.E : 0;
+  const int64_t seg_end = spare ? (int64_t)(jw - sg.nx + 1) * sg.len / sg.E : 1;
+  // SPLIT: the XCD's units this workgroup ran pieces of, [k_lo, k_hi], and those with two pieces here
+  // (bit k - k_lo: a range cut at the local end)
+  int k_lo = -1, k_hi = -1;
+  uint64_t two = 0;
   while (seg_pos < seg_end) {
-  int vid, split = 0, t0, t1;
+  int vid, split = 0, t0, t1, slot = 0;
   if constexpr (SPLIT) {
-    vid = (int)(seg_pos / nt);
-    t0 = (int)(seg_pos - (int64_t)vid * nt);
-    const int64_t e = seg_end - (int64_t)vid * nt;
-    t1 = (int)(e < nt ? e : nt);
-    // a piece that begins inside the local keys (not at the start) ends at the local end
-    if (t0 > 0 && t0 < nt_loc && t1 > nt_loc) t1 = nt_loc;
+    if (!spare) {
+      vid = sg.us + jw;
+      t0 = 0;
+      t1 = sg.R;
+      slot = kSplitSlots * vid;
+      seg_pos = seg_end;
+      k_lo = k_hi = jw;
+    } else {
+      const int k = (int)(seg_pos / sg.L);
+      vid = sg.us + k;
+      t0 = sg.R + (int)(seg_pos - (int64_t)k * sg.L);
+      const int64_t e = seg_end - (int64_t)k * sg.L;
+      t1 = sg.R + e < nt ? (int)(sg.R + e) : nt;
+      if (t0 < nt_loc && nt_loc < t1) t1 = nt_loc;
+      const UnitCuts cu = unit_cuts(sg, k, nt, nt_loc);
+      slot = kSplitSlots * vid + 1 + (cu.n >= 1 && cu.c0 <= t0) + (cu.n == 2 && cu.c1 <= t0);
+      seg_pos = (int64_t)k * sg.L + (t1 - sg.R);
+      if (k_lo < 0) k_lo = k;
+      if (k == k_hi) two |= 1ull << (k - k_lo);
+      k_hi = k;
+    }
   } else {
     const int lin = xcd_remap(blockIdx.x, n_qt * a.n_heads * nsplit);
     vid = lin / nsplit;
@@ -697,11 +727,8 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     // tiles of this workgroup: all of them, or one contiguous range per split in the LSE-only form
     t0 = LSE_ONLY ? (int)((int64_t)split * nt / nsplit) : 0;
     t1 = LSE_ONLY ? (int)((int64_t)(split + 1) * nt / nsplit) : nt;
+    seg_pos = seg_end;
   }
-  // workspace slot of this piece: the workgroup's slots in piece order
-  const int slot = kSplitPieces * pos + (n_pieces < kSplitPieces ? n_pieces : kSplitPieces - 1);
-  ++n_pieces;
-  seg_pos = SPLIT ? (int64_t)vid * nt + t1 : seg_end;
   const int head = vid / n_qt, qt = vid % n_qt;
   const int head_off = head * D;
   const int qi = qt * 256 + w * 32 + l32;
@@ -1086,35 +1113,36 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
       write_lse(a.lse_hist, th > 0.f ? (m + __log2f(th)) * kLn2 : -INFINITY, head, qi, n_q, hf);
     }
   } else {
-    // a cut unit: store this piece's state, count it, and merge if it was the unit's last
+    // a cut unit: store this piece's state (counted once the workgroup's last piece is stored)
     store_state(slot_ws);
     slot_ws[kSplitScal + tid] = m;
     slot_ws[kSplitScal + 512 + tid] = l;
     slot_ws[kSplitScal + 2 * 512 + tid] = l_loc;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int64_t u0 = (int64_t)vid * nt;
-      const int first = (int)(((u0 + 1) * gridDim.x - 1) / total);
-      const int last = (int)(((u0 + nt) * gridDim.x - 1) / total);
-      int npc = 0;
-      for (int p = first; p <= last; ++p) npc += unit_pieces(vid, p, gridDim.x, total, nt, nt_loc).n;
-      const int done = atomicAdd(a.split_count + vid, 1);
-      s_merge = done == npc - 1;
-    }
-    __syncthreads();
-    if (s_merge) {
-      if (pending0 < 0) pending0 = vid;
-      else pending1 = vid;
-    }
   }
   }   // segments
   if constexpr (SPLIT) {
-    if (pending0 >= 0) {
-      __threadfence();
-      merge_unit(a, pending0, nt, nt_loc, nt_hist, total, n_qt, tid);
+    // Every wave's stores complete in L2; then wave 0 makes them visible at agent scope with one release
+    // (a write-back of the XCD's L2; a sequentially consistent fence would also invalidate it, dropping
+    // the K/V tiles the XCD's other workgroups are reading) and counts each unit's pieces, one lane per
+    // unit. The increment that completes a unit's count gives its merge to this workgroup.
+    ISPA_WAIT_VMCNT(0);
+    __syncthreads();
+    if (w == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const int k = k_lo + lane;
+      bool last = false;
+      if (k_lo >= 0 && k <= k_hi) {
+        const int here = 1 + (int)((two >> lane) & 1);
+        const int npc = 2 + unit_cuts(sg, k, nt, nt_loc).n;
+        last = atomicAdd(a.split_count + sg.us + k, here) + here == npc;
+      }
+      const uint64_t mine = __ballot(last);
+      if (mine != 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other pieces' states
+      if (lane == 0) s_merge = mine;
     }
-    if (pending1 >= 0) merge_unit(a, pending1, nt, nt_loc, nt_hist, total, n_qt, tid);
+    __syncthreads();
+    for (uint64_t p = s_merge; p != 0; p &= p - 1)
+      merge_unit(a, sg, k_lo + __builtin_ctzll(p), nt, nt_loc, nt_hist, n_qt, tid);
   }
 }
 
@@ -1302,17 +1330,19 @@ hipError_t launch_attn_fp8(const AttnArgs &a, int head_dim, hipStream_t s) {
 int attn_balanced_grid(int64_t n_q, int n_heads, int64_t n_keys_loc, int64_t n_keys_hist, int cus) {
   const int64_t units = ((n_q + 255) / 256) * (int64_t)n_heads;
   const int64_t nt = (n_keys_loc + 63) / 64 + (n_keys_hist + 63) / 64;
-  if (units <= 0 || cus <= 0 || nt < 2) return 0;
-  // one round only (a workgroup's range is then shorter than a unit: at most three pieces), and at
-  // least four tiles per workgroup
-  if (units >= cus || units * 10 >= (int64_t)cus * 9 || units * nt < 4 * (int64_t)cus) return 0;
+  if (units <= 0 || cus <= 0 || cus % 8 != 0 || nt < 16) return 0;
+  const int64_t S = cus / 8, nx_min = units / 8, nx_max = (units + 7) / 8;
+  // a tenth or more of the compute units idle under the plain schedule; spare workgroups on every XCD;
+  // at least as many main workgroups as spare ones (a unit's remaining tiles then meet at most one
+  // spare-range boundary); one bit per unit of an XCD in a 64-bit mask
+  if (units * 10 >= (int64_t)cus * 9 || nx_max >= S || 2 * nx_min < S || S > 64) return 0;
   return cus;
 }
 
 size_t attn_balanced_ws_bytes(int64_t n_q, int n_heads, int grid) {
   if (grid <= 0) return 0;
   const int64_t units = ((n_q + 255) / 256) * (int64_t)n_heads;
-  const size_t slots = (size_t)kSplitPieces * grid * kSplitSlotFloats * sizeof(float);
+  const size_t slots = (size_t)kSplitSlots * units * kSplitSlotFloats * sizeof(float);
   return slots + (((size_t)units * sizeof(int) + 255) / 256) * 256;
 }
 
@@ -1330,7 +1360,7 @@ hipError_t launch_attn_bf16_balanced(const AttnArgs &a, int head_dim, int grid, 
   if (units == 0) return hipSuccess;
   AttnArgs b = a;
   b.split_ws = (float *)ws;
-  b.split_count = (int *)((char *)ws + (size_t)kSplitPieces * grid * kSplitSlotFloats * sizeof(float));
+  b.split_count = (int *)((char *)ws + (size_t)kSplitSlots * units * kSplitSlotFloats * sizeof(float));
   hipLaunchKernelGGL(zero_counts_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, b.split_count, units);
   hipLaunchKernelGGL((attn_dual_bf16_pp_kernel<128, false, false, false, false, true>), dim3(grid), dim3(512), 0, s,
                      b, n_qt);

@@ -318,41 +318,72 @@ def test_balanced_workload_rows(cfg, chunk):
         assert np.all(np.abs(x[fin] - y[fin]) <= 1e-5), (k, float(np.abs(x[fin] - y[fin]).max()))
 
 
-def test_balanced_many_pieces_full_compare():
-    """Few units (2 heads x 3 query tiles) over many key tiles: every unit is cut into about forty
-    pieces, local and history keys alike; all rows against the oracle."""
-    inp = inputs.attention_case(23, 2, 128, 600, 40, 3000, 9000, dtype="bf16", rho=0.95)
-    _log("case: balanced schedule, 2 x 128, 600 queries, 40/3000/9000 keys (many pieces per unit)")
-    need, out = run_attn_balanced(inp)
-    assert need > 0
-    ref = oatt.dual_stream(inp)
-    rep = check_attention(out, ref, "bf16")
-    sig = bf16_p_sigma(inp)
-    _log(f"  {rep}; worst element in bf16-rounding sigmas: {check_attention_tight(out, ref, sig)}")
-    _, plain = run_attn(inp)
-    for k in ("lse_loc", "lse_hist", "lse_full"):
-        assert np.all(np.abs(to_host64(out[k]) - to_host64(plain[k])) <= 1e-5), k
+def _tile_rows(n_q, seed):
+    """Three query rows of every 256-query tile (its first, its last and one between): every unit of
+    every head is checked."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for t0 in range(0, n_q, 256):
+        t1 = min(n_q, t0 + 256)
+        rows += [t0, t1 - 1, int(rng.integers(t0, t1))]
+    return np.unique(np.array(rows))
+
+
+def _balanced_against_oracle_and_plain(inp, rows, want_full=True):
+    need, out = run_attn_balanced(inp, want_full=want_full)
+    assert need > 0, "expected the balanced schedule"
+    ref = oatt.dual_stream(inp, rows=rows)
+    rep = check_attention(out, ref, "bf16", rows=rows)
+    sig = bf16_p_sigma(inp, rows=rows)
+    _log(f"  {rep}; worst element in bf16-rounding sigmas: {check_attention_tight(out, ref, sig, rows)}")
+    _, out2 = run_attn_balanced(inp, want_full=want_full)
+    assert _same_outputs(out, out2), "balanced schedule not repeatable"
+    if want_full:
+        _, plain = run_attn(inp)
+        for k in ("lse_loc", "lse_hist", "lse_full"):
+            x, y = to_host64(out[k]), to_host64(plain[k])
+            fin = np.isfinite(y)
+            assert np.array_equal(np.isfinite(x), fin), k
+            assert np.all(np.abs(x[fin] - y[fin]) <= 1e-5), (k, float(np.abs(x[fin] - y[fin]).max()))
+    return out
+
+
+def test_balanced_cut_inside_local_keys():
+    """12 heads x 15 query tiles (180 units, the last tile ragged): each XCD's main workgroups stop at
+    R = 45 or 47 of 58 key tiles, inside the local keys (48 tiles), so A_loc is merged too, and the
+    spare workgroups' ranges cut units' remaining tiles both at range boundaries and at the local end."""
+    inp = inputs.attention_case(23, 12, 128, 3800, 40, 3000, 600, dtype="bf16", rho=0.95)
+    _log("case: balanced schedule, 12 x 128, 3800 queries, 40/3000/600 keys (cuts inside the local keys)")
+    _balanced_against_oracle_and_plain(inp, _tile_rows(3800, 1))
+
+
+def test_balanced_main_piece_ends_at_local_end():
+    """8 heads x 16 query tiles (128 units: 16 per XCD, as many spare workgroups as main ones, so the
+    spare ranges are whole units' remaining tiles) with 26 local and 14 history key tiles: R = 16 x 40 /
+    32 + 6 = 26, the main piece ends exactly at the local end and writes A_loc itself."""
+    inp = inputs.attention_case(25, 8, 128, 4096, 32, 1632, 896, dtype="bf16")
+    _log("case: balanced schedule, 8 x 128, 4096 queries, 32/1632/896 keys (main piece = local keys)")
+    _balanced_against_oracle_and_plain(inp, _tile_rows(4096, 2))
 
 
 def test_balanced_local_only_and_empty_history():
-    inp = inputs.attention_case(24, 2, 128, 600, 16, 12000, 700, dtype="bf16")
-    _log("case: balanced schedule, local-only call and a call with an empty history")
-    need, out = run_attn_balanced(inp, want_full=False)
-    assert need > 0
-    ref = oatt.dual_stream(inp)
-    check_attention(out, ref, "bf16")
-    check_attention_tight(out, ref, bf16_p_sigma(inp))
+    inp = inputs.attention_case(24, 12, 128, 3800, 16, 5000, 700, dtype="bf16")
+    _log("case: balanced schedule, local-only call and a call with an empty history (180 units)")
+    rows = _tile_rows(3800, 3)
+    _balanced_against_oracle_and_plain(inp, rows, want_full=False)
     inp0 = dict(inp, hist_k=inp["hist_k"][:0], hist_v=inp["hist_v"][:0])
-    _, out0 = run_attn_balanced(inp0)
+    out0 = _balanced_against_oracle_and_plain(inp0, rows)
     torch = torch_mod()
     assert torch.equal(out0["a_full"], out0["a_loc"]) and torch.equal(out0["lse_full"], out0["lse_loc"])
     assert bool(torch.all(torch.isneginf(out0["lse_hist"])))
-    check_attention(out0, oatt.dual_stream(inp0), "bf16")
 
 
 def test_balanced_plain_when_units_fill_the_gpu():
-    """40 heads x 19 query tiles fill 256 compute units in three rounds: no workspace, the plain call."""
+    """40 heads x 19 query tiles fill 256 compute units in three rounds, and 2 heads x 3 query tiles leave
+    too few units to keep the lockstep per XCD: no workspace, the plain call."""
     import kv_cache_attention_split_amd as ispa
     torch = torch_mod()
     q = torch.empty((4680, 40, 128), dtype=torch.bfloat16, device="cuda")
     assert ispa.ispa_attn_dual_balanced_workspace(q, 9360, 9360) == 0
+    q = torch.empty((600, 2, 128), dtype=torch.bfloat16, device="cuda")
+    assert ispa.ispa_attn_dual_balanced_workspace(q, 3040, 9000) == 0
