@@ -13,6 +13,18 @@
 #include "ispa_internal.hpp"
 #include "device_common.hpp"
 
+// Wait until at most n of this wave's vector-memory operations are in flight (n < 64).
+#define ISPA_LINALG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
+// Workgroup barrier that waits for this wave's LDS operations but not for its copies in flight (those
+// are waited for explicitly before it); the empty asm statements keep memory accesses on their side.
+#define ISPA_LINALG_LDS_BARRIER()        \
+  do {                                   \
+    asm volatile("" ::: "memory");       \
+    __builtin_amdgcn_s_waitcnt(0xc07f);  \
+    __builtin_amdgcn_s_barrier();        \
+    asm volatile("" ::: "memory");       \
+  } while (0)
+
 namespace ispa {
 namespace {
 
@@ -22,6 +34,70 @@ constexpr int GT = 128;        // GEMM output tile of the wide launches (and of 
 // GEMM tile GTT x GTT, k step GK per stage; 4 waves, each a (GTT/2)^2 quarter. GTT = 128 with
 // GK = 16 for wide launches; GTT = 64 with GK = 32 when a launch has too few 128-tiles to fill the
 // chip (4x the workgroups, same staging shape).
+// Epilogue of a GEMM tile held as NBK x NBK 32x32 MFMA blocks per wave (wave (wm, wn) of a 2 x 2 grid,
+// WT x WT each): C = alpha AB + beta C, or in dot mode the tile's sum of E .* (alpha AB) (and E2 .*)
+// in fp64, written to the problem's partials at `tile`.
+template <int NBK, int WT>
+__device__ __forceinline__ void gemm_epilogue(const GemmBatch &bt, const GemmShape &sh, int p, int tile, bool diag,
+                                              int m0, int n0, int wm, int wn, int tid, f32x16 (&acc)[NBK][NBK]) {
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  if (!sh.dot) {
+    float *C = bt.C[p];
+#pragma unroll
+    for (int bi = 0; bi < NBK; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NBK; ++bj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * WT + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+          const int col = n0 + wn * WT + bj * 32 + l32;
+          if (row < sh.M && col < sh.N) {
+            float *c = C + (int64_t)row * sh.ldc + col;
+            float val = sh.alpha * acc[bi][bj][v];
+            if (sh.beta != 0.f) val = fmaf(sh.beta, *c, val);
+            *c = val;
+          }
+        }
+    return;
+  }
+  // dot epilogue: sum E .* (alpha AB) (and E2 .* (alpha AB)) over this tile in fp64
+  const float *E = bt.E[p];
+  const float *E2 = bt.E2[p];
+  const bool two = sh.dot == 2;
+  double s = 0.0, s2 = 0.0;
+#pragma unroll
+  for (int bi = 0; bi < NBK; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NBK; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * WT + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
+        const int col = n0 + wn * WT + bj * 32 + l32;
+        if (row < sh.M && col < sh.N) {
+          const double prod = (double)(sh.alpha * acc[bi][bj][v]);
+          s += (double)E[(int64_t)row * sh.lde + col] * prod;
+          if (two) s2 += (double)E2[(int64_t)row * sh.lde + col] * prod;
+        }
+      }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    s += __shfl_xor(s, off, 64);
+    s2 += __shfl_xor(s2, off, 64);
+  }
+  __shared__ double wsum[2][4];
+  if (lane == 0) {
+    wsum[0][w] = s;
+    wsum[1][w] = s2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double *part = (double *)bt.C[p];   // dot mode: C holds this problem's partial array
+    const double wgt = (sh.sym && !diag) ? 2.0 : 1.0;
+    part[tile] = wgt * (((wsum[0][0] + wsum[0][1]) + wsum[0][2]) + wsum[0][3]);
+    if (two) bt.P2[p][tile] = wgt * (((wsum[1][0] + wsum[1][1]) + wsum[1][2]) + wsum[1][3]);
+  }
+}
+
 template <int GTT, int GK>
 __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmShape sh) {
   constexpr int GST = GK + 4;    // LDS row stride (floats): rows of 16-byte reads spread over the banks
@@ -153,61 +229,160 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch bt, GemmSh
     __syncthreads();
   }
 
-  if (!sh.dot) {
-    float *C = bt.C[p];
+  gemm_epilogue<NBK, WT>(bt, sh, p, tile, ti == tj, m0, n0, wm, wn, tid, acc);
+}
+
+// ------------------------------------------------------------------------------------------------
+// GEMM with direct global -> LDS copies (global_load_lds, no staging registers) into a ring of four
+// 16-deep k stages, so that three stages are in flight while one is multiplied. 128 x 128 tiles, four
+// waves of 64 x 64 (2 x 2 blocks of v_mfma_f32_32x32x2f32), 64 KB of LDS: two workgroups per CU. Each
+// operand's stage takes the layout its copy gives: an operand whose memory rows run along k (A, or B^T)
+// lands as 128 rows of 16 k (64 B, the four 16-byte chunks of a row XOR-swizzled by row / 4) and is read
+// with 16-byte reads; one whose rows run along the output index (A^T, or B) lands as 16 rows of 128
+// (512 B) and is read with 4-byte reads, consecutive lanes on consecutive addresses. MFMA s takes
+// k = 8 hf + s from lane half hf on both operands. Needs M, N multiples of 16, K a multiple of 64 (whole
+// turns of the ring), leading dimensions multiples of 4 and 16-byte aligned operands (the host checks);
+// rows past M or N are clamped (their outputs are not stored). Tiles are ordered XCD-aware over
+// (problem, tile).
+// ------------------------------------------------------------------------------------------------
+constexpr int DlT = 128, DlK = 16, DlStage = DlT * DlK;   // tile, stage depth, floats per operand stage
+
+// one operand's share of a stage copy: 8 KB = 8 wave instructions, two per wave
+template <bool KROWS>
+struct DlCopy {
+  const float *src[2];
+};
+template <bool KROWS>
+__device__ __forceinline__ DlCopy<KROWS> dl_copy_setup(const float *base, int ld, int i0, int n_idx, int w,
+                                                        int lane) {
+  DlCopy<KROWS> c;
 #pragma unroll
-    for (int bi = 0; bi < NBK; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < NBK; ++bj)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * WT + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-          const int col = n0 + wn * WT + bj * 32 + l32;
-          if (row < sh.M && col < sh.N) {
-            float *c = C + (int64_t)row * sh.ldc + col;
-            float val = sh.alpha * acc[bi][bj][v];
-            if (sh.beta != 0.f) val = fmaf(sh.beta, *c, val);
-            *c = val;
-          }
-        }
+  for (int h = 0; h < 2; ++h) {
+    const int ii = w + 4 * h;   // instruction: 1 KB block ii of the stage
+    if constexpr (KROWS) {
+      // memory rows along k: block ii = index rows 16 ii .. +15, lane -> row 16 ii + lane / 4,
+      // stored chunk lane % 4 holding source chunk (lane % 4) ^ ((row / 4) % 4)
+      const int r = 16 * ii + (lane >> 2);
+      const int ch = (lane & 3) ^ ((r >> 2) & 3);
+      const int rc = i0 + r < n_idx ? i0 + r : n_idx - 1;
+      c.src[h] = base + (int64_t)rc * ld + 4 * ch;
+    } else {
+      // memory rows along the index: block ii = k rows 2 ii, 2 ii + 1, lane -> 4 consecutive indices
+      const int k = 2 * ii + (lane >> 5);
+      int col = i0 + 4 * (lane & 31);
+      col = col + 4 <= n_idx ? col : n_idx - 4;
+      c.src[h] = base + (int64_t)k * ld + col;
+    }
+  }
+  return c;
+}
+
+template <bool TA, bool TB>
+__global__ void __launch_bounds__(kThreads, 2) gemm_f32_dl_kernel(GemmBatch bt, GemmShape sh, int tiles) {
+  constexpr bool AK = !TA, BK = TB;   // operand memory rows along k
+  // four ring slots, each the A stage then the B stage (one array per slot: the compiler then tells a
+  // slot's reads from the copies in flight into the others and waits only where they may meet)
+  __shared__ __attribute__((aligned(1024))) float ring0[2 * DlStage], ring1[2 * DlStage], ring2[2 * DlStage],
+      ring3[2 * DlStage];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int p = lin / tiles, tile = lin % tiles;
+  const int tn = (sh.N + DlT - 1) / DlT;
+  const int ti = tile / tn, tj = tile % tn;
+  const int m0 = ti * DlT, n0 = tj * DlT;
+  if (sh.dot && sh.sym && tj > ti) {
+    if (threadIdx.x == 0) {
+      ((double *)bt.C[p])[tile] = 0.0;
+      if (sh.dot == 2) bt.P2[p][tile] = 0.0;
+    }
     return;
   }
-  // dot epilogue: sum E .* (alpha AB) (and E2 .* (alpha AB)) over this tile in fp64
-  const float *E = bt.E[p];
-  const float *E2 = bt.E2[p];
-  const bool two = sh.dot == 2;
-  double s = 0.0, s2 = 0.0;
+  if (sh.lower && n0 > m0 + DlT - 1) return;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wm = w >> 1, wn = w & 1;
+
+  // A stage: op(A)[m0 + i][k0 + k]; B stage: op(B)[k0 + k][n0 + j]
+  const DlCopy<AK> ca = dl_copy_setup<AK>(bt.A[p], sh.lda, m0, sh.M, w, lane);
+  const DlCopy<BK> cb = dl_copy_setup<BK>(bt.B[p], sh.ldb, n0, sh.N, w, lane);
+  // source advance per stage: 16 k along a row, or 16 memory rows
+  const int64_t adv_a = AK ? DlK : (int64_t)DlK * sh.lda;
+  const int64_t adv_b = BK ? DlK : (int64_t)DlK * sh.ldb;
+  auto copy_stage = [&](int st, float *slot) {
 #pragma unroll
-  for (int bi = 0; bi < NBK; ++bi)
+    for (int h = 0; h < 2; ++h) copy_to_lds<16>(ca.src[h] + st * adv_a, slot + 256 * (w + 4 * h));
 #pragma unroll
-    for (int bj = 0; bj < NBK; ++bj)
+    for (int h = 0; h < 2; ++h) copy_to_lds<16>(cb.src[h] + st * adv_b, slot + DlStage + 256 * (w + 4 * h));
+  };
+
+  // operand of block b (0, 1) of this wave for MFMA s: index wbase + 32 b + l32, k = 8 hf + s
+  auto read_ops = [&](const float *sa, const float *sb, float (&av)[2][8], float (&bv)[2][8]) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * WT + bi * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-        const int col = n0 + wn * WT + bj * 32 + l32;
-        if (row < sh.M && col < sh.N) {
-          const double prod = (double)(sh.alpha * acc[bi][bj][v]);
-          s += (double)E[(int64_t)row * sh.lde + col] * prod;
-          if (two) s2 += (double)E2[(int64_t)row * sh.lde + col] * prod;
+    for (int b = 0; b < 2; ++b) {
+      const int ia = wm * 64 + 32 * b + l32, jb = wn * 64 + 32 * b + l32;
+      if constexpr (AK) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 x = *(const f32x4 *)(sa + ia * DlK + 4 * ((2 * hf + q) ^ ((ia >> 2) & 3)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[b][4 * q + e] = x[e];
         }
-      }
+      } else {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    s += __shfl_xor(s, off, 64);
-    s2 += __shfl_xor(s2, off, 64);
+        for (int s = 0; s < 8; ++s) av[b][s] = sa[(8 * hf + s) * DlT + ia];
+      }
+      if constexpr (BK) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const f32x4 x = *(const f32x4 *)(sb + jb * DlK + 4 * ((2 * hf + q) ^ ((jb >> 2) & 3)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bv[b][4 * q + e] = x[e];
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) bv[b][s] = sb[(8 * hf + s) * DlT + jb];
+      }
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
+
+  const int nst = sh.K / DlK;
+  // stage st from slot `cur`; the slot read in the previous stage (`fill`) is refilled with st + 3. Every
+  // stage issues its four copies (past the last stage the last one again, into a slot nobody reads), so
+  // the wait is the same everywhere: the compiler then sees no branch-dependent count and adds no wait
+  // of its own before the reads.
+  auto stage = [&](int st, const float *cur, float *fill) {
+    ISPA_LINALG_WAIT_VMCNT(8);   // this wave's copies of stage st have landed (st + 1, st + 2 may fly)
+    ISPA_LINALG_LDS_BARRIER();   // everyone's; and every wave is done with the slot refilled below
+    copy_stage(st + 3 < nst ? st + 3 : nst - 1, fill);
+    float av[2][8], bv[2][8];
+    read_ops(cur, cur + DlStage, av, bv);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma_f32_32x32x2(av[bi][s], bv[bj][s], acc[bi][bj]);
+  };
+  if (nst > 0) {
+    copy_stage(0, ring0);
+    copy_stage(nst > 1 ? 1 : 0, ring1);
+    copy_stage(nst > 2 ? 2 : nst - 1, ring2);
   }
-  __shared__ double wsum[2][4];
-  if (lane == 0) {
-    wsum[0][w] = s;
-    wsum[1][w] = s2;
+  for (int st = 0; st < nst; st += 4) {
+    stage(st, ring0, ring3);
+    stage(st + 1, ring1, ring0);
+    stage(st + 2, ring2, ring1);
+    stage(st + 3, ring3, ring2);
   }
-  __syncthreads();
-  if (tid == 0) {
-    double *part = (double *)bt.C[p];   // dot mode: C holds this problem's partial array
-    const double wgt = (sh.sym && ti != tj) ? 2.0 : 1.0;
-    part[tile] = wgt * (((wsum[0][0] + wsum[0][1]) + wsum[0][2]) + wsum[0][3]);
-    if (two) bt.P2[p][tile] = wgt * (((wsum[1][0] + wsum[1][1]) + wsum[1][2]) + wsum[1][3]);
-  }
+  ISPA_LINALG_WAIT_VMCNT(0);   // no copy may land in LDS after the workgroup has ended
+  gemm_epilogue<2, 64>(bt, sh, p, tile, ti == tj, m0, n0, wm, wn, tid, acc);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -563,7 +738,26 @@ hipError_t launch_gemm_f32(const GemmBatch &b, int count, const GemmShape &sh, d
   // fewer than two 128-tiles per CU: 64-tiles (dot launches keep 128-tiles: their partial
   // count is gemm_tiles; in-place launches too, so that one workgroup owns each 128 extent)
   const int t128 = gemm_tiles(sh.M, sh.N);
-  if (!sh.dot && !sh.inplace && (int64_t)t128 * count < 512) {
+  // the direct-copy kernel: M, N in 16s, K in 64s, 16-byte rows and operands, no operand subtraction;
+  // K of at least 256 unless in place (with 8 stages of 16 the register-staged kernel, three
+  // workgroups per CU, hides the load latency better: 189 against 251 us for the largest Cholesky
+  // update at d = 1536; the in-place products with a diagonal inverse run 24 against 34 us here)
+  bool dl = !sh.sub && sh.M % 16 == 0 && sh.N % 16 == 0 && sh.K % 64 == 0 && sh.lda % 4 == 0 &&
+            sh.ldb % 4 == 0 && (sh.K >= 256 || sh.inplace) &&
+            ((int64_t)t128 * count >= 512 || sh.dot || sh.inplace);
+  for (int q = 0; q < count && dl; ++q)
+    dl = ((uintptr_t)bb.A[q] % 16 == 0) && ((uintptr_t)bb.B[q] % 16 == 0);
+  if (dl) {
+    const dim3 grid((unsigned)(t128 * count));
+    if (sh.ta == 0 && sh.tb == 0)
+      hipLaunchKernelGGL((gemm_f32_dl_kernel<false, false>), grid, dim3(kThreads), 0, s, bb, sh, t128);
+    else if (sh.ta == 0)
+      hipLaunchKernelGGL((gemm_f32_dl_kernel<false, true>), grid, dim3(kThreads), 0, s, bb, sh, t128);
+    else if (sh.tb == 0)
+      hipLaunchKernelGGL((gemm_f32_dl_kernel<true, false>), grid, dim3(kThreads), 0, s, bb, sh, t128);
+    else
+      hipLaunchKernelGGL((gemm_f32_dl_kernel<true, true>), grid, dim3(kThreads), 0, s, bb, sh, t128);
+  } else if (!sh.dot && !sh.inplace && (int64_t)t128 * count < 512) {
     dim3 grid(((sh.M + 63) / 64) * ((sh.N + 63) / 64), count);
     hipLaunchKernelGGL((gemm_f32_kernel<64, 32>), grid, dim3(kThreads), 0, s, bb, sh);
   } else {
@@ -610,10 +804,12 @@ hipError_t launch_potrf_diag(float *L, int64_t L_stride, int d, int k0, int nb, 
   const size_t shmem = 2 * (size_t)nb * (nb + 1) * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void *)potrf_diag_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        2 * 128 * 129 * (int)sizeof(float));
-    hipFuncSetAttribute((const void *)potrf_diag_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        2 * 64 * 65 * (int)sizeof(float));
+    hipError_t e = hipFuncSetAttribute((const void *)potrf_diag_kernel<128>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * 128 * 129 * (int)sizeof(float));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)potrf_diag_kernel<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              2 * 64 * 65 * (int)sizeof(float));
+    if (e != hipSuccess) return e;
     attr_set = true;
   }
   if (nb == 128)
