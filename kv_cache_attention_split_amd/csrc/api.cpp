@@ -815,26 +815,22 @@ ispa_status solve_impl(int32_t d, int32_t batch, float lambda, const float *cons
     if (er != nullptr) ISPA_TRY(launch_sumsq_tiles(Bp(0), per_f, d, cnt, term(2, p0), er->stride, s));
     ISPA_TRY(back(0, nt));
     if (er != nullptr) {
-      // eps = <W, H W> - <dW, B> - lambda ||dW||^2 with H = (F + G) - (X + X^T): H goes to the factor's
-      // region (L is no longer needed), then one product W W^T, lower tiles only, reduced against H and
-      // F in its epilogue (<F, W W^T> = ||A_full W||^2 is the reference)
+      // eps = <W, H W> - <dW, B> - lambda ||dW||^2 with H = (F + G) - (X + X^T): one product W W^T, lower
+      // tiles only, whose epilogue forms H element by element in fp64 from F, G and X (and X's mirror
+      // element) and reduces the product against H and against F (<F, W W^T> = ||A_full W||^2 is the
+      // reference)
       ISPA_TRY(launch_sumsq_tiles(Bp(0), per_f, d, cnt, term(3, p0), er->stride, s));
-      CPtrBatch f{}, x{};
-      for (int i = 0; i < cnt; ++i) {
-        f.p[i] = er->F[p0 + i];
-        x.p[i] = X[p0 + i];
-      }
-      ISPA_TRY(launch_h_form(f, x, g, Lp(0), per_f, d, cnt, s));
       GemmBatch b{};
       GemmShape sh{};
       sh.M = d; sh.N = d; sh.K = d;
       sh.lda = d; sh.ldb = d; sh.ldc = d; sh.lde = d;
-      sh.ta = 0; sh.tb = 1; sh.dot = 2; sh.sym = 1;
+      sh.ta = 0; sh.tb = 1; sh.dot = 2; sh.sym = 1; sh.hform = 1;
       sh.alpha = 1.f; sh.beta = 0.f;
       for (int i = 0; i < cnt; ++i) {
         b.A[i] = Wuse[i];
         b.B[i] = Wuse[i];
-        b.E[i] = Lp(i);
+        b.E[i] = X[p0 + i];
+        b.A2[i] = G[p0 + i];
         b.E2[i] = er->F[p0 + i];
       }
       ISPA_TRY(launch_gemm_f32(b, cnt, sh, term(0, p0), er->stride, s, term(1, p0)));

@@ -128,6 +128,7 @@ struct GemmShape {
   int lda, ldb, ldc, lde;
   int ta, tb, lower, sub, dot;
   int sym;        // dot mode with a symmetric product and E: lower tiles only, off-diagonal ones x2
+  int hform;      // dot mode: E = (E2 + A2) - (X + X^T) with X = E, formed in fp64 per element
   int inplace;    // C aliases an operand within one 128-row or 128-column extent: 128 tiles only
   float alpha, beta;
 };
@@ -176,8 +177,6 @@ hipError_t launch_sub(const CPtrBatch &a, const CPtrBatch &b, const PtrBatch &ou
                       hipStream_t s);
 hipError_t launch_copy(const CPtrBatch &in, const PtrBatch &out, int d, int count, hipStream_t s);
 // H = (F + G) - (X + X^T) elementwise (exactly symmetric when F and G are), d x d
-hipError_t launch_h_form(const CPtrBatch &F, const CPtrBatch &X, const CPtrBatch &G, float *H, int64_t H_stride,
-                         int d, int count, hipStream_t s);
 hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t s);
 
 // ------------------------------------------------------------------------------------------------

@@ -60,9 +60,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmBatch &bt, const GemmSha
         }
     return;
   }
-  // dot epilogue: sum E .* (alpha AB) (and E2 .* (alpha AB)) over this tile in fp64
+  // dot epilogue: sum E .* (alpha AB) (and E2 .* (alpha AB)) over this tile in fp64; with hform the
+  // weight is (E2 + A2) - (E + E^T) element by element
   const float *E = bt.E[p];
   const float *E2 = bt.E2[p];
+  const float *A2 = bt.A2[p];
   const bool two = sh.dot == 2;
   double s = 0.0, s2 = 0.0;
 #pragma unroll
@@ -75,8 +77,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmBatch &bt, const GemmSha
         const int col = n0 + wn * WT + bj * 32 + l32;
         if (row < sh.M && col < sh.N) {
           const double prod = (double)(sh.alpha * acc[bi][bj][v]);
-          s += (double)E[(int64_t)row * sh.lde + col] * prod;
-          if (two) s2 += (double)E2[(int64_t)row * sh.lde + col] * prod;
+          const int64_t rc = (int64_t)row * sh.lde + col;
+          double e = (double)E[rc];
+          if (sh.hform) e = ((double)E2[rc] + (double)A2[rc]) - (e + (double)E[(int64_t)col * sh.lde + row]);
+          s += e * prod;
+          if (two) s2 += (double)E2[rc] * prod;
         }
       }
 #pragma unroll
@@ -284,12 +289,29 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_f32_dl_kernel(GemmBatch bt, 
   // slot's reads from the copies in flight into the others and waits only where they may meet)
   __shared__ __attribute__((aligned(1024))) float ring0[2 * DlStage], ring1[2 * DlStage], ring2[2 * DlStage],
       ring3[2 * DlStage];
+  // the symmetric dot mode runs the lower tiles only (`tiles` = T (T + 1) / 2 per problem, T = tn),
+  // each zeroing the partial of its mirror tile; otherwise every tile of the grid (`tiles` = T_m T_n)
+  const bool tri = sh.dot && sh.sym;
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int p = lin / tiles, tile = lin % tiles;
+  const int p = lin / tiles, t = lin % tiles;
   const int tn = (sh.N + DlT - 1) / DlT;
-  const int ti = tile / tn, tj = tile % tn;
+  int ti, tj;
+  if (tri) {
+    ti = (int)((sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
+    while (ti * (ti + 1) / 2 > t) --ti;
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    tj = t - ti * (ti + 1) / 2;
+    if (ti != tj && threadIdx.x == 0) {
+      ((double *)bt.C[p])[tj * tn + ti] = 0.0;
+      if (sh.dot == 2) bt.P2[p][tj * tn + ti] = 0.0;
+    }
+  } else {
+    ti = t / tn;
+    tj = t % tn;
+  }
+  const int tile = ti * tn + tj;
   const int m0 = ti * DlT, n0 = tj * DlT;
-  if (sh.dot && sh.sym && tj > ti) {
+  if (sh.dot && sh.sym && tj > ti) {   // (not reached in the triangular grid)
     if (threadIdx.x == 0) {
       ((double *)bt.C[p])[tile] = 0.0;
       if (sh.dot == 2) bt.P2[p][tile] = 0.0;
@@ -466,7 +488,7 @@ __device__ __forceinline__ int leaf_factor(float *Sb, float *Xb, float *colbuf, 
       lbad = lbad ? lbad : j + 1;
       p = 1.f;
     }
-    const float ip = 1.f / p;
+    const float ip = __builtin_amdgcn_rcpf(p);   // v_rcp_f32 (1 ulp): the division sat on the step chain
     const float ca = (c > j) ? vc * ip : 0.f;    // A[c][j] / A[j][j] for the columns still to come
     float ylo, yhi;
     halves_pair(y[j & 15], ylo, yhi);
@@ -693,29 +715,6 @@ __global__ void __launch_bounds__(256) sumsq_tiles_kernel(const float *base, int
   if (tid == 0) part[layer * stride + tile] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
 }
 
-// H = (F + G) - (X + X^T): X^T through a 32 x 33 LDS tile. Each element's two sums are commutative, so
-// H is exactly symmetric when F and G are.
-__global__ void h_form_kernel(CPtrBatch F, CPtrBatch X, CPtrBatch G, float *Hbase, int64_t H_stride, int d) {
-  __shared__ float t[32][33];
-  const int layer = blockIdx.z;
-  const float *x = X.p[layer];
-  const int bx = blockIdx.x * 32, by = blockIdx.y * 32;   // output columns bx.., rows by..
-  const int tx = threadIdx.x, ty = threadIdx.y;           // 32 x 8
-  for (int r = ty; r < 32; r += 8) {                      // t[c][r'] = X[bx + r][by + tx] = X^T[by + tx][bx + r]
-    const int gr = bx + r, gc = by + tx;
-    if (gr < d && gc < d) t[r][tx] = x[(int64_t)gr * d + gc];
-  }
-  __syncthreads();
-  float *H = Hbase + layer * H_stride;
-  for (int r = ty; r < 32; r += 8) {
-    const int gr = by + r, gc = bx + tx;
-    if (gr < d && gc < d) {
-      const int64_t e = (int64_t)gr * d + gc;
-      H[e] = (F.p[layer][e] + G.p[layer][e]) - (x[e] + t[tx][r]);
-    }
-  }
-}
-
 inline int grid_for(int64_t n4) {
   int64_t g = (n4 + kThreads - 1) / kThreads;
   return (int)(g < 1024 ? (g < 1 ? 1 : g) : 1024);
@@ -743,20 +742,23 @@ hipError_t launch_gemm_f32(const GemmBatch &b, int count, const GemmShape &sh, d
   // workgroups per CU, hides the load latency better: 189 against 251 us for the largest Cholesky
   // update at d = 1536; the in-place products with a diagonal inverse run 24 against 34 us here)
   bool dl = !sh.sub && sh.M % 16 == 0 && sh.N % 16 == 0 && sh.K % 64 == 0 && sh.lda % 4 == 0 &&
-            sh.ldb % 4 == 0 && (sh.K >= 256 || sh.inplace) &&
+            sh.ldb % 4 == 0 && (sh.K >= 256 || sh.inplace) && (!(sh.dot && sh.sym) || sh.M == sh.N) &&
             ((int64_t)t128 * count >= 512 || sh.dot || sh.inplace);
   for (int q = 0; q < count && dl; ++q)
     dl = ((uintptr_t)bb.A[q] % 16 == 0) && ((uintptr_t)bb.B[q] % 16 == 0);
   if (dl) {
-    const dim3 grid((unsigned)(t128 * count));
+    // symmetric dot mode: lower tiles only (M = N)
+    const int tn = (sh.N + GT - 1) / GT;
+    const int tiles = (sh.dot && sh.sym) ? tn * (tn + 1) / 2 : t128;
+    const dim3 grid((unsigned)(tiles * count));
     if (sh.ta == 0 && sh.tb == 0)
-      hipLaunchKernelGGL((gemm_f32_dl_kernel<false, false>), grid, dim3(kThreads), 0, s, bb, sh, t128);
+      hipLaunchKernelGGL((gemm_f32_dl_kernel<false, false>), grid, dim3(kThreads), 0, s, bb, sh, tiles);
     else if (sh.ta == 0)
-      hipLaunchKernelGGL((gemm_f32_dl_kernel<false, true>), grid, dim3(kThreads), 0, s, bb, sh, t128);
+      hipLaunchKernelGGL((gemm_f32_dl_kernel<false, true>), grid, dim3(kThreads), 0, s, bb, sh, tiles);
     else if (sh.tb == 0)
-      hipLaunchKernelGGL((gemm_f32_dl_kernel<true, false>), grid, dim3(kThreads), 0, s, bb, sh, t128);
+      hipLaunchKernelGGL((gemm_f32_dl_kernel<true, false>), grid, dim3(kThreads), 0, s, bb, sh, tiles);
     else
-      hipLaunchKernelGGL((gemm_f32_dl_kernel<true, true>), grid, dim3(kThreads), 0, s, bb, sh, t128);
+      hipLaunchKernelGGL((gemm_f32_dl_kernel<true, true>), grid, dim3(kThreads), 0, s, bb, sh, tiles);
   } else if (!sh.dot && !sh.inplace && (int64_t)t128 * count < 512) {
     dim3 grid(((sh.M + 63) / 64) * ((sh.N + 63) / 64), count);
     hipLaunchKernelGGL((gemm_f32_kernel<64, 32>), grid, dim3(kThreads), 0, s, bb, sh);
@@ -781,14 +783,6 @@ hipError_t launch_sumsq_tiles(const float *base, int64_t layer_stride, int d, in
   if (count <= 0) return hipSuccess;
   hipLaunchKernelGGL(sumsq_tiles_kernel, dim3(gemm_tiles(d, d), count), dim3(256), 0, s, base, layer_stride, d,
                      part, stride);
-  return hipGetLastError();
-}
-
-hipError_t launch_h_form(const CPtrBatch &F, const CPtrBatch &X, const CPtrBatch &G, float *H, int64_t H_stride,
-                         int d, int count, hipStream_t s) {
-  if (count <= 0) return hipSuccess;
-  dim3 grid((d + 31) / 32, (d + 31) / 32, count);
-  hipLaunchKernelGGL(h_form_kernel, grid, dim3(32, 8), 0, s, F, X, G, H, H_stride, d);
   return hipGetLastError();
 }
 
