@@ -708,45 +708,74 @@ ispa_status solve_impl(int32_t d, int32_t batch, float lambda, const float *cons
     }
     ISPA_TRY(launch_shift_copy(g, Lp(0), per_f, d, lambda, cnt, s));
 
-    // blocked right-looking Cholesky: L L^T = G + lambda I
-    for (int k = 0; k < nt; ++k) {
-      const int k0 = k * nb;
-      ISPA_TRY(launch_potrf_diag(Lp(0), per_f, d, k0, nb, Vp(0) + k * linv_blk, per_f, info + p0, cnt, s));
-      const int rem = d - k0 - nb;
-      if (rem <= 0) continue;
-      // panel: L[k0+nb:, k0:k0+nb] = A[k0+nb:, k0:k0+nb] Linv_k^T
-      {
-        GemmBatch b{};
-        GemmShape sh{};
-        sh.M = rem; sh.N = nb; sh.K = nb;
-        sh.lda = d; sh.ldb = nb; sh.ldc = d;
-        sh.ta = 0; sh.tb = 1;
-        sh.alpha = 1.f; sh.beta = 0.f;
-        sh.inplace = 1;                        // C = A: each row's nb columns in one workgroup
-        for (int i = 0; i < cnt; ++i) {
-          float *panel = Lp(i) + (int64_t)(k0 + nb) * d + k0;
-          b.A[i] = panel;
-          b.B[i] = Vp(i) + k * linv_blk;
-          b.C[i] = panel;
-        }
-        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+    // Cholesky L L^T = G + lambda I, recursive over block columns: factor the leading half, form the
+    // panel below it (a triangular solve from the right, itself recursive: its single block columns
+    // are products with a diagonal block's inverse, in place), remove the panel's contribution from
+    // the trailing half with one lower-tile product whose depth is the whole leading half, then
+    // factor the trailing half. The same products as the block-column-by-block-column form, in fewer
+    // and deeper GEMMs. A single block is the diagonal-block kernel (factor and inverse).
+    auto panel = [&](int r0, int r1, int j) -> hipError_t {   // L[r0:r1, j] = A[r0:r1, j] Linv_j^T
+      GemmBatch b{};
+      GemmShape sh{};
+      sh.M = (r1 - r0) * nb; sh.N = nb; sh.K = nb;
+      sh.lda = d; sh.ldb = nb; sh.ldc = d;
+      sh.ta = 0; sh.tb = 1;
+      sh.alpha = 1.f; sh.beta = 0.f;
+      sh.inplace = 1;                        // C = A: each row's nb columns in one workgroup
+      for (int i = 0; i < cnt; ++i) {
+        float *pnl = Lp(i) + (int64_t)(r0 * nb) * d + j * nb;
+        b.A[i] = pnl;
+        b.B[i] = Vp(i) + j * linv_blk;
+        b.C[i] = pnl;
       }
-      // trailing update (lower tiles): A22 -= L21 L21^T
-      {
-        GemmBatch b{};
-        GemmShape sh{};
-        sh.M = rem; sh.N = rem; sh.K = nb;
-        sh.lda = d; sh.ldb = d; sh.ldc = d;
-        sh.ta = 0; sh.tb = 1; sh.lower = 1;
-        sh.alpha = -1.f; sh.beta = 1.f;
-        for (int i = 0; i < cnt; ++i) {
-          const float *panel = Lp(i) + (int64_t)(k0 + nb) * d + k0;
-          b.A[i] = panel;
-          b.B[i] = panel;
-          b.C[i] = Lp(i) + (int64_t)(k0 + nb) * d + k0 + nb;
-        }
-        ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+      return launch_gemm_f32(b, cnt, sh, nullptr, 0, s);
+    };
+    // L[r0:r1, c0:c1] = A[r0:r1, c0:c1] L[c0:c1, c0:c1]^-T, over the block columns c0 .. c1
+    std::function<hipError_t(int, int, int, int)> trsm = [&](int r0, int r1, int c0, int c1) -> hipError_t {
+      if (c1 - c0 == 1) return panel(r0, r1, c0);
+      const int cm = c0 + (c1 - c0) / 2;
+      hipError_t e = trsm(r0, r1, c0, cm);
+      if (e != hipSuccess) return e;
+      GemmBatch b{};
+      GemmShape sh{};
+      sh.M = (r1 - r0) * nb; sh.N = (c1 - cm) * nb; sh.K = (cm - c0) * nb;
+      sh.lda = d; sh.ldb = d; sh.ldc = d;
+      sh.ta = 0; sh.tb = 1;
+      sh.alpha = -1.f; sh.beta = 1.f;
+      for (int i = 0; i < cnt; ++i) {
+        b.A[i] = Lp(i) + (int64_t)(r0 * nb) * d + c0 * nb;   // L[r0:r1, c0:cm]
+        b.B[i] = Lp(i) + (int64_t)(cm * nb) * d + c0 * nb;   // L[cm:c1, c0:cm] (transposed)
+        b.C[i] = Lp(i) + (int64_t)(r0 * nb) * d + cm * nb;   // A[r0:r1, cm:c1]
       }
+      e = launch_gemm_f32(b, cnt, sh, nullptr, 0, s);
+      return e != hipSuccess ? e : trsm(r0, r1, cm, c1);
+    };
+    std::function<hipError_t(int, int)> chol = [&](int k0, int k1) -> hipError_t {
+      if (k1 - k0 == 1)
+        return launch_potrf_diag(Lp(0), per_f, d, k0 * nb, nb, Vp(0) + k0 * linv_blk, per_f, info + p0, cnt, s);
+      const int km = k0 + (k1 - k0) / 2;
+      hipError_t e = chol(k0, km);
+      if (e == hipSuccess) e = trsm(km, k1, k0, km);
+      if (e != hipSuccess) return e;
+      // trailing half: A[km:k1, km:k1] -= L[km:k1, k0:km] L[km:k1, k0:km]^T (lower tiles)
+      GemmBatch b{};
+      GemmShape sh{};
+      sh.M = (k1 - km) * nb; sh.N = sh.M; sh.K = (km - k0) * nb;
+      sh.lda = d; sh.ldb = d; sh.ldc = d;
+      sh.ta = 0; sh.tb = 1; sh.lower = 1;
+      sh.alpha = -1.f; sh.beta = 1.f;
+      for (int i = 0; i < cnt; ++i) {
+        const float *pnl = Lp(i) + (int64_t)(km * nb) * d + k0 * nb;
+        b.A[i] = pnl;
+        b.B[i] = pnl;
+        b.C[i] = Lp(i) + (int64_t)(km * nb) * d + km * nb;
+      }
+      e = launch_gemm_f32(b, cnt, sh, nullptr, 0, s);
+      return e != hipSuccess ? e : chol(km, k1);
+    };
+    {
+      const hipError_t e = chol(0, nt);
+      if (e != hipSuccess) return ISPA_E_HIP;
     }
 
     // Triangular sweeps, recursive over block rows: a range of block rows is split in two halves; the
