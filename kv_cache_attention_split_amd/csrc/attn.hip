@@ -517,6 +517,9 @@ __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel
 #define ISPA_SPLIT_MARGIN 6
 #endif
 constexpr int kSplitSlots = 4;                               // per unit
+// pieces of one workgroup: a spare range of nx L / E tiles meets at most ceil(nx / E) + 1 units, each cut at
+// most once more at the local end; the host keeps 2 (ceil(nx / E) + 1) within this table
+constexpr int kSplitMaxPieces = 72;
 constexpr size_t kSplitScal = 16 * 512 * 4;                 // floats of one stored accumulator
 constexpr size_t kSplitSlotFloats = kSplitScal + 4 * 512;
 
@@ -671,6 +674,9 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][TBV];
   __shared__ __attribute__((aligned(256))) float bbuf[2][BIAS ? BK : 1];   // bias of tiles, beside K
   __shared__ uint64_t s_merge;   // SPLIT: the units (bit k - k_lo) whose merge falls to this workgroup
+  __shared__ int4 s_piece[SPLIT ? kSplitMaxPieces : 1];   // SPLIT: this workgroup's pieces
+  __shared__ int s_npiece, s_klo, s_khi;
+  __shared__ uint64_t s_two;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -685,41 +691,53 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
 
   // SPLIT (balanced schedule, see split_geom): a main workgroup runs one piece, [0, R) of its unit; a
   // spare one walks its range of the XCD's remaining tiles piece by piece (a piece ends at a unit's end
-  // and at the local end). Otherwise one pass: the workgroup's own unit (and key range).
-  const int jw = (int)(blockIdx.x >> 3);
-  const SplitGeom sg = SPLIT ? split_geom((int)(blockIdx.x & 7), n_qt * a.n_heads, (int)(gridDim.x >> 3), nt)
-                             : SplitGeom{0, 0, 0, 0, 1, 1};
-  const bool spare = SPLIT && jw >= sg.nx;
-  int64_t seg_pos = spare ? (int64_t)(jw - sg.nx) * sg.len / sg.E : 0;
-  const int64_t seg_end = spare ? (int64_t)(jw - sg.nx + 1) * sg.len / sg.E : 1;
-  // SPLIT: the XCD's units this workgroup ran pieces of, [k_lo, k_hi], and those with two pieces here
-  // (bit k - k_lo: a range cut at the local end)
-  int k_lo = -1, k_hi = -1;
-  uint64_t two = 0;
-  while (seg_pos < seg_end) {
+  // and at the local end). Thread 0 lists the pieces (unit, first tile, end tile, slot) in LDS before
+  // the tile loops, so that the schedule's state is not held in registers across them (it spilled
+  // scalar registers inside the tile loop). Otherwise one pass: the workgroup's own unit (and key range).
+  int npiece = 1;
+  if constexpr (SPLIT) {
+    if (tid == 0) {
+      const int jw = (int)(blockIdx.x >> 3);
+      const SplitGeom sg = split_geom((int)(blockIdx.x & 7), n_qt * a.n_heads, (int)(gridDim.x >> 3), nt);
+      int n = 0, k_lo = -1, k_hi = -1;
+      uint64_t two = 0;
+      if (jw < sg.nx) {
+        s_piece[n++] = int4{sg.us + jw, 0, sg.R, kSplitSlots * (sg.us + jw)};
+        k_lo = k_hi = jw;
+      } else {
+        int64_t pos = (int64_t)(jw - sg.nx) * sg.len / sg.E;
+        const int64_t end = (int64_t)(jw - sg.nx + 1) * sg.len / sg.E;
+        while (pos < end && n < kSplitMaxPieces) {
+          const int k = (int)(pos / sg.L);
+          const int t0 = sg.R + (int)(pos - (int64_t)k * sg.L);
+          const int64_t e = end - (int64_t)k * sg.L;
+          int t1 = sg.R + e < nt ? (int)(sg.R + e) : nt;
+          if (t0 < nt_loc && nt_loc < t1) t1 = nt_loc;
+          const UnitCuts cu = unit_cuts(sg, k, nt, nt_loc);
+          const int slot = kSplitSlots * (sg.us + k) + 1 + (cu.n >= 1 && cu.c0 <= t0) + (cu.n == 2 && cu.c1 <= t0);
+          s_piece[n++] = int4{sg.us + k, t0, t1, slot};
+          pos = (int64_t)k * sg.L + (t1 - sg.R);
+          if (k_lo < 0) k_lo = k;
+          if (k == k_hi) two |= 1ull << (k - k_lo);
+          k_hi = k;
+        }
+      }
+      s_npiece = n;
+      s_klo = k_lo;
+      s_khi = k_hi;
+      s_two = two;
+    }
+    __syncthreads();
+    npiece = s_npiece;
+  }
+  for (int pi = 0; pi < npiece; ++pi) {
   int vid, split = 0, t0, t1, slot = 0;
   if constexpr (SPLIT) {
-    if (!spare) {
-      vid = sg.us + jw;
-      t0 = 0;
-      t1 = sg.R;
-      slot = kSplitSlots * vid;
-      seg_pos = seg_end;
-      k_lo = k_hi = jw;
-    } else {
-      const int k = (int)(seg_pos / sg.L);
-      vid = sg.us + k;
-      t0 = sg.R + (int)(seg_pos - (int64_t)k * sg.L);
-      const int64_t e = seg_end - (int64_t)k * sg.L;
-      t1 = sg.R + e < nt ? (int)(sg.R + e) : nt;
-      if (t0 < nt_loc && nt_loc < t1) t1 = nt_loc;
-      const UnitCuts cu = unit_cuts(sg, k, nt, nt_loc);
-      slot = kSplitSlots * vid + 1 + (cu.n >= 1 && cu.c0 <= t0) + (cu.n == 2 && cu.c1 <= t0);
-      seg_pos = (int64_t)k * sg.L + (t1 - sg.R);
-      if (k_lo < 0) k_lo = k;
-      if (k == k_hi) two |= 1ull << (k - k_lo);
-      k_hi = k;
-    }
+    const int4 pc = s_piece[pi];
+    vid = pc.x;
+    t0 = pc.y;
+    t1 = pc.z;
+    slot = pc.w;
   } else {
     const int lin = xcd_remap(blockIdx.x, n_qt * a.n_heads * nsplit);
     vid = lin / nsplit;
@@ -727,7 +745,6 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     // tiles of this workgroup: all of them, or one contiguous range per split in the LSE-only form
     t0 = LSE_ONLY ? (int)((int64_t)split * nt / nsplit) : 0;
     t1 = LSE_ONLY ? (int)((int64_t)(split + 1) * nt / nsplit) : nt;
-    seg_pos = seg_end;
   }
   const int head = vid / n_qt, qt = vid % n_qt;
   const int head_off = head * D;
@@ -1119,8 +1136,15 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     slot_ws[kSplitScal + 512 + tid] = l;
     slot_ws[kSplitScal + 2 * 512 + tid] = l_loc;
   }
-  }   // segments
+  }   // pieces
   if constexpr (SPLIT) {
+    // the XCD's geometry again, from an opaque copy of the workgroup id (the first one is not kept live
+    // across the tile loops), and the touched units from LDS
+    int xw = (int)blockIdx.x;
+    asm volatile("" : "+s"(xw));
+    const SplitGeom sg = split_geom(xw & 7, n_qt * a.n_heads, (int)(gridDim.x >> 3), nt);
+    const int k_lo = s_klo, k_hi = s_khi;
+    const uint64_t two = s_two;
     // Every wave's stores complete in L2; then wave 0 makes them visible at agent scope with one release
     // (a write-back of the XCD's L2; a sequentially consistent fence would also invalidate it, dropping
     // the K/V tiles the XCD's other workgroups are reading) and counts each unit's pieces, one lane per
@@ -1336,6 +1360,9 @@ int attn_balanced_grid(int64_t n_q, int n_heads, int64_t n_keys_loc, int64_t n_k
   // at least as many main workgroups as spare ones (a unit's remaining tiles then meet at most one
   // spare-range boundary); one bit per unit of an XCD in a 64-bit mask
   if (units * 10 >= (int64_t)cus * 9 || nx_max >= S || 2 * nx_min < S || S > 64) return 0;
+  // the pieces of a spare workgroup fit its table
+  const int64_t e_min = S - nx_max;
+  if (2 * ((nx_max + e_min - 1) / e_min + 1) > kSplitMaxPieces) return 0;
   return cus;
 }
 
