@@ -751,7 +751,9 @@ def main():
     a_loc = [torch.empty((n_q, d), dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
     a_full = [torch.empty_like(x) for x in a_loc]
     lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
-    stats = [[torch.zeros((d, d), dtype=torch.float32, device="cuda") for _ in range(3)] for _ in range(n_layers)]
+    # every layer's G, X, F in one allocation, so that the warmup's start clears them with one fill
+    stats_all = torch.zeros((n_layers, 3, d, d), dtype=torch.float32, device="cuda")
+    stats = [[stats_all[li, j] for j in range(3)] for li in range(n_layers)]
     dW = [torch.empty((d, d), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
     info = torch.zeros((n_layers,), dtype=torch.int32, device="cuda")
     eps = torch.zeros((n_layers,), dtype=torch.float64, device="cuda")
@@ -775,9 +777,7 @@ def main():
     timing = {"attn": [], "stats": [], "solve": []}
 
     def step(record: bool):
-        for s in stats:
-            for t in s:
-                t.zero_()
+        stats_all.zero_()
         for c, ch in enumerate(wl.chunks):
             for li, L in enumerate(layers):
                 sk, sv = L.seg(ch.sink)

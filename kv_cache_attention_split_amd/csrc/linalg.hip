@@ -738,11 +738,13 @@ hipError_t launch_gemm_f32(const GemmBatch &b, int count, const GemmShape &sh, d
   // count is gemm_tiles; in-place launches too, so that one workgroup owns each 128 extent)
   const int t128 = gemm_tiles(sh.M, sh.N);
   // the direct-copy kernel: M, N in 16s, K in 64s, 16-byte rows and operands, no operand subtraction;
-  // K of at least 256 unless in place (with 8 stages of 16 the register-staged kernel, three
-  // workgroups per CU, hides the load latency better: 189 against 251 us for the largest Cholesky
-  // update at d = 1536; the in-place products with a diagonal inverse run 24 against 34 us here)
+  // lower-tile products only with K of at least 256 (with 8 stages of 16 and half the workgroups
+  // returning at once, the register-staged kernel, three workgroups per CU, hides the load latency
+  // better: 189 against 251 us for the largest K = 128 Cholesky update at d = 1536; full-tile K = 128
+  // products, such as the sweeps' short splits, run faster here: solve 0.2435 against 0.2478 ms per
+  // layer, and the in-place products with a diagonal inverse 24 against 34 us)
   bool dl = !sh.sub && sh.M % 16 == 0 && sh.N % 16 == 0 && sh.K % 64 == 0 && sh.lda % 4 == 0 &&
-            sh.ldb % 4 == 0 && (sh.K >= 256 || sh.inplace) && (!(sh.dot && sh.sym) || sh.M == sh.N) &&
+            sh.ldb % 4 == 0 && (sh.K >= 256 || sh.inplace || !sh.lower) && (!(sh.dot && sh.sym) || sh.M == sh.N) &&
             ((int64_t)t128 * count >= 512 || sh.dot || sh.inplace);
   for (int q = 0; q < count && dl; ++q)
     dl = ((uintptr_t)bb.A[q] % 16 == 0) && ((uintptr_t)bb.B[q] % 16 == 0);
