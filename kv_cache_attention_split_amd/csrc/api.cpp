@@ -642,6 +642,43 @@ struct EpsRequest {
   int64_t stride;
 };
 
+// A second stream per device for work that runs beside the caller's stream inside one call (created
+// once, default priority, non-blocking; the call forks to it and joins back through events).
+hipError_t side_stream(hipStream_t *out) {
+  static std::mutex mu;
+  static std::vector<hipStream_t> streams;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)streams.size() <= dev) streams.resize(dev + 1, nullptr);
+  if (streams[dev] == nullptr) {
+    e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      streams[dev] = nullptr;
+      return e;
+    }
+  }
+  *out = streams[dev];
+  return hipSuccess;
+}
+// Two events of one call (no timing), destroyed when the call returns (a recorded event may be
+// destroyed before it completes).
+struct EventPair {
+  hipEvent_t e[2] = {nullptr, nullptr};
+  hipError_t create() {
+    for (auto &x : e) {
+      const hipError_t r = hipEventCreateWithFlags(&x, hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+  ~EventPair() {
+    for (auto &x : e)
+      if (x != nullptr) (void)hipEventDestroy(x);
+  }
+};
+
 ispa_status solve_impl(int32_t d, int32_t batch, float lambda, const float *const *G, const float *const *X,
                        const float *const *W, int32_t w_is_linear_weight, float *const *dW, int32_t *info,
                        void *ws, const EpsRequest *er, hipStream_t s) {
@@ -654,6 +691,13 @@ ispa_status solve_impl(int32_t d, int32_t batch, float lambda, const float *cons
 
   const int tiles = gemm_tiles(d, d);
   auto term = [&](int g, int layer) { return er->part + ((int64_t)g * batch + layer) * er->stride; };
+  // the error at the optimum runs on a second stream of this device (fork and join through events)
+  hipStream_t side = nullptr;
+  EventPair ev;
+  if (er != nullptr) {
+    if (side_stream(&side) != hipSuccess || ev.create() != hipSuccess) return ISPA_E_HIP;
+  }
+  hipEvent_t side_ready = ev.e[0], side_done = ev.e[1];
   for (int p0 = 0; p0 < batch; p0 += kMaxBatch) {
     const int cnt = std::min(batch - p0, kMaxBatch);
     float *base = (float *)ws + (int64_t)p0 * per_f;
@@ -705,6 +749,30 @@ ispa_status solve_impl(int32_t d, int32_t batch, float lambda, const float *cons
         b.C[i] = Bp(i);
       }
       ISPA_TRY(launch_gemm_f32(b, cnt, sh, nullptr, 0, s));
+    }
+    if (er != nullptr) {
+      // eps = <W, H W> - <dW, B> - lambda ||dW||^2 with H = (F + G) - (X + X^T): one product W W^T, lower
+      // tiles only, whose epilogue forms H element by element in fp64 from F, G and X (and X's mirror
+      // element) and reduces the product against H and against F (<F, W W^T> = ||A_full W||^2 is the
+      // reference). It depends on W and the statistics only, so it runs on a second stream beside the
+      // factorisation (whose diagonal blocks occupy 30 workgroups), joined before the reduction.
+      ISPA_TRY(hipEventRecord(side_ready, s));
+      ISPA_TRY(hipStreamWaitEvent(side, side_ready, 0));
+      GemmBatch b{};
+      GemmShape sh{};
+      sh.M = d; sh.N = d; sh.K = d;
+      sh.lda = d; sh.ldb = d; sh.ldc = d; sh.lde = d;
+      sh.ta = 0; sh.tb = 1; sh.dot = 2; sh.sym = 1; sh.hform = 1;
+      sh.alpha = 1.f; sh.beta = 0.f;
+      for (int i = 0; i < cnt; ++i) {
+        b.A[i] = Wuse[i];
+        b.B[i] = Wuse[i];
+        b.E[i] = X[p0 + i];
+        b.A2[i] = G[p0 + i];
+        b.E2[i] = er->F[p0 + i];
+      }
+      ISPA_TRY(launch_gemm_f32(b, cnt, sh, term(0, p0), er->stride, side, term(1, p0)));
+      ISPA_TRY(hipEventRecord(side_done, side));
     }
     ISPA_TRY(launch_shift_copy(g, Lp(0), per_f, d, lambda, cnt, s));
 
@@ -844,25 +912,9 @@ ispa_status solve_impl(int32_t d, int32_t batch, float lambda, const float *cons
     if (er != nullptr) ISPA_TRY(launch_sumsq_tiles(Bp(0), per_f, d, cnt, term(2, p0), er->stride, s));
     ISPA_TRY(back(0, nt));
     if (er != nullptr) {
-      // eps = <W, H W> - <dW, B> - lambda ||dW||^2 with H = (F + G) - (X + X^T): one product W W^T, lower
-      // tiles only, whose epilogue forms H element by element in fp64 from F, G and X (and X's mirror
-      // element) and reduces the product against H and against F (<F, W W^T> = ||A_full W||^2 is the
-      // reference)
       ISPA_TRY(launch_sumsq_tiles(Bp(0), per_f, d, cnt, term(3, p0), er->stride, s));
-      GemmBatch b{};
-      GemmShape sh{};
-      sh.M = d; sh.N = d; sh.K = d;
-      sh.lda = d; sh.ldb = d; sh.ldc = d; sh.lde = d;
-      sh.ta = 0; sh.tb = 1; sh.dot = 2; sh.sym = 1; sh.hform = 1;
-      sh.alpha = 1.f; sh.beta = 0.f;
-      for (int i = 0; i < cnt; ++i) {
-        b.A[i] = Wuse[i];
-        b.B[i] = Wuse[i];
-        b.E[i] = X[p0 + i];
-        b.A2[i] = G[p0 + i];
-        b.E2[i] = er->F[p0 + i];
-      }
-      ISPA_TRY(launch_gemm_f32(b, cnt, sh, term(0, p0), er->stride, s, term(1, p0)));
+      // the error product ran beside the factorisation: its partials are complete before the reduction
+      ISPA_TRY(hipStreamWaitEvent(s, side_done, 0));
     }
     // dW in the caller's orientation
     CPtrBatch in{};
