@@ -82,6 +82,25 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef int s32x2 __attribute__((ext_vector_type(2)));
 
+// Tile of BK keys from key j0 of a run, when it lies whole inside one of the run's two pointers: its
+// base (`tb`, with the head's column offset) and row stride (`st`, elements). Each lane's 64-bit
+// source address is then the tile base plus its row and chunk offset; rows (< BK) and strides
+// (< 2^23 elements) both fit in 24 bits, so the offset is one full-rate 24-bit multiply (exact: the
+// product is below 2^29). Returns false for a tile that crosses the sink/current boundary or the
+// run's end (those copies clamp per lane).
+template <int BK, bool VALUE>
+__device__ __forceinline__ bool tile_plan(const SegRun &run, int64_t j0, int head_off, const uint16_t *&tb,
+                                          uint32_t &st) {
+  const int64_t j1 = j0 + BK;
+  const bool in_first = j1 <= run.split && j1 <= run.n;
+  const bool in_second = j0 >= run.split && j1 <= run.n;
+  const uint16_t *base0 = VALUE ? run.v0 : run.k0;
+  const uint16_t *base1 = VALUE ? run.v1 : run.k1;
+  tb = (in_first ? base0 + j0 * run.s0 : base1 + (j0 - run.split) * run.s1) + head_off;
+  st = (uint32_t)(in_first ? run.s0 : run.s1);
+  return in_first || in_second;
+}
+
 // Stage one K or V tile (BK rows) into LDS with direct global->LDS loads: each wave instruction
 // fills 1 KiB (1024 / (2D) rows); lane l writes LDS position base + 16 l, so it fetches the global
 // chunk that the swizzle assigns to that position. The per-lane (row, chunk) of each of the wave's
@@ -91,22 +110,16 @@ __device__ __forceinline__ void dma_tile(const SegRun &run, int64_t j0, int head
                                          int w, const int (&rr)[BK * D * 2 / 4096],
                                          const int (&cc8)[BK * D * 2 / 4096]) {
   constexpr int NW = BK * D * 2 / 4096;     // instructions per wave per tile
-  const int64_t j1 = j0 + BK;
-  const bool in_first = j1 <= run.split && j1 <= run.n;
-  const bool in_second = j0 >= run.split && j1 <= run.n;
-  const uint16_t *base0 = VALUE ? run.v0 : run.k0;
-  const uint16_t *base1 = VALUE ? run.v1 : run.k1;
-  if (in_first || in_second) {
-    // whole tile inside one sub-run: no clamping; each lane's 64-bit address is the tile base plus
-    // its row and chunk offset. Rows (< BK) and strides (< 2^23 elements) both fit in 24 bits, so the
-    // offset is one full-rate 24-bit multiply (exact: the product is below 2^29)
-    const uint16_t *tb = (in_first ? base0 + j0 * run.s0 : base1 + (j0 - run.split) * run.s1) + head_off;
-    const uint32_t st = (uint32_t)(in_first ? run.s0 : run.s1);
+  const uint16_t *tb;
+  uint32_t st;
+  if (tile_plan<BK, VALUE>(run, j0, head_off, tb, st)) {
 #pragma unroll
     for (int ii = 0; ii < NW; ++ii)
       copy_to_lds<16>(tb + (__umul24((uint32_t)rr[ii], st) + (uint32_t)cc8[ii]), lds_tile + 1024 * (w + 4 * ii));
     return;
   }
+  const uint16_t *base0 = VALUE ? run.v0 : run.k0;
+  const uint16_t *base1 = VALUE ? run.v1 : run.k1;
 #pragma unroll
   for (int ii = 0; ii < NW; ++ii) {
     int64_t j = j0 + rr[ii];
@@ -217,6 +230,9 @@ __device__ __forceinline__ void write_lse(float *out, float val, int head, int q
 #endif
 #ifndef ISPA_ATTN_VCOPY_VEC
 #define ISPA_ATTN_VCOPY_VEC 1   // ping-pong kernel, bf16 values: value copies in the vector phase
+#endif
+#ifndef ISPA_ATTN_VCOPY_B
+#define ISPA_ATTN_VCOPY_B 1     // ping-pong kernel, bf16 values: group B copies the values
 #endif
 
 template <int D, bool BIAS>
@@ -664,6 +680,11 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   constexpr int TBV = FP8V ? BK * D : TB;    // bytes of a value tile
   // where group A issues the value copies: beside the softmax where the matrix phase is the longer one
   constexpr bool VCOPY_VEC = !LSE_ONLY && !FP8V && ISPA_ATTN_VCOPY_VEC;
+  // bf16 values: group B copies V(i+1) at the start of its vector phase of tile i, beside group A's
+  // matrix phase i+1. Issuing a 1 KiB global->LDS copy holds a wave for about 40 cycles, more while
+  // other copies are in flight, so the copies go to the phases with slack: B's softmax is shorter than A's
+  // matrix phase plus A's key copies, and A's vector phase then carries no copies at all
+  constexpr bool VCOPY_B = !LSE_ONLY && !FP8V && ISPA_ATTN_VCOPY_B;
   constexpr int NKK = D / 16;
   constexpr int NK8 = D / 64;                // e4m3 k-steps
   constexpr int NDB = D / 32;
@@ -679,7 +700,8 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   __shared__ uint64_t s_two;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  // the wave index as a uniform value (group branches and LDS bases stay scalar)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int grp = w >> 2, wl = w & 3;
   const int n_q = a.n_q;
   const int out_stride = a.n_heads * D;
@@ -907,6 +929,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   // prologue: K(t0) for everyone; group B then falls one barrier behind
   if (grp == 0) {
     if (!LSE_ONLY || t0 < t1) dma_k(t0, t0 & 1);
+    if (VCOPY_B && t0 < t1) dma_v(t0, t0 & 1);   // group B copies the later value tiles
     if (BIAS && wl == 0) dma_b(t0, t0 & 1);
     ISPA_WAIT_VMCNT(0);
   }
@@ -1019,10 +1042,15 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
         dma_k(i + 1, (i + 1) & 1);
         if (BIAS && wl == 0) dma_b(i + 1, (i + 1) & 1);
       }
-      if (!VCOPY_VEC && !LSE_ONLY && i < t1) dma_v(i, i & 1);
+      if (!VCOPY_B && !VCOPY_VEC && !LSE_ONLY && i < t1) dma_v(i, i & 1);
     }
+    // VCOPY_B: group B's copies of V(i) (issued in its vector phase of tile i-1) land before group A's
+    // matrix phase i+1 reads them
+    if (VCOPY_B && grp == 1) ISPA_WAIT_VMCNT(0);
     ISPA_LDS_BARRIER();
-    if (VCOPY_VEC && grp == 0 && i < t1) dma_v(i, i & 1);
+    if (!VCOPY_B && VCOPY_VEC && grp == 0 && i < t1) dma_v(i, i & 1);
+    // V(i+1) goes to the buffer of V(i-1), which both groups finished reading in their matrix phases i
+    if (VCOPY_B && grp == 1 && i + 1 < t1) dma_v(i + 1, (i + 1) & 1);
     // ---- vector phase: softmax of tile i ----
     // accumulator holds tiles 0 .. nt_loc-1: the local keys end here (a piece that begins later inside
     // the local keys ends at their end, and its state is merged)
@@ -1106,9 +1134,9 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
       }
       l += sum;
     }
-    // this step's copies (K(i+1), V(i)) have landed; executed by both groups (a no-op for B) so that
-    // no path enters the next matrix phase with a copy pending
-    ISPA_WAIT_VMCNT(0);
+    // this step's copies of group A (K(i+1), and V(i) unless group B copies the values) have landed;
+    // group B waits for its value copies at the end of its next matrix phase instead
+    if (!VCOPY_B || grp == 0) ISPA_WAIT_VMCNT(0);
     ISPA_LDS_BARRIER();
   }
   if (grp == 0) ISPA_LDS_BARRIER();     // matches group B's extra prologue barrier
