@@ -109,8 +109,8 @@ class Layer:
 # rocprofv3 FETCH_SIZE x 1.9997 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
 # attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only
 # while the source is unchanged.
-ATTN_TRAFFIC = {"sha256": "2ebc04ce4fbd30bb2349995b052edc3da921d918798c2fe6f816f0559610b8c0",
-                "bytes_per_launch": 157818715}
+ATTN_TRAFFIC = {"sha256": "7ff5a528f1dc3ff3767e58f24f231ea72ca1d7723ff134769df6856342bc2505",
+                "bytes_per_launch": 157859059}
 
 
 def attn_traffic():
