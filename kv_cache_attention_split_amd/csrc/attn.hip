@@ -232,7 +232,7 @@ __device__ __forceinline__ void write_lse(float *out, float val, int head, int q
 #define ISPA_ATTN_VCOPY_VEC 1   // ping-pong kernel, bf16 values: value copies in the vector phase
 #endif
 #ifndef ISPA_ATTN_VCOPY_B
-#define ISPA_ATTN_VCOPY_B 1     // ping-pong kernel, bf16 values: group B copies the values
+#define ISPA_ATTN_VCOPY_B 1     // ping-pong kernel with value products: group B copies the values
 #endif
 
 template <int D, bool BIAS>
@@ -680,11 +680,11 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   constexpr int TBV = FP8V ? BK * D : TB;    // bytes of a value tile
   // where group A issues the value copies: beside the softmax where the matrix phase is the longer one
   constexpr bool VCOPY_VEC = !LSE_ONLY && !FP8V && ISPA_ATTN_VCOPY_VEC;
-  // bf16 values: group B copies V(i+1) at the start of its vector phase of tile i, beside group A's
+  // bf16 or e4m3 values: group B copies V(i+1) at the start of its vector phase of tile i, beside group A's
   // matrix phase i+1. Issuing a 1 KiB global->LDS copy holds a wave for about 40 cycles, more while
   // other copies are in flight, so the copies go to the phases with slack: B's softmax is shorter than A's
   // matrix phase plus A's key copies, and A's vector phase then carries no copies at all
-  constexpr bool VCOPY_B = !LSE_ONLY && !FP8V && ISPA_ATTN_VCOPY_B;
+  constexpr bool VCOPY_B = !LSE_ONLY && ISPA_ATTN_VCOPY_B;
   constexpr int NKK = D / 16;
   constexpr int NK8 = D / 64;                // e4m3 k-steps
   constexpr int NDB = D / 32;
