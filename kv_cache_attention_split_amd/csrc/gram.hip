@@ -282,15 +282,24 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
 // the 128 x 128 kernel (32 rows x 128 columns, chunk c of row r at c ^ 4 (r mod 4)): A columns i0..,
 // i0+128.., B columns j0.., j0+128..; wave (wm, wn) reads half-panels wm and 2 + wn only.
 // ---------------------------------------------------------------------------------------------
+#ifndef ISPA_GRAM_WAVES
+#define ISPA_GRAM_WAVES 8   // waves of the 256 x 256 tile kernel: 4 (128 x 128 each) or 8 (128 x 64 each)
+#endif
 constexpr int BTW = 256;                      // output tile
 constexpr int kStageW = 4 * kPart;            // 32 KB
-constexpr int kCopiesW = kStageW / 1024 / 4;  // 8 copy instructions per wave per stage
 
+template <int BJ>
 struct HalfOpsW {
-  bf16x8 a[4], b[4];   // one 16-row step: [32-column block]
+  bf16x8 a[4], b[BJ];   // one 16-row step: [32-column block]
 };
 
-__global__ void __launch_bounds__(kThreads, 1) gram_bf16_wide_kernel(GramArgs g) {
+// NWV = 4: waves of 128 x 128 (one wave per SIMD); NWV = 8: waves of 128 x 64 (two per SIMD, so that one
+// wave's MFMAs run while the other is held issuing its global->LDS copies, which take tens to hundreds of
+// cycles each and otherwise leave the matrix core idle)
+template <int NWV>
+__global__ void __launch_bounds__(64 * NWV, 1) gram_bf16_wide_kernel(GramArgs g) {
+  constexpr int BJ = NWV == 8 ? 2 : 4;               // 32-column blocks of a wave
+  constexpr int kCW = kStageW / 1024 / NWV;          // copy instructions per wave per stage
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageW];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageW];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageW];
@@ -298,7 +307,9 @@ __global__ void __launch_bounds__(kThreads, 1) gram_bf16_wide_kernel(GramArgs g)
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = NWV == 8 ? w >> 2 : w >> 1, wn = NWV == 8 ? w & 3 : w & 1;
+  // the wave's B half-panel and its first column in it
+  const int bpart = NWV == 8 ? 2 + (wn >> 1) : 2 + wn, bcol = NWV == 8 ? 64 * (wn & 1) : 0;
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int layer = lin / g.tiles;
@@ -327,11 +338,11 @@ __global__ void __launch_bounds__(kThreads, 1) gram_bf16_wide_kernel(GramArgs g)
   // Copy instruction ii of wave w fills 1 KB block blk = w + 4 ii of a stage: half-panel blk / 8, rows
   // 4 (blk mod 8) .. +3; lane l lands at row 4 (blk mod 8) + l / 16, stored chunk l mod 16, which holds
   // source chunk (l mod 16) ^ (4 (l / 16)). Columns past d are clamped (their outputs are not stored).
-  const uint8_t *src[kCopiesW];
-  int crow[kCopiesW];
+  const uint8_t *src[kCW];
+  int crow[kCW];
 #pragma unroll
-  for (int ii = 0; ii < kCopiesW; ++ii) {
-    const int blk = w + 4 * ii;
+  for (int ii = 0; ii < kCW; ++ii) {
+    const int blk = w + NWV * ii;
     const int part = blk >> 3;
     const int r = 4 * (blk & 7) + (lane >> 4);
     const int c = (lane & 15) ^ (4 * (lane >> 4));
@@ -348,66 +359,75 @@ __global__ void __launch_bounds__(kThreads, 1) gram_bf16_wide_kernel(GramArgs g)
   // reaches past the last row selects the zero block per lane.
   auto copy_stage = [&](auto full, int s, uint8_t *slot) {
 #pragma unroll
-    for (int ii = 0; ii < kCopiesW; ++ii) {
+    for (int ii = 0; ii < kCW; ++ii) {
       const uint8_t *p = src[ii] + (int64_t)s * stage_bytes;
       if constexpr (!decltype(full)::value) {
         const int64_t n = (int64_t)s * BR + crow[ii];
         p = n < n_rows ? p : (const uint8_t *)(uintptr_t)zero_row;
       }
-      copy_to_lds<16>(p, slot + 1024 * (w + 4 * ii));
+      copy_to_lds<16>(p, slot + 1024 * (w + NWV * ii));
     }
   };
-  auto read_half = [&](const uint8_t *slot, int t, HalfOpsW &o) {
+  auto read_half = [&](const uint8_t *slot, int t, HalfOpsW<BJ> &o) {
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) o.a[bi] = read_operand(slot + kPart * wm, bi * 32, 16 * t, lane);
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) o.b[bj] = read_operand(slot + kPart * (2 + wn), bj * 32, 16 * t, lane);
+    for (int bj = 0; bj < BJ; ++bj) o.b[bj] = read_operand(slot + kPart * bpart, bcol + bj * 32, 16 * t, lane);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][BJ];
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj)
+    for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
-  auto mma = [&](const HalfOpsW &o) {
+  if constexpr (NWV == 8) {
+    // two waves per SIMD share 512 registers: the accumulators are pinned to AGPRs, which leaves the
+    // VGPRs to the operands and addresses (left to itself the compiler kept all in VGPRs and spilled)
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mfma_bf16_32x32x16(o.a[bi], o.b[bj], acc[bi][bj]);
+      for (int bj = 0; bj < BJ; ++bj) asm volatile("" : "+a"(acc[bi][bj]));
+  }
+  auto mma = [&](const HalfOpsW<BJ> &o) {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < BJ; ++bj) acc[bi][bj] = mfma_bf16_32x32x16(o.a[bi], o.b[bj], acc[bi][bj]);
   };
+  constexpr int M = 4 * BJ;          // MFMAs per half-stage
+  constexpr int R = 2 * (4 + BJ);    // operand reads per half-stage (two per operand)
 
   // Stage s, pipelined by half-stage (16 rows): the first half's operands are in registers (h0); the
   // second half is read while the first is multiplied; then, once every wave is done with the slot and
   // this wave's copies of stage s+1 have landed, the slot is refilled with stage s+4 and the first half
   // of stage s+1 is read while the second half of stage s is multiplied.
-  HalfOpsW h0, h1;
+  HalfOpsW<BJ> h0, h1;
   auto stage = [&](auto full, int s, uint8_t *cur, const uint8_t *nxt) {
     read_half(cur, 1, h1);
     mma(h0);
-    // one MFMA first (the wait for h0's reads then precedes h1's reads), h1's reads within the next
-    // eight MFMAs, and seven MFMAs left to cover their latency before the barrier's wait
+    // one MFMA first (the wait for h0's reads then precedes h1's reads), h1's reads two per MFMA, and
+    // the remaining MFMAs to cover their latency before the barrier's wait
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 7, 0);
-    ISPA_GRAM_WAIT_VMCNT(kCopiesW * (NS - 2));   // this wave's copies of stage s+1 have landed
-    ISPA_GRAM_LDS_BARRIER();                     // ... everyone's; all reads of stage s are done
+    __builtin_amdgcn_sched_group_barrier(0x008, M - 1 - R / 2, 0);
+    ISPA_GRAM_WAIT_VMCNT(kCW * (NS - 2));   // this wave's copies of stage s+1 have landed
+    ISPA_GRAM_LDS_BARRIER();                // ... everyone's; all reads of stage s are done
     copy_stage(full, s + NS, cur);
     read_half(nxt, 0, h0);
     mma(h1);
-    // one copy and one operand (two reads) per MFMA over the first eight, then seven MFMAs
+    // per MFMA: one copy while copies remain, two operand reads while reads remain
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < M; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i < kCW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i < R / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   using full_t = std::integral_constant<bool, true>;
@@ -416,7 +436,7 @@ __global__ void __launch_bounds__(kThreads, 1) gram_bf16_wide_kernel(GramArgs g)
   copy_stage(part_t{}, 1, ring1);
   copy_stage(part_t{}, 2, ring2);
   copy_stage(part_t{}, 3, ring3);
-  ISPA_GRAM_WAIT_VMCNT(kCopiesW * (NS - 1));
+  ISPA_GRAM_WAIT_VMCNT(kCW * (NS - 1));
   ISPA_GRAM_LDS_BARRIER();
   read_half(ring0, 0, h0);
   // turns of the ring whose refills (stages s + 4 .. s + 7) hold only existing rows, then the rest
@@ -441,8 +461,8 @@ __global__ void __launch_bounds__(kThreads, 1) gram_bf16_wide_kernel(GramArgs g)
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-      const int cl = j0 + wn * 128 + bj * 32 + l32;
+    for (int bj = 0; bj < BJ; ++bj) {
+      const int cl = j0 + 128 * (bpart - 2) + bcol + bj * 32 + l32;
       const int clc = cl < d ? cl : d - 1;
       float cur[16];
 #pragma unroll
@@ -461,8 +481,8 @@ __global__ void __launch_bounds__(kThreads, 1) gram_bf16_wide_kernel(GramArgs g)
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) {
-        const int mr = j0 + wn * 128 + bj * 32 + l32;
+      for (int bj = 0; bj < BJ; ++bj) {
+        const int mr = j0 + 128 * (bpart - 2) + bcol + bj * 32 + l32;
         const int mrc = mr < d ? mr : d - 1;
         f32x4 cur[4];
 #pragma unroll
@@ -759,7 +779,10 @@ hipError_t launch_gram_bf16_batch(int64_t n_rows, int d, int batch, const uint16
     g.tiles = gram_tiles(d, bt, with_f);
     const dim3 grid((unsigned)(g.tiles * cnt));
     if (wide)
-      hipLaunchKernelGGL(gram_bf16_wide_kernel, grid, dim3(kThreads), 0, s, g);
+      if (ISPA_GRAM_WAVES == 8)
+        hipLaunchKernelGGL(gram_bf16_wide_kernel<8>, grid, dim3(512), 0, s, g);
+      else
+        hipLaunchKernelGGL(gram_bf16_wide_kernel<4>, grid, dim3(256), 0, s, g);
     else
       hipLaunchKernelGGL(gram_bf16_kernel, grid, dim3(kThreads), 0, s, g);
     const hipError_t e = hipGetLastError();
