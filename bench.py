@@ -3,9 +3,12 @@
 
 One step = one full ISPA warmup of a Wan-1.3B-shaped model (workload "wan1.3b-warmup"): for each of
 the 4 chunks (4680 queries of a 3-frame chunk, history growing 0 -> 9 frames), the dual-stream
-attention of each of the 30 layers (12 heads x 128) into that layer's A_loc / A_full, then the
-warmup-statistics update of all 30 layers in one batched call; after the last chunk one batched ridge
-solve of all layers (d = 1536, lambda = 1e-2) with each layer's reconstruction error at its optimum,
+attention of each of the 30 layers (12 heads x 128) into that layer's rows of A_loc / A_full (each layer
+keeps the rows of all its warmup chunks side by side, 18,720 x 1536 per output); after the last chunk
+the warmup statistics of all 30 layers over all their rows in one batched call (the same sums as one
+update per chunk, `--stats-per-chunk`, with a quarter of the statistics' read-modify-write traffic),
+then one batched ridge solve of all layers (d = 1536, lambda = 1e-2) with each layer's reconstruction
+error at its optimum,
 the errors copied to the host and the K = 15 L-Layers selected there. Inputs are seeded synthetic
 tensors already resident in HBM when the timed region starts. `--workload-cfg 4` runs the same step
 at the 14B shape (40 layers x 40 heads, d = 5120, K = 20).
@@ -45,6 +48,9 @@ def parse():
     ap.add_argument("--workload-cfg", type=int, default=3, choices=(3, 4),
                     help="workload of the timed step: 3 = the Wan-1.3B warmup (default), 4 = the 14B warmup "
                          "(40 layers x 40 heads, d = 5120)")
+    ap.add_argument("--stats-per-chunk", action="store_true",
+                    help="update the statistics after every chunk (one batched call per chunk over that chunk's "
+                         "rows, outputs reused) instead of once over the rows of all warmup chunks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the attention timings on workloads 5 and 4 that follow the step")
@@ -125,14 +131,15 @@ def attn_traffic():
     return ATTN_TRAFFIC["bytes_per_launch"] if digest == ATTN_TRAFFIC["sha256"] else None
 
 
-# HBM bytes per statistics launch of the warmup step (one batched call: 30 layers x one 4680-row
-# chunk, the 256 x 256 tile kernel with 8 waves), from the same FETCH_SIZE / WRITE_SIZE runs and factors, taken on
-# the statistics source with this SHA-256; reported only while the source is unchanged.
+# HBM bytes per statistics launch of the warmup step (one batched call of the 30 layers, the 256 x 256
+# tile kernel with 8 waves), keyed by the rows per launch (4680: one chunk's rows, the per-chunk form),
+# from the same FETCH_SIZE / WRITE_SIZE runs and factors, taken on the statistics source with this
+# SHA-256; reported only while the source is unchanged and for a launch of those rows.
 GRAM_TRAFFIC = {"sha256": "117777c9986c15ae8dac066d4ca2a13854a27d43c48b311d237735b7e157cdf4",
-                "bytes_per_launch": 5946484912}
+                "bytes_per_launch": {4680: 5946484912}}
 
 
-def gram_traffic():
+def gram_traffic(rows):
     import hashlib
     src = os.path.join(ROOT, "kv_cache_attention_split_amd", "csrc", "gram.hip")
     try:
@@ -140,7 +147,7 @@ def gram_traffic():
             digest = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    return GRAM_TRAFFIC["bytes_per_launch"] if digest == GRAM_TRAFFIC["sha256"] else None
+    return GRAM_TRAFFIC["bytes_per_launch"].get(rows) if digest == GRAM_TRAFFIC["sha256"] else None
 
 
 def cpu_baseline(wl):
@@ -748,9 +755,15 @@ def main():
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t0
 
-    # each layer's chunk outputs stay until the chunk's statistics are taken
-    a_loc = [torch.empty((n_q, d), dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    # each layer's attention outputs: the rows of all warmup chunks side by side (chunk c writes rows
+    # [c n_q, (c + 1) n_q)), taken by one statistics call after the last chunk; with --stats-per-chunk
+    # one chunk's rows, taken after every chunk
+    n_ch = len(wl.chunks)
+    per_chunk = args.stats_per_chunk
+    rows_kept = n_q if per_chunk else n_ch * n_q
+    a_loc = [torch.empty((rows_kept, d), dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
     a_full = [torch.empty_like(x) for x in a_loc]
+    row0 = [0 if per_chunk else c * n_q for c in range(n_ch)]
     lse = [torch.empty((H, n_q), dtype=torch.float32, device="cuda") for _ in range(3)]
     # every layer's G, X, F in one allocation, so that the warmup's start clears them with one fill
     stats_all = torch.zeros((n_layers, 3, d, d), dtype=torch.float32, device="cuda")
@@ -768,8 +781,8 @@ def main():
     seg_keys = [sum(wl.segment_sizes(c)[k] for k in ("n_sink", "n_cur", "n_hist"))
                 for c in range(len(wl.chunks))]
     flops_attn = sum(attn_flops(n_q, nk, H, dh) for nk in seg_keys) * n_layers
-    flops_stats_chunk = 4.0 * n_q * d * d * n_layers        # one batched call
-    flops_stats = flops_stats_chunk * len(wl.chunks)
+    flops_stats = 4.0 * n_q * d * d * n_layers * n_ch
+    flops_stats_launch = flops_stats / n_ch if per_chunk else flops_stats   # one batched call
     flops_solve = 13.0 / 3.0 * d ** 3 * n_layers
     flops_err = 1.0 * d ** 3 * n_layers                     # W W^T, lower tiles
     flops_step = flops_attn + flops_stats + flops_solve + flops_err
@@ -787,18 +800,19 @@ def main():
                 if record:
                     e0, e1 = ev(), ev()
                     e0.record()
-                ispa.ispa_attn_dual(L.q[c], sk, sv, ck, cv, hk, hv, wl.scale, a_loc[li], a_full[li],
-                                    lse[0], lse[1], lse[2])
+                ispa.ispa_attn_dual(L.q[c], sk, sv, ck, cv, hk, hv, wl.scale, a_loc[li][row0[c]:row0[c] + n_q],
+                                    a_full[li][row0[c]:row0[c] + n_q], lse[0], lse[1], lse[2])
                 if record:
                     e1.record()
                     timing["attn"].append((e0, e1, seg_keys[c]))
-            if record:
-                e0, e1 = ev(), ev()
-                e0.record()
-            ispa.ispa_absorb_accumulate_batched(a_loc, a_full, Gs, Xs, Fs)
-            if record:
-                e1.record()
-                timing["stats"].append((e0, e1))
+            if per_chunk or c == n_ch - 1:
+                if record:
+                    e0, e1 = ev(), ev()
+                    e0.record()
+                ispa.ispa_absorb_accumulate_batched(a_loc, a_full, Gs, Xs, Fs)
+                if record:
+                    e1.record()
+                    timing["stats"].append((e0, e1))
         if record:
             e3, e4 = ev(), ev()
             e3.record()
@@ -812,7 +826,15 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    # per-kernel event timing (separate pass, so the step timing below carries no event overhead)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        sel, flags = step(False)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-kernel event timing: a separate pass (so the step timing above carries no event overhead),
+    # taken after the timed steps, when the clocks have left the lower state of the first tenths of a
+    # second of load (a pass right after two warm-up steps on a fresh box read the attention 40 % low)
     step(True)
     torch.cuda.synchronize()
     att = [(a.elapsed_time(b), nk) for a, b, nk in timing["attn"]]
@@ -823,15 +845,8 @@ def main():
     stats_avg_ms = stats_ms / len(timing["stats"])
     solve_ms = sum(a.elapsed_time(b) for a, b in timing["solve"])
 
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        sel, flags = step(False)
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-
     att_tflops = att_flops_per_launch / att_avg_ms / 1e9
-    stats_tflops = flops_stats_chunk / stats_avg_ms / 1e9
+    stats_tflops = flops_stats_launch / stats_avg_ms / 1e9
     info_h = info.cpu().tolist()
     eps_h = eps.cpu().tolist()
     ref_h = ref.cpu().tolist()
@@ -853,7 +868,8 @@ def main():
         "data": "synthetic (seeded N(0,1) queries/values, AR(1) rho=0.95 keys across latent frames, W ~ N(0,1/d))",
         "config": {"workload": wl.name, "layers": n_layers, "chunks": len(wl.chunks),
                    "heads": H, "head_dim": dh, "queries_per_chunk": n_q,
-                   "keys_per_chunk": seg_keys, "lambda": wl.lam, "k_select": min(wl.k_select, n_layers)},
+                   "keys_per_chunk": seg_keys, "lambda": wl.lam, "k_select": min(wl.k_select, n_layers),
+                   "statistics": "per chunk" if per_chunk else "once over all warmup rows"},
         "attn_tflops": round(att_tflops, 1),
         "attn_frac_mfma_peak": round(att_tflops / PEAK_BF16_TFLOPS, 4),
         "attn_ms_per_layer": round(att_ms / n_layers, 4),
@@ -874,9 +890,10 @@ def main():
         "roofline_statistics": {"kernel": stats_kernel_name(d, n_layers), "bound": "mfma",
                                 "achieved": round(stats_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                 "frac": round(stats_tflops / PEAK_BF16_TFLOPS, 4),
-                                "traffic": gram_traffic() if wl.cfg == 3 and n_layers == wl.n_layers else None,
+                                "traffic": gram_traffic(rows_kept) if wl.cfg == 3 and n_layers == wl.n_layers else None,
                                 "avg_launch_ms": round(stats_avg_ms, 5),
-                                "flops_per_launch": flops_stats_chunk},
+                                "rows_per_launch": rows_kept,
+                                "flops_per_launch": flops_stats_launch},
         **extra,
         "setup_s": round(t_setup, 1),
     }
