@@ -234,6 +234,16 @@ __device__ __forceinline__ void write_lse(float *out, float val, int head, int q
 #ifndef ISPA_ATTN_VCOPY_B
 #define ISPA_ATTN_VCOPY_B 1     // ping-pong kernel with value products: group B copies the values
 #endif
+// Ping-pong kernel: a wave runs its matrix phase at this priority (s_setprio) and drops back to 0 after
+// the matrix products (mode 1) or after the phase's copies (mode 2). Where both waves of a SIMD have an
+// instruction ready, the one in its matrix phase issues first: the MFMAs and their operand reads are the
+// critical path, the other wave's softmax fills the cycles between them. 0 turns it off.
+#ifndef ISPA_ATTN_PRIO
+#define ISPA_ATTN_PRIO 1
+#endif
+#ifndef ISPA_ATTN_PRIO_MODE
+#define ISPA_ATTN_PRIO_MODE 1
+#endif
 
 template <int D, bool BIAS>
 __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel(AttnArgs a, int n_qt) {
@@ -947,6 +957,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
 
   for (int i = t0; i <= t1; ++i) {
     // ---- matrix phase: scores of tile i, value product of tile i-1 ----
+    if constexpr (ISPA_ATTN_PRIO > 0) __builtin_amdgcn_s_setprio(ISPA_ATTN_PRIO);
     if (i < t1) {
       if constexpr (BIAS) {
         // the score accumulators start at b / tau instead of 0, so the softmax below sees
@@ -1033,6 +1044,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
+    if constexpr (ISPA_ATTN_PRIO > 0 && ISPA_ATTN_PRIO_MODE == 1) __builtin_amdgcn_s_setprio(0);
     // copies after this phase's LDS reads: K(i+1) and the bias of tile i+1 here; V(i) here as well when
     // the copies go in the matrix phase (VCOPY_VEC false), else at the start of the vector phase, which
     // has no LDS access (the compiler adds no wait for it) and runs beside group B's matrix phase, which
@@ -1047,6 +1059,7 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     // VCOPY_B: group B's copies of V(i) (issued in its vector phase of tile i-1) land before group A's
     // matrix phase i+1 reads them
     if (VCOPY_B && grp == 1) ISPA_WAIT_VMCNT(0);
+    if constexpr (ISPA_ATTN_PRIO > 0 && ISPA_ATTN_PRIO_MODE == 2) __builtin_amdgcn_s_setprio(0);
     ISPA_LDS_BARRIER();
     if (!VCOPY_B && VCOPY_VEC && grp == 0 && i < t1) dma_v(i, i & 1);
     // V(i+1) goes to the buffer of V(i-1), which both groups finished reading in their matrix phases i
