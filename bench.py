@@ -113,11 +113,10 @@ class Layer:
 
 # HBM bytes per attention launch of the warmup step (average over its 4 chunk shapes), from
 # rocprofv3 FETCH_SIZE x 1.9997 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
-# attention source with SHA-256 7ff5a528...2505 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md); the source
-# with the SHA-256 below differs from it only outside the step's kernel, whose compiled code is the same
-# instruction for instruction. Reported only while the source is unchanged.
-ATTN_TRAFFIC = {"sha256": "b1255a264d2d1509ca2ed5c7127ca2656cb3a0709bad9230f079f9024e2d09a1",
-                "bytes_per_launch": 157859059}
+# attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only while
+# the source is unchanged.
+ATTN_TRAFFIC = {"sha256": "1d50ae91282a18853e433039b0e57221c3b7212cac8ad5c24893fcb0d3942b39",
+                "bytes_per_launch": 157849331}
 
 
 def attn_traffic():
@@ -132,11 +131,12 @@ def attn_traffic():
 
 
 # HBM bytes per statistics launch of the warmup step (one batched call of the 30 layers, the 256 x 256
-# tile kernel with 8 waves), keyed by the rows per launch (4680: one chunk's rows, the per-chunk form),
+# tile kernel with 8 waves), keyed by the rows per launch (18,720: the rows of all 4 warmup chunks; 4680:
+# one chunk's rows, the per-chunk form),
 # from the same FETCH_SIZE / WRITE_SIZE runs and factors, taken on the statistics source with this
 # SHA-256; reported only while the source is unchanged and for a launch of those rows.
 GRAM_TRAFFIC = {"sha256": "117777c9986c15ae8dac066d4ca2a13854a27d43c48b311d237735b7e157cdf4",
-                "bytes_per_launch": {4680: 5946484912}}
+                "bytes_per_launch": {4680: 5946484912, 18720: 19436119333}}
 
 
 def gram_traffic(rows):
