@@ -787,7 +787,16 @@ def main():
     flops_err = 1.0 * d ** 3 * n_layers                     # W W^T, lower tiles
     flops_step = flops_attn + flops_stats + flops_solve + flops_err
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    # the event-timed pass takes its events from a pool made beforehand: creating two timing events per
+    # launch inside the pass (host work between the launches) let the queue run dry in a fresh process,
+    # and the idle gaps then counted in the launches' times (attention read 40 % low)
+    n_events = 2 * (n_layers * n_ch + n_ch + 1)
+    pool = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    for e in pool:
+        e.record()                  # the device events are made at the first record
+    torch.cuda.synchronize()
+    pool_it = iter(())
+    ev = lambda: next(pool_it)   # noqa: E731
     timing = {"attn": [], "stats": [], "solve": []}
 
     def step(record: bool):
@@ -833,8 +842,8 @@ def main():
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # per-kernel event timing: a separate pass (so the step timing above carries no event overhead),
-    # taken after the timed steps, when the clocks have left the lower state of the first tenths of a
-    # second of load (a pass right after two warm-up steps on a fresh box read the attention 40 % low)
+    # taken after the timed steps
+    pool_it = iter(pool)
     step(True)
     torch.cuda.synchronize()
     att = [(a.elapsed_time(b), nk) for a, b, nk in timing["attn"]]
