@@ -115,8 +115,8 @@ class Layer:
 # rocprofv3 FETCH_SIZE x 1.9997 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
 # attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only while
 # the source is unchanged.
-ATTN_TRAFFIC = {"sha256": "1d50ae91282a18853e433039b0e57221c3b7212cac8ad5c24893fcb0d3942b39",
-                "bytes_per_launch": 157849331}
+ATTN_TRAFFIC = {"sha256": "fc0dc71ae4362feb9b24b1bce1fb79494da70e0325a04918ab0e71e8adbdda4d",
+                "bytes_per_launch": 157849316}
 
 
 def attn_traffic():

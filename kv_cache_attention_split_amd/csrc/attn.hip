@@ -244,6 +244,9 @@ __device__ __forceinline__ void write_lse(float *out, float val, int head, int q
 #ifndef ISPA_ATTN_PRIO_MODE
 #define ISPA_ATTN_PRIO_MODE 1
 #endif
+#ifndef ISPA_ATTN_LANE_OFFS
+#define ISPA_ATTN_LANE_OFFS 1   // ping-pong kernel: K and V^T operand reads from per-lane offsets set once
+#endif
 
 template <int D, bool BIAS>
 __global__ void __launch_bounds__(kThreads, ISPA_ATTN_WGS) attn_dual_bf16_kernel(AttnArgs a, int n_qt) {
@@ -862,20 +865,48 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     j = j < nseg ? j : nseg - 1;
     copy_to_lds<4>(bias_ptr(a, hist, j, head), bbuf[buf]);
   };
+  const int g = lane >> 4, sl = lane & 15;
+  // The swizzle of a tile row depends on the row mod 16 only, so the byte offset of (R0 + r, col) is
+  // R0 * 2D + that of (r, col) for R0 a multiple of 16: a lane's K and V^T operand reads differ by their
+  // 32-key block b (and the 16-row half h2 of a V^T read) only in an immediate. With LANE_OFFS the
+  // lane's offsets of the 32-key block 0 (8 for K, one per 16-column step; 2 per 32-column block for
+  // V^T) are formed once, before the tile loop, and kept (the empty asm stops the compiler from forming
+  // them again in every tile, which it did: about 56 address instructions per wave and tile).
+  constexpr bool LOFFS = ISPA_ATTN_LANE_OFFS && !FP8;
+  int koff[LOFFS ? NKK : 1], voff[LOFFS && !FP8V ? 2 * NDB : 1];
+  if constexpr (LOFFS) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      koff[kk] = kv_off<D>(l32, 16 * kk + 8 * hf);
+      asm volatile("" : "+v"(koff[kk]));
+    }
+    if constexpr (!FP8V) {
+      const int r = 4 * (g >> 1) + (sl >> 2);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
+        voff[2 * db] = kv_off<D>(r, col);
+        voff[2 * db + 1] = kv_off<D>(r + 8, col);
+        asm volatile("" : "+v"(voff[2 * db]), "+v"(voff[2 * db + 1]));
+      }
+    }
+  }
   auto kread = [&](int buf, int i) -> bf16x8 {
     const int kk = i / NB, b = i % NB;
+    if constexpr (LOFFS) return *(const bf16x8 *)(kbuf[buf] + koff[kk] + 32 * b * (D * 2));
     return *(const bf16x8 *)(kbuf[buf] + kv_off<D>(32 * b + l32, 16 * kk + 8 * hf));
   };
-  const int g = lane >> 4, sl = lane & 15;
   auto vread = [&](int u, int i) -> bf16x8 {
     const uint8_t *vt = vbuf[u & 1];
     const int db = i / (2 * NB), b = (i / 2) % NB, h2 = i % 2;
     const int col = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
     const int row = 32 * b + 16 * h2 + 4 * (g >> 1) + (sl >> 2);
+    const int off_lo = LOFFS ? voff[LOFFS ? 2 * db : 0] + (32 * b + 16 * h2) * (D * 2) : kv_off<D>(row, col);
+    const int off_hi = LOFFS ? voff[LOFFS ? 2 * db + 1 : 0] + (32 * b + 16 * h2) * (D * 2) : kv_off<D>(row + 8, col);
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(vt + kv_off<D>(row, col)));
+        (__attribute__((address_space(3))) s16x4 *)(vt + off_lo));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4 *)(vt + kv_off<D>(row + 8, col)));
+        (__attribute__((address_space(3))) s16x4 *)(vt + off_hi));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // e4m3 V^T operand of 32-column block db for the 64 keys of a tile: byte j of lane (column l32, half
