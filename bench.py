@@ -69,6 +69,9 @@ def parse():
                     help="time the TempCache merge and attention over merged vs original history")
     ap.add_argument("--gram-only-cfg", type=int, default=None,
                     help="time only the statistics update of one chunk at workload 3's or 4's width")
+    ap.add_argument("--gram-rows", type=int, default=None,
+                    help="rows per statistics call for --gram-only-cfg (default: one chunk, 4680; the warmup "
+                         "step's call takes all 4 chunks' rows, 18720)")
     ap.add_argument("--absorb-cfg", type=int, default=None,
                     help="time the whole Layer Absorb of workload 3 or 4 (all layers: statistics of the "
                          "warmup chunks, one batched solve, one batched error, ranking) per layer")
@@ -131,12 +134,11 @@ def attn_traffic():
 
 
 # HBM bytes per statistics launch of the warmup step (one batched call of the 30 layers, the 256 x 256
-# tile kernel with 8 waves), keyed by the rows per launch (18,720: the rows of all 4 warmup chunks; 4680:
-# one chunk's rows, the per-chunk form),
-# from the same FETCH_SIZE / WRITE_SIZE runs and factors, taken on the statistics source with this
-# SHA-256; reported only while the source is unchanged and for a launch of those rows.
-GRAM_TRAFFIC = {"sha256": "117777c9986c15ae8dac066d4ca2a13854a27d43c48b311d237735b7e157cdf4",
-                "bytes_per_launch": {4680: 5946484912, 18720: 19436119333}}
+# tile kernel with 8 waves), keyed by the rows per launch (18,720: the rows of all 4 warmup chunks), from
+# the same FETCH_SIZE / WRITE_SIZE runs and factors, taken on the statistics source with this SHA-256;
+# reported only while the source is unchanged and for a launch of those rows.
+GRAM_TRAFFIC = {"sha256": "3b62d338fb31b413ddf715092cac91de06e1d8c463d40af5e74865947c28bb91",
+                "bytes_per_launch": {18720: 21306776110}}
 
 
 def gram_traffic(rows):
@@ -319,14 +321,14 @@ def attn_report(cfg, steps, warmup, torch):
     print(json.dumps(out), flush=True)
 
 
-def gram_report(cfg, steps, warmup, torch):
-    """Statistics update of one 4680-row chunk at a workload's width d: one layer per call, and all the
-    workload's layers in one batched call (warm median time and rate; 4 N d^2 FLOP per layer: G and F as
-    half products, X in full)."""
+def gram_report(cfg, steps, warmup, torch, rows=None):
+    """Statistics update of N rows (one 4680-row chunk unless given) at a workload's width d: one layer
+    per call, and all the workload's layers in one batched call (warm median time and rate; 4 N d^2 FLOP
+    per layer: G and F as half products, X in full)."""
     import ispa_inputs as inputs
     import kv_cache_attention_split_amd as ispa
     wl = inputs.CONFIGS[cfg]
-    d, n, L = wl.d, inputs.CHUNK_TOKENS, wl.n_layers
+    d, n, L = wl.d, rows or inputs.CHUNK_TOKENS, wl.n_layers
     g = torch.Generator(device="cuda").manual_seed(1234 + cfg)
     a_loc = [(0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16) for _ in range(L)]
     a_full = [(0.02 * torch.randn((n, d), device="cuda", generator=g)).to(torch.bfloat16) for _ in range(L)]
@@ -731,7 +733,7 @@ def main():
         tempcache_report(max(args.steps, 20), max(args.warmup, 5), torch)
         return
     if args.gram_only_cfg is not None:
-        gram_report(args.gram_only_cfg, max(args.steps, 20), max(args.warmup, 5), torch)
+        gram_report(args.gram_only_cfg, max(args.steps, 20), max(args.warmup, 5), torch, args.gram_rows)
         return
     if args.absorb_cfg is not None:
         absorb_report(args.absorb_cfg, min(args.steps, 5), min(args.warmup, 1), torch)

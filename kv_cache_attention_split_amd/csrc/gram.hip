@@ -46,10 +46,10 @@ static __device__ __attribute__((aligned(16))) uint32_t g_zero_row[4];
   } while (0)
 
 // One launch covers the tiles of up to kMaxGramLayers layers (same n_rows and d): workgroup ids run
-// over (layer, tile) pairs, tiles of one layer consecutive, in the XCD-aware order (each XCD takes a
-// contiguous range, so the tiles that share a layer's rows share an L2; measured better than giving
-// every XCD a share of each layer, which keeps all XCDs on one layer but spreads an XCD's concurrent
-// tiles over several layers).
+// over (layer, tile) pairs, tiles of one layer consecutive, in an XCD-aware order (the 128 x 128 kernel:
+// each XCD takes a contiguous range, so the tiles that share a layer's rows share an L2, measured better
+// than giving every XCD a share of each layer, which spreads an XCD's concurrent tiles over several
+// layers; the 256 x 256 kernel: blocks of 32 consecutive ids in turn over the XCDs, see there).
 constexpr int kMaxGramLayers = 48;
 struct GramArgs {
   const uint16_t *a_loc[kMaxGramLayers], *a_full[kMaxGramLayers];
@@ -311,7 +311,21 @@ __global__ void __launch_bounds__(64 * NWV, 1) gram_bf16_wide_kernel(GramArgs g)
   // the wave's B half-panel and its first column in it
   const int bpart = NWV == 8 ? 2 + (wn >> 1) : 2 + wn, bcol = NWV == 8 ? 64 * (wn & 1) : 0;
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  // Workgroup b runs on XCD b mod 8 as that XCD's (b / 8)-th workgroup; an XCD runs 32 at a time, one per
+  // CU. Each XCD's next 32 are the next unclaimed block of 32 consecutive (layer, tile) ids: the XCD's
+  // concurrent tiles share one layer's rows in its L2, and the 8 XCDs together hold about 256 consecutive
+  // tiles (a few layers) rather than 8 ranges far apart, so rows that miss an L2 are more often in the
+  // memory-side cache. Workgroups past the last whole round of 256 keep their own id.
+  int lin;
+  {
+    const int b = (int)blockIdx.x, full = (int)(gridDim.x / 256) * 256;
+    if (b < full) {
+      const int x = b & 7, slot = b >> 3;
+      lin = (((slot >> 5) << 3) + x) * 32 + (slot & 31);
+    } else {
+      lin = b;
+    }
+  }
   const int layer = lin / g.tiles;
   int idx = lin % g.tiles;
   int mat, ti, tj;   // mat: 0 = G, 1 = F, 2 = X
