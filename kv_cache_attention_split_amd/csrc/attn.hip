@@ -872,23 +872,24 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
   // lane's offsets of the 32-key block 0 (8 for K, one per 16-column step; 2 per 32-column block for
   // V^T) are formed once, before the tile loop, and kept (the empty asm stops the compiler from forming
   // them again in every tile, which it did: about 56 address instructions per wave and tile).
-  constexpr bool LOFFS = ISPA_ATTN_LANE_OFFS && !FP8;
-  int koff[LOFFS ? NKK : 1], voff[LOFFS && !FP8V ? 2 * NDB : 1];
+  constexpr bool LOFFS = ISPA_ATTN_LANE_OFFS && !FP8;        // bf16 keys
+  constexpr bool LOFFS_V = ISPA_ATTN_LANE_OFFS && !FP8V && !LSE_ONLY;   // bf16 values
+  int koff[LOFFS ? NKK : 1], voff[LOFFS_V ? 2 * NDB : 1];
   if constexpr (LOFFS) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       koff[kk] = kv_off<D>(l32, 16 * kk + 8 * hf);
       asm volatile("" : "+v"(koff[kk]));
     }
-    if constexpr (!FP8V) {
-      const int r = 4 * (g >> 1) + (sl >> 2);
+  }
+  if constexpr (LOFFS_V) {
+    const int r = 4 * (g >> 1) + (sl >> 2);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
-        voff[2 * db] = kv_off<D>(r, col);
-        voff[2 * db + 1] = kv_off<D>(r + 8, col);
-        asm volatile("" : "+v"(voff[2 * db]), "+v"(voff[2 * db + 1]));
-      }
+    for (int db = 0; db < NDB; ++db) {
+      const int col = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
+      voff[2 * db] = kv_off<D>(r, col);
+      voff[2 * db + 1] = kv_off<D>(r + 8, col);
+      asm volatile("" : "+v"(voff[2 * db]), "+v"(voff[2 * db + 1]));
     }
   }
   auto kread = [&](int buf, int i) -> bf16x8 {
@@ -901,8 +902,8 @@ __global__ void __launch_bounds__(512, 1) attn_dual_bf16_pp_kernel(AttnArgs a, i
     const int db = i / (2 * NB), b = (i / 2) % NB, h2 = i % 2;
     const int col = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
     const int row = 32 * b + 16 * h2 + 4 * (g >> 1) + (sl >> 2);
-    const int off_lo = LOFFS ? voff[LOFFS ? 2 * db : 0] + (32 * b + 16 * h2) * (D * 2) : kv_off<D>(row, col);
-    const int off_hi = LOFFS ? voff[LOFFS ? 2 * db + 1 : 0] + (32 * b + 16 * h2) * (D * 2) : kv_off<D>(row + 8, col);
+    const int off_lo = LOFFS_V ? voff[LOFFS_V ? 2 * db : 0] + (32 * b + 16 * h2) * (D * 2) : kv_off<D>(row, col);
+    const int off_hi = LOFFS_V ? voff[LOFFS_V ? 2 * db + 1 : 0] + (32 * b + 16 * h2) * (D * 2) : kv_off<D>(row + 8, col);
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4 *)(vt + off_lo));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
