@@ -116,11 +116,10 @@ class Layer:
 
 # HBM bytes per attention launch of the warmup step (average over its 4 chunk shapes), from
 # rocprofv3 FETCH_SIZE x 1.9997 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
-# attention source with SHA-256 fc0dc71a...da4d (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md); the source
-# with the SHA-256 below differs from it only in the FP8-score form: the step kernel's compiled code is
-# the same instruction for instruction. Reported only while the source is unchanged.
-ATTN_TRAFFIC = {"sha256": "be0f9c8d921720e675c91d43e83b6d0c9da7b50e74b051adf21717ce0a2979c9",
-                "bytes_per_launch": 157849316}
+# attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only while
+# the source is unchanged.
+ATTN_TRAFFIC = {"sha256": "05c5ba7a265e1e1c22e3e41ce5cdbe9d4d5ef40aa88ac9e5c44291568b9dde2a",
+                "bytes_per_launch": 157905645}
 
 
 def attn_traffic():
