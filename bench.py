@@ -914,11 +914,14 @@ def main():
 
 
 def stats_kernel_name(d, n_layers):
-    """The statistics kernel one batched call of n_layers layers at width d runs (the library's rule:
-    256 x 256 tiles once a launch of up to 48 layers has 512 of them)."""
+    """The statistics kernels one batched call of n_layers layers at width d runs (the library's rule:
+    256 x 256 tiles once a launch of up to 48 layers has 512 of them, their last partial round of 256
+    workgroups as quarters on the 128 x 128 kernel)."""
     T = (d + 255) // 256
-    wide = (T * (T + 1) + T * T) * min(n_layers, 48) >= 512
-    return "gram_bf16_wide_kernel" if wide else "gram_bf16_kernel"
+    n_wide = (T * (T + 1) + T * T) * min(n_layers, 48)
+    if n_wide < 512:
+        return "gram_bf16_kernel"
+    return "gram_bf16_wide_kernel" + (" + gram_bf16_kernel (last partial round)" if n_wide % 256 else "")
 
 
 def extra_attention(step_cfg, torch):

@@ -56,7 +56,12 @@ struct GramArgs {
   float *G[kMaxGramLayers], *X[kMaxGramLayers], *F[kMaxGramLayers];
   int64_t n_rows;
   int d, T, n_upper, with_f, tiles;   // T: tiles per dimension; tiles: per layer
+  // 128 x 128 kernel only: tail_first >= 0 makes it cover the 256 x 256 tiles tail_first, tail_first + 1,
+  // ... of a wide launch's tile list (Tw, n_upper_w, tiles_w: that list's geometry), workgroup 4 u + q
+  // taking quarter q of tile tail_first + u
+  int tail_first, Tw, n_upper_w, tiles_w;
 };
+
 
 __device__ __forceinline__ void tri_decode(int idx, int T, int &ti, int &tj) {
   // idx enumerates pairs ti <= tj row by row
@@ -67,6 +72,22 @@ __device__ __forceinline__ void tri_decode(int idx, int T, int &ti, int &tj) {
   }
   ti = r;
   tj = r + idx;
+}
+
+// tile idx of a layer's list: the upper tiles of G, the upper tiles of F (if present), all tiles of X
+__device__ __forceinline__ void decode_tile(int idx, int T, int n_upper, int with_f, int &mat, int &ti, int &tj) {
+  if (idx < n_upper) {
+    mat = 0;
+    tri_decode(idx, T, ti, tj);
+  } else if (with_f && idx < 2 * n_upper) {
+    mat = 1;
+    tri_decode(idx - n_upper, T, ti, tj);
+  } else {
+    mat = 2;
+    idx -= n_upper * (with_f ? 2 : 1);
+    ti = idx / T;
+    tj = idx % T;
+  }
 }
 
 // A stage holds each operand row-major ([row of the chunk][128 columns], 256 bytes per row) with the
@@ -111,21 +132,22 @@ __global__ void __launch_bounds__(kThreads, 2) gram_bf16_kernel(GramArgs g) {
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wm = w >> 1, wn = w & 1;
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int layer = lin / g.tiles;
-  int idx = lin % g.tiles;
-  int mat, ti, tj;   // mat: 0 = G, 1 = F, 2 = X
-  if (idx < g.n_upper) {
-    mat = 0;
-    tri_decode(idx, g.T, ti, tj);
-  } else if (g.with_f && idx < 2 * g.n_upper) {
-    mat = 1;
-    tri_decode(idx - g.n_upper, g.T, ti, tj);
+  int layer, mat, ti, tj;   // mat: 0 = G, 1 = F, 2 = X
+  if (g.tail_first >= 0) {
+    // a quarter of a 256 x 256 tile of a wide launch's list; a quarter that lies past d, or below the
+    // diagonal of G or F (its elements come from the mirror of the quarter above), has no work. Every
+    // element is the same fixed-order sum as in the 256 x 256 kernel.
+    const int u = g.tail_first + (int)(blockIdx.x >> 2), q = (int)(blockIdx.x & 3);
+    layer = u / g.tiles_w;
+    int TI, TJ;
+    decode_tile(u % g.tiles_w, g.Tw, g.n_upper_w, g.with_f, mat, TI, TJ);
+    ti = 2 * TI + (q >> 1);
+    tj = 2 * TJ + (q & 1);
+    if (ti >= g.T || tj >= g.T || (mat != 2 && ti > tj)) return;   // uniform: the whole workgroup
   } else {
-    mat = 2;
-    idx -= g.n_upper * (g.with_f ? 2 : 1);
-    ti = idx / g.T;
-    tj = idx % g.T;
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    layer = lin / g.tiles;
+    decode_tile(lin % g.tiles, g.T, g.n_upper, g.with_f, mat, ti, tj);
   }
   const uint16_t *P = (mat == 1) ? g.a_full[layer] : g.a_loc[layer];   // rows of the left factor
   const uint16_t *Q = (mat == 0) ? g.a_loc[layer] : g.a_full[layer];   // rows of the right factor
@@ -764,6 +786,9 @@ int gram_tiles(int d, int bt, bool with_f) {
   return T * (T + 1) / 2 * (with_f ? 2 : 1) + T * T;
 }
 
+#ifndef ISPA_GRAM_TAIL_SPLIT
+#define ISPA_GRAM_TAIL_SPLIT 1   // tiles of a wide launch's last partial round of 256 go to the 128 x 128 kernel
+#endif
 #ifndef ISPA_GRAM_WIDE_MIN
 #define ISPA_GRAM_WIDE_MIN 512   // wide-tile workgroups a launch needs before the wide kernel is used
 #endif
@@ -791,16 +816,40 @@ hipError_t launch_gram_bf16_batch(int64_t n_rows, int d, int batch, const uint16
     g.n_upper = g.T * (g.T + 1) / 2;
     g.with_f = with_f;
     g.tiles = gram_tiles(d, bt, with_f);
-    const dim3 grid((unsigned)(g.tiles * cnt));
-    if (wide)
+    g.tail_first = -1;
+    g.Tw = g.n_upper_w = g.tiles_w = 0;
+    const int n_wg = g.tiles * cnt;
+    if (wide) {
+      // The 256 x 256 kernel runs whole rounds of 256 workgroups (one per CU); the tiles of a last,
+      // partial round would hold a few CUs for a whole tile while the rest idle, so they go to the
+      // 128 x 128 kernel as quarters (four times the workgroups, two per CU), launched after it.
+      const int full = ISPA_GRAM_TAIL_SPLIT ? n_wg / 256 * 256 : n_wg;
+      const int tail = full > 0 ? n_wg - full : 0;
+      const int main_wg = n_wg - tail;
       if (ISPA_GRAM_WAVES == 8)
-        hipLaunchKernelGGL(gram_bf16_wide_kernel<8>, grid, dim3(512), 0, s, g);
+        hipLaunchKernelGGL(gram_bf16_wide_kernel<8>, dim3((unsigned)main_wg), dim3(512), 0, s, g);
       else
-        hipLaunchKernelGGL(gram_bf16_wide_kernel<4>, grid, dim3(256), 0, s, g);
-    else
-      hipLaunchKernelGGL(gram_bf16_kernel, grid, dim3(kThreads), 0, s, g);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(gram_bf16_wide_kernel<4>, dim3((unsigned)main_wg), dim3(256), 0, s, g);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (tail > 0) {
+        GramArgs gt = g;
+        gt.Tw = g.T;
+        gt.n_upper_w = g.n_upper;
+        gt.tiles_w = g.tiles;
+        gt.tail_first = main_wg;
+        gt.T = (d + BT - 1) / BT;
+        gt.n_upper = gt.T * (gt.T + 1) / 2;
+        gt.tiles = gram_tiles(d, BT, with_f);
+        hipLaunchKernelGGL(gram_bf16_kernel, dim3((unsigned)(4 * tail)), dim3(kThreads), 0, s, gt);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    } else {
+      hipLaunchKernelGGL(gram_bf16_kernel, dim3((unsigned)n_wg), dim3(kThreads), 0, s, g);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
