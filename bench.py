@@ -133,12 +133,13 @@ def attn_traffic():
     return ATTN_TRAFFIC["bytes_per_launch"] if digest == ATTN_TRAFFIC["sha256"] else None
 
 
-# HBM bytes per statistics launch of the warmup step (one batched call of the 30 layers, the 256 x 256
-# tile kernel with 8 waves), keyed by the rows per launch (18,720: the rows of all 4 warmup chunks), from
-# the same FETCH_SIZE / WRITE_SIZE runs and factors, taken on the statistics source with this SHA-256;
-# reported only while the source is unchanged and for a launch of those rows.
-GRAM_TRAFFIC = {"sha256": "3b62d338fb31b413ddf715092cac91de06e1d8c463d40af5e74865947c28bb91",
-                "bytes_per_launch": {18720: 21306776110}}
+# HBM bytes per statistics call of the warmup step (one batched call of the 30 layers: the 256 x 256
+# tile kernel with 8 waves and its last partial round as 128 x 128 quarters), keyed by the rows per call
+# (18,720: the rows of all 4 warmup chunks), from the same FETCH_SIZE / WRITE_SIZE runs and factors (both
+# kernels summed), taken on the statistics source with this SHA-256; reported only while the source is
+# unchanged and for a call of those rows.
+GRAM_TRAFFIC = {"sha256": "92f1230a9384da7f2650c35455050235c5e5385a8b44801c213cb5c712bda26d",
+                "bytes_per_launch": {18720: 20602037030}}
 
 
 def gram_traffic(rows):
