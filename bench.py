@@ -116,20 +116,23 @@ class Layer:
 
 # HBM bytes per attention launch of the warmup step (average over its 4 chunk shapes), from
 # rocprofv3 FETCH_SIZE x 1.9997 + WRITE_SIZE x 1.000 (factors from a 256 MiB device copy), taken on the
-# attention source with this SHA-256 (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only while
-# the source is unchanged.
-ATTN_TRAFFIC = {"sha256": "05c5ba7a265e1e1c22e3e41ce5cdbe9d4d5ef40aa88ac9e5c44291568b9dde2a",
-                "bytes_per_launch": 157905645}
+# build whose attention source and build script (with its compiler flags) hash to this SHA-256
+# (profiles/attn_dual_bf16_pp_wan1.3b-warmup.md). Reported only while both are unchanged.
+ATTN_TRAFFIC = {"sha256": "71294b539a289b56b3f04cfd50f79d77fcb354c4871113d55b4933307ef06ee3",
+                "bytes_per_launch": 157836418}
 
 
 def attn_traffic():
+    # keyed by the attention source and the build script (which holds its compiler flags)
     import hashlib
-    src = os.path.join(ROOT, "kv_cache_attention_split_amd", "csrc", "attn.hip")
+    h = hashlib.sha256()
     try:
-        with open(src, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        for part in (("csrc", "attn.hip"), ("build.py",)):
+            with open(os.path.join(ROOT, "kv_cache_attention_split_amd", *part), "rb") as f:
+                h.update(f.read())
     except OSError:
         return None
+    digest = h.hexdigest()
     return ATTN_TRAFFIC["bytes_per_launch"] if digest == ATTN_TRAFFIC["sha256"] else None
 
 

@@ -33,6 +33,13 @@ COMMON = [
 ]
 
 
+# Per-source flags. attn.hip: the machine scheduler's instruction-level-parallelism strategy; measured on the
+# ping-pong attention kernel (18,720-key chunk, within one call): 0.5194-0.5198 ms against 0.5258-0.5259
+# with the default strategy (+1.2 %), no spills in any of the file's kernels (the plain kernel then holds
+# 251 VGPRs, two waves per SIMD as before).
+PER_SOURCE = {"attn.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -42,7 +49,8 @@ def hipcc() -> str:
 
 def _compile(src: str, defines: List[str], verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *PER_SOURCE.get(src, []), *[f"-D{d}" for d in defines], "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")
